@@ -1,0 +1,252 @@
+"""Flash-LoRA-Attention for AMD MI355X (gfx950): thin Python binding.
+
+Multi-LoRA agents share a base KV cache and a low-rank (LR) cache and apply
+their own up-projections B_k, B_v (LRAgent, arXiv 2602.01053v2, §3 and App. B;
+PReCache, arXiv 2609.34054, PreLRShared).  All arithmetic runs in the HIP
+kernels of ``liblra_attn.so`` (C ABI in ``include/lra_attn.h``); this module
+only marshals torch tensors (device memory) and the current HIP stream into
+those calls.  There is no CPU fallback: if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
+    "lr_cache_build", "rope_table", "abi_version", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "liblra_attn.so")
+
+LRA_F32, LRA_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "lra_abi_version", "lra_status_str", "lra_last_error", "lra_attn_decode_workspace_size",
+    "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build", "lra_rope_table_build",
+)
+
+
+class LraError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"status {status}: {detail}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+
+
+def load():
+    """Load liblra_attn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} not found: build it with "
+                          "`python -m attention_shared_base_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(lib_path)
+    lib.lra_abi_version.restype = I32
+    lib.lra_abi_version.argtypes = []
+    lib.lra_status_str.restype = ctypes.c_char_p
+    lib.lra_status_str.argtypes = [I32]
+    lib.lra_last_error.restype = ctypes.c_char_p
+    lib.lra_last_error.argtypes = []
+    lib.lra_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.lra_attn_decode_workspace_size.argtypes = [ctypes.POINTER(Dims), I32, I32, I32, I32]
+    lib.lra_attn_decode.restype = I32
+    lib.lra_attn_decode.argtypes = [
+        ctypes.POINTER(Dims), P, I32, P, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, I32,
+        P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.lra_attn_prefill.restype = I32
+    lib.lra_attn_prefill.argtypes = [
+        ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, P, P]
+    lib.lra_lr_cache_build.restype = I32
+    lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, P, P, ctypes.c_int64, P]
+    lib.lra_rope_table_build.restype = I32
+    lib.lra_rope_table_build.argtypes = [ctypes.c_double, I32, I32, P, P, P]
+    _lib = lib
+    return lib
+
+
+def abi_version():
+    return int(load().lra_abi_version())
+
+
+def _check(status):
+    if status != 0:
+        lib = load()
+        raise LraError(status, f"{lib.lra_status_str(status).decode()} — {lib.lra_last_error().decode()}")
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LRA_BF16
+    if t.dtype == torch.float32:
+        return LRA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    import torch
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _contig(name, t):
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.device.type == "cuda", f"{name} must be a device tensor")
+    return t
+
+
+def _dims(h_q, h_kv, d, r, dtype, scale):
+    return Dims(h_q, h_kv, d, r, dtype, float(scale))
+
+
+def decode_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, dtype, n_req, n_ctx,
+                          max_req_per_ctx, max_ctx_len):
+    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, dtype, 0.0)
+    return int(load().lra_attn_decode_workspace_size(ctypes.byref(dims), n_req, n_ctx,
+                                                      max_req_per_ctx, max_ctx_len))
+
+
+def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table, ctx_len,
+           b_k, b_v, *, max_req_per_ctx, max_ctx_len, out=None, workspace=None,
+           softmax_scale=0.0, stream=None):
+    """Paged decode (``lra_attn_decode``).  Layouts as in include/lra_attn.h:
+
+    q [n_req, H_q, d]; k_pool [n_pages, H_kv, d/8, 16, 8]; v_pool [n_pages, H_kv, d, 16];
+    lk_pool [n_pages, 16, r]; lv_pool [n_pages, r, 16]; block_table [n_ctx, max_blocks];
+    ctx_len [n_ctx]; ctx_req_start [n_ctx+1]; req_agent [n_req]; b_k, b_v [n_agents, r, H_kv*d].
+    ``workspace`` (uint8, zero-filled before first use) is allocated when not given.
+    """
+    import torch
+    lib = load()
+    n_req, h_q, d = q.shape
+    n_pages, h_kv, d8, page, eight = k_pool.shape
+    _need(d8 * 8 == d and eight == 8, "k_pool must be [n_pages, H_kv, d/8, page, 8]")
+    r = lk_pool.shape[2]
+    n_ctx, max_blocks = block_table.shape
+    n_agents = b_k.shape[0]
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
+                    ("lv_pool", lv_pool), ("b_k", b_k), ("b_v", b_v)):
+        _contig(name, t)
+        _need(_dtype_code(t) == dt, f"{name} dtype differs from q")
+    for name, t in (("ctx_req_start", ctx_req_start), ("req_agent", req_agent),
+                    ("block_table", block_table), ("ctx_len", ctx_len)):
+        _contig(name, t)
+        _need(t.dtype == torch.int32, f"{name} must be int32")
+    _need(tuple(v_pool.shape) == (n_pages, h_kv, d, page), "v_pool must be [n_pages, H_kv, d, page]")
+    _need(tuple(lk_pool.shape) == (n_pages, page, r), "lk_pool must be [n_pages, page, r]")
+    _need(tuple(lv_pool.shape) == (n_pages, r, page), "lv_pool must be [n_pages, r, page]")
+    _need(tuple(b_k.shape) == (n_agents, r, h_kv * d) and b_v.shape == b_k.shape,
+          "b_k/b_v must be [n_agents, r, H_kv*d]")
+    _need(ctx_req_start.shape == (n_ctx + 1,) and ctx_len.shape == (n_ctx,)
+          and req_agent.shape == (n_req,), "index array shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    _contig("out", out)
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale)
+    ws_bytes = int(lib.lra_attn_decode_workspace_size(ctypes.byref(dims), n_req, n_ctx,
+                                                      max_req_per_ctx, max_ctx_len))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lra_attn_decode(
+        ctypes.byref(dims), _ptr(q), n_req, _ptr(ctx_req_start), n_ctx, max_req_per_ctx,
+        _ptr(req_agent), _ptr(k_pool), _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, page,
+        _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
+        _ptr(out), _ptr(workspace), wsz, _stream(q, stream)))
+    return out
+
+
+def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, rope_sin=None,
+            out=None, softmax_scale=0.0, stream=None):
+    """Chunked prefill (``lra_attn_prefill``): q [n_req, q_len, H_q, d] over
+    k_base/v_base [H_kv, kv_len, d], l_k/l_v [kv_len, r]; optional RoPE tables
+    [kv_len, d/2] fp32 rotate the adapter key term."""
+    import torch
+    lib = load()
+    n_req, q_len, h_q, d = q.shape
+    h_kv, kv_len, _ = k_base.shape
+    r = l_k.shape[1]
+    n_agents = b_k.shape[0]
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k_base", k_base), ("v_base", v_base), ("l_k", l_k), ("l_v", l_v),
+                    ("b_k", b_k), ("b_v", b_v)):
+        _contig(name, t)
+        _need(_dtype_code(t) == dt, f"{name} dtype differs from q")
+    _contig("req_agent", req_agent)
+    _need(req_agent.dtype == torch.int32 and req_agent.shape == (n_req,), "req_agent [n_req] int32")
+    _need(tuple(v_base.shape) == (h_kv, kv_len, d), "v_base shape")
+    _need(tuple(l_k.shape) == (kv_len, r) and tuple(l_v.shape) == (kv_len, r), "l_k/l_v [kv_len, r]")
+    _need(tuple(b_k.shape) == (n_agents, r, h_kv * d) and b_v.shape == b_k.shape, "b_k/b_v shape")
+    if rope_cos is not None:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            _contig(name, t)
+            _need(t.dtype == torch.float32 and t.shape[0] >= kv_len and t.shape[1] == d // 2,
+                  f"{name} must be fp32 [>=kv_len, d/2]")
+    if out is None:
+        out = torch.empty_like(q)
+    _contig("out", out)
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale)
+    _check(lib.lra_attn_prefill(
+        ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_base), _ptr(v_base),
+        kv_len, _ptr(l_k), _ptr(l_v), _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
+        _ptr(rope_sin), _ptr(out), _stream(q, stream)))
+    return out
+
+
+def lr_cache_build(x, a_k, a_v, l_k, l_v, *, row_offset=0, stream=None):
+    """LR-cache rows ``L[row_offset + i] = x[i] A`` (``lra_lr_cache_build``).
+
+    x [n_tok, d_model]; a_k, a_v [r, d_model] (LoRA A weight layout, out x in);
+    l_k, l_v [>= row_offset + n_tok, r], written in place.
+    """
+    lib = load()
+    n_tok, d_model = x.shape
+    r = a_k.shape[0]
+    dt = _dtype_code(x)
+    for name, t in (("x", x), ("a_k", a_k), ("a_v", a_v), ("l_k", l_k), ("l_v", l_v)):
+        _contig(name, t)
+        _need(_dtype_code(t) == dt, f"{name} dtype differs from x")
+    _need(tuple(a_k.shape) == (r, d_model) and tuple(a_v.shape) == (r, d_model), "a_k/a_v [r, d_model]")
+    _need(l_k.shape[1] == r and l_v.shape[1] == r, "l_k/l_v [*, r]")
+    _need(l_k.shape[0] >= row_offset + n_tok and l_v.shape[0] >= row_offset + n_tok,
+          "l_k/l_v too short for row_offset + n_tok")
+    _check(lib.lra_lr_cache_build(dt, _ptr(x), n_tok, d_model, _ptr(a_k), _ptr(a_v), r,
+                                  _ptr(l_k), _ptr(l_v), int(row_offset), _stream(x, stream)))
+    return l_k, l_v
+
+
+def rope_table(theta, head_dim, n_pos, device="cuda", stream=None):
+    """fp32 cos/sin tables [n_pos, head_dim/2] of pos * theta^(-2i/d), built on the GPU."""
+    import torch
+    lib = load()
+    cos = torch.empty((n_pos, head_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check(lib.lra_rope_table_build(float(theta), head_dim, n_pos, _ptr(cos), _ptr(sin),
+                                    _stream(cos, stream)))
+    return cos, sin

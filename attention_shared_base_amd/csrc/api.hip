@@ -1,0 +1,320 @@
+// C ABI: argument validation, work planning and dispatch to the gfx950 kernels.
+// Declarations and the contract of every entry point are in include/lra_attn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "lra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+lra_status fail(lra_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+// Shared checks of the dims struct.  Returns LRA_OK or a status with detail.
+lra_status check_dims(const lra_dims* d) {
+    if (!d) return fail(LRA_ERR_NULL_PTR, "dims is NULL");
+    if (d->n_q_heads <= 0 || d->n_kv_heads <= 0)
+        return fail(LRA_ERR_BAD_SHAPE, "head counts must be positive (H_q=%d, H_kv=%d)", d->n_q_heads, d->n_kv_heads);
+    if (d->n_q_heads % d->n_kv_heads != 0)
+        return fail(LRA_ERR_BAD_SHAPE, "H_q=%d is not a multiple of H_kv=%d", d->n_q_heads, d->n_kv_heads);
+    if (d->dtype != LRA_F32 && d->dtype != LRA_BF16)
+        return fail(LRA_ERR_UNSUPPORTED, "dtype %d (expected LRA_F32=0 or LRA_BF16=1)", d->dtype);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(LRA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
+    if (d->rank != 8 && d->rank != 16 && d->rank != 32)
+        return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 8, 16, 32)", d->rank);
+    if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
+        return fail(LRA_ERR_BAD_SHAPE, "softmax_scale is not finite");
+    return LRA_OK;
+}
+
+float eff_scale(const lra_dims* d) {
+    return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+}
+
+#define REQUIRE_PTR(p)                                                  \
+    do {                                                                \
+        if (!(p)) return fail(LRA_ERR_NULL_PTR, "%s is NULL", #p);      \
+        if (!aligned16(p)) return fail(LRA_ERR_MISALIGNED, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+}  // namespace
+
+namespace lra {
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+lra_status check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: %s", what, hipGetErrorString(e));
+        return LRA_ERR_HIP;
+    }
+    return LRA_OK;
+}
+
+bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, int max_ctx_len,
+                 DecodePlan* p) {
+    const int g = d.n_q_heads / d.n_kv_heads;
+    if (g < 1 || g > 16 || n_ctx < 1 || max_req_per_ctx < 1 || max_ctx_len < 0 || n_req < 0) return false;
+    p->g = g;
+    p->rpg = 16 / g;
+    p->n_rg = (max_req_per_ctx + p->rpg - 1) / p->rpg;
+    const long long units = (long long)n_ctx * p->n_rg * d.n_kv_heads;
+    if (units > (1 << 26)) return false;
+    p->n_units = (int)units;
+    // Chunk length: enough workgroups to fill 256 CUs a few times over, each
+    // still streaming several 32-token steps per wavefront.
+    int chunk = env_int("LRA_DECODE_CHUNK", 0);
+    if (chunk <= 0) {
+        const int target = env_int("LRA_DECODE_TARGET_WG", 512);
+        long long c = ((long long)max_ctx_len * units + target - 1) / (target > 0 ? target : 512);
+        c = ((c + 127) / 128) * 128;
+        if (c < 128) c = 128;
+        if (c > 1024) c = 1024;
+        chunk = (int)c;
+    }
+    chunk = ((chunk + 127) / 128) * 128;
+    p->chunk = chunk;
+    p->n_split = max_ctx_len > 0 ? (max_ctx_len + chunk - 1) / chunk : 1;
+    const long long wgs = units * p->n_split;
+    if (wgs > 0x7ffffff0LL) return false;
+    p->grid = (int)((wgs + 7) / 8 * 8);
+    const int dr2 = d.head_dim + d.rank + 2;
+    p->ws_counter_bytes = ((size_t)p->n_units * sizeof(int32_t) + 255) / 256 * 256;
+    p->ws_part_bytes = p->n_split > 1 ? (size_t)p->n_units * p->n_split * 16 * dr2 * sizeof(float) : 0;
+    p->ws_total = p->n_split > 1 ? p->ws_counter_bytes + p->ws_part_bytes : 0;
+    return true;
+}
+
+}  // namespace lra
+
+extern "C" {
+
+int32_t lra_abi_version(void) { return LRA_ABI_VERSION; }
+
+const char* lra_status_str(lra_status s) {
+    switch (s) {
+        case LRA_OK: return "LRA_OK";
+        case LRA_ERR_NULL_PTR: return "LRA_ERR_NULL_PTR: a required pointer is NULL";
+        case LRA_ERR_BAD_SHAPE: return "LRA_ERR_BAD_SHAPE: inconsistent or out-of-range sizes";
+        case LRA_ERR_UNSUPPORTED: return "LRA_ERR_UNSUPPORTED: valid but not implemented";
+        case LRA_ERR_MISALIGNED: return "LRA_ERR_MISALIGNED: device pointer not 16-byte aligned";
+        case LRA_ERR_WORKSPACE_TOO_SMALL: return "LRA_ERR_WORKSPACE_TOO_SMALL: workspace below the queried size";
+        case LRA_ERR_HIP: return "LRA_ERR_HIP: a HIP call or kernel launch failed";
+        default: return "unknown lra_status";
+    }
+}
+
+const char* lra_last_error(void) { return g_err; }
+
+size_t lra_attn_decode_workspace_size(const lra_dims* dims, int32_t n_req, int32_t n_ctx,
+                                      int32_t max_req_per_ctx, int32_t max_ctx_len) {
+    if (check_dims(dims) != LRA_OK) return 0;
+    if (dims->dtype != LRA_BF16) return 0;
+    lra::DecodePlan p;
+    if (!lra::decode_plan(*dims, n_req, n_ctx, max_req_per_ctx, max_ctx_len, &p)) return 0;
+    return p.ws_total;
+}
+
+lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
+                           const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
+                           const int32_t* req_agent, const void* k_pool, const void* v_pool,
+                           const void* lk_pool, const void* lv_pool, int32_t n_pages,
+                           int32_t page_size, const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
+                           const void* b_v, int32_t n_agents, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+    if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
+    if (n_ctx < 1) return fail(LRA_ERR_BAD_SHAPE, "n_ctx %d < 1", n_ctx);
+    if (max_req_per_ctx < 1 || max_req_per_ctx > (n_req > 0 ? n_req : 1))
+        return fail(LRA_ERR_BAD_SHAPE, "max_req_per_ctx %d outside [1, n_req=%d]", max_req_per_ctx, n_req);
+    if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
+    if (max_blocks < 1) return fail(LRA_ERR_BAD_SHAPE, "max_blocks %d < 1", max_blocks);
+    if (max_ctx_len < 0 || (long long)max_ctx_len > (long long)max_blocks * page_size)
+        return fail(LRA_ERR_BAD_SHAPE, "max_ctx_len %d outside [0, max_blocks*page_size=%lld]",
+                    max_ctx_len, (long long)max_blocks * page_size);
+    if (n_agents < 1) return fail(LRA_ERR_BAD_SHAPE, "n_agents %d < 1", n_agents);
+    const int g = dims->n_q_heads / dims->n_kv_heads;
+    if (dims->dtype == LRA_BF16 && g > 16)
+        return fail(LRA_ERR_UNSUPPORTED, "bf16 decode packs at most 16 query heads per KV head (g=%d)", g);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(ctx_req_start);
+    REQUIRE_PTR(req_agent);
+    REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool);
+    REQUIRE_PTR(lk_pool);
+    REQUIRE_PTR(lv_pool);
+    REQUIRE_PTR(block_table);
+    REQUIRE_PTR(ctx_len);
+    REQUIRE_PTR(b_k);
+    REQUIRE_PTR(b_v);
+    REQUIRE_PTR(out);
+
+    lra::DecodeArgs a;
+    a.q = q;
+    a.ctx_req_start = ctx_req_start;
+    a.req_agent = req_agent;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.lk_pool = lk_pool;
+    a.lv_pool = lv_pool;
+    a.block_table = block_table;
+    a.ctx_len = ctx_len;
+    a.b_k = b_k;
+    a.b_v = b_v;
+    a.out = out;
+    a.workspace = workspace;
+    a.n_req = n_req;
+    a.n_ctx = n_ctx;
+    a.n_pages = n_pages;
+    a.max_blocks = max_blocks;
+    a.max_ctx_len = max_ctx_len;
+    a.n_agents = n_agents;
+    a.h_q = dims->n_q_heads;
+    a.h_kv = dims->n_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.rank = dims->rank;
+    a.scale = eff_scale(dims);
+
+    if (dims->dtype == LRA_F32) {
+        if (n_req == 0) return LRA_OK;
+        return lra::launch_decode_f32(a, (hipStream_t)stream);
+    }
+    lra::DecodePlan p;
+    if (!lra::decode_plan(*dims, n_req, n_ctx, max_req_per_ctx, max_ctx_len, &p))
+        return fail(LRA_ERR_BAD_SHAPE, "decode: problem too large to plan");
+    if (p.ws_total > 0) {
+        if (!workspace) return fail(LRA_ERR_NULL_PTR, "workspace is NULL (need %zu bytes)", p.ws_total);
+        if (!aligned16(workspace)) return fail(LRA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+        if (workspace_bytes < p.ws_total)
+            return fail(LRA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, p.ws_total);
+    }
+    if (n_req == 0) return LRA_OK;
+    return lra::launch_decode_bf16(a, p, (hipStream_t)stream);
+}
+
+lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, int32_t q_len,
+                            const int32_t* req_agent, const void* k_base, const void* v_base,
+                            int32_t kv_len, const void* l_k, const void* l_v, const void* b_k,
+                            const void* b_v, int32_t n_agents, const float* rope_cos,
+                            const float* rope_sin, void* out, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
+    if (q_len < 1) return fail(LRA_ERR_BAD_SHAPE, "q_len %d < 1", q_len);
+    if (kv_len < q_len) return fail(LRA_ERR_BAD_SHAPE, "kv_len %d < q_len %d", kv_len, q_len);
+    if (n_agents < 1) return fail(LRA_ERR_BAD_SHAPE, "n_agents %d < 1", n_agents);
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return fail(LRA_ERR_NULL_PTR, "rope_cos and rope_sin must both be given or both NULL");
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(req_agent);
+    REQUIRE_PTR(k_base);
+    REQUIRE_PTR(v_base);
+    REQUIRE_PTR(l_k);
+    REQUIRE_PTR(l_v);
+    REQUIRE_PTR(b_k);
+    REQUIRE_PTR(b_v);
+    REQUIRE_PTR(out);
+    if (rope_cos) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+    }
+    lra::PrefillArgs a;
+    a.q = q;
+    a.req_agent = req_agent;
+    a.k_base = k_base;
+    a.v_base = v_base;
+    a.l_k = l_k;
+    a.l_v = l_v;
+    a.b_k = b_k;
+    a.b_v = b_v;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.out = out;
+    a.n_req = n_req;
+    a.q_len = q_len;
+    a.kv_len = kv_len;
+    a.n_agents = n_agents;
+    a.h_q = dims->n_q_heads;
+    a.h_kv = dims->n_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.rank = dims->rank;
+    a.scale = eff_scale(dims);
+    if (n_req == 0) return LRA_OK;
+    if (dims->dtype == LRA_F32) return lra::launch_prefill_f32(a, (hipStream_t)stream);
+    return lra::launch_prefill_bf16(a, (hipStream_t)stream);
+}
+
+lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,
+                              const void* a_k, const void* a_v, int32_t rank, void* l_k, void* l_v,
+                              int64_t row_offset, void* stream) {
+    g_err[0] = 0;
+    if (dtype != LRA_F32 && dtype != LRA_BF16)
+        return fail(LRA_ERR_UNSUPPORTED, "dtype %d (expected LRA_F32=0 or LRA_BF16=1)", dtype);
+    if (rank != 8 && rank != 16 && rank != 32)
+        return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 8, 16, 32)", rank);
+    if (n_tok < 0) return fail(LRA_ERR_BAD_SHAPE, "n_tok %d < 0", n_tok);
+    if (d_model <= 0) return fail(LRA_ERR_BAD_SHAPE, "d_model %d <= 0", d_model);
+    if (d_model % 32 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %d is not a multiple of 32", d_model);
+    if (row_offset < 0) return fail(LRA_ERR_BAD_SHAPE, "row_offset %lld < 0", (long long)row_offset);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(a_k);
+    REQUIRE_PTR(a_v);
+    REQUIRE_PTR(l_k);
+    REQUIRE_PTR(l_v);
+    lra::LRBuildArgs a;
+    a.x = x;
+    a.a_k = a_k;
+    a.a_v = a_v;
+    a.l_k = l_k;
+    a.l_v = l_v;
+    a.n_tok = n_tok;
+    a.d_model = d_model;
+    a.rank = rank;
+    a.row_offset = row_offset;
+    if (n_tok == 0) return LRA_OK;
+    if (dtype == LRA_F32) return lra::launch_lr_build_f32(a, (hipStream_t)stream);
+    return lra::launch_lr_build_bf16(a, (hipStream_t)stream);
+}
+
+lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos, float* cos_out,
+                                float* sin_out, void* stream) {
+    g_err[0] = 0;
+    if (!(theta > 0.0) || isinf(theta)) return fail(LRA_ERR_BAD_SHAPE, "theta must be finite and > 0");
+    if (head_dim <= 0 || head_dim % 2 != 0) return fail(LRA_ERR_BAD_SHAPE, "head_dim %d must be even and > 0", head_dim);
+    if (n_pos < 0) return fail(LRA_ERR_BAD_SHAPE, "n_pos %d < 0", n_pos);
+    REQUIRE_PTR(cos_out);
+    REQUIRE_PTR(sin_out);
+    if (n_pos == 0) return LRA_OK;
+    return lra::launch_rope_table(theta, head_dim, n_pos, cos_out, sin_out, (hipStream_t)stream);
+}
+
+}  // extern "C"

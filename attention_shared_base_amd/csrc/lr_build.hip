@@ -1,0 +1,151 @@
+// Shared low-rank cache build L = X A for newly processed tokens.
+//
+// PReCache (PreLRShared) builds the adapters' low-rank caches when a context
+// chunk is first processed by multiplying its hidden states with the adapters'
+// input (down-projection) matrices; with a shared A (LRAgent §3 BaseLRShared)
+// one product serves every agent.  Here both the key and the value
+// down-projections are applied in one pass over X:  [L_k | L_v] = X [A_k | A_v].
+//
+// The product is tall and skinny (d_model x 2r with 2r <= 64) and bound by
+// reading X once from HBM.  A workgroup owns 16 tokens; its 8 wavefronts take
+// interleaved 32-wide slices of d_model (so together they stream each X row
+// contiguously) and each accumulates the full 16 x 2r tile with
+// v_mfma_f32_16x16x32_bf16; the eight partial tiles are summed in LDS and
+// rounded once to bf16.
+#include "lra_common.h"
+#include "lra_internal.h"
+
+namespace {
+
+constexpr int TOK = 16;
+constexpr int WAVES = 8;
+
+template <int R>
+__global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __restrict__ x,
+                                                                const bf16* __restrict__ a_k,
+                                                                const bf16* __restrict__ a_v,
+                                                                bf16* __restrict__ l_k,
+                                                                bf16* __restrict__ l_v,
+                                                                int n_tok, int d_model,
+                                                                long long row_offset) {
+    constexpr int NT = (2 * R + 15) / 16;  // 16-column output tiles
+    constexpr int NC = NT * 16;
+    __shared__ float sm[WAVES][TOK][NC + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int tok0 = blockIdx.x * TOK;
+
+    const bool tok_ok = tok0 + l16 < n_tok;
+    const bf16* xp = x + (size_t)(tok0 + l16) * d_model + 8 * kq;
+    const bf16* wp[NT];
+    bool col_ok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + l16;
+        col_ok[nt] = col < 2 * R;
+        const bf16* base = col < R ? a_k + (size_t)col * d_model
+                                   : a_v + (size_t)(col_ok[nt] ? col - R : 0) * d_model;
+        wp[nt] = base + 8 * kq;
+    }
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = zf4();
+
+    const int n_steps = d_model / 32;
+#pragma unroll 4
+    for (int st = wave; st < n_steps; st += WAVES) {
+        const int k = st * 32;
+        const bf16x8 xa = tok_ok ? ldg_stream((const bf16x8*)(xp + k)) : zero8();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8 wb = col_ok[nt] ? ldg((const bf16x8*)(wp[nt] + k)) : zero8();
+            acc[nt] = mfma16x16x32(xa, wb, acc[nt]);
+        }
+    }
+    // C lane layout: tokens 4*kq + v, column l16 of each tile
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm[wave][4 * kq + v][nt * 16 + l16] = acc[nt][v];
+    __syncthreads();
+    for (int e = tid; e < TOK * 2 * R; e += blockDim.x) {
+        const int t = e / (2 * R), c = e % (2 * R);
+        if (tok0 + t >= n_tok) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += sm[w][t][c];
+        const size_t row = (size_t)(row_offset + tok0 + t);
+        if (c < R) l_k[row * R + c] = (bf16)s;
+        else l_v[row * R + (c - R)] = (bf16)s;
+    }
+}
+
+__global__ void lra_lr_build_f32_kernel(const float* __restrict__ x, const float* __restrict__ a_k,
+                                        const float* __restrict__ a_v, float* __restrict__ l_k,
+                                        float* __restrict__ l_v, int n_tok, int d_model, int r,
+                                        long long row_offset) {
+    const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (long long)n_tok * 2 * r) return;
+    const int t = (int)(e / (2 * r)), c = (int)(e % (2 * r));
+    const float* w = c < r ? a_k + (size_t)c * d_model : a_v + (size_t)(c - r) * d_model;
+    const float* xr = x + (size_t)t * d_model;
+    float s = 0.f;
+    for (int k = 0; k < d_model; ++k) s += xr[k] * w[k];
+    const size_t row = (size_t)(row_offset + t);
+    if (c < r) l_k[row * r + c] = s;
+    else l_v[row * r + (c - r)] = s;
+}
+
+__global__ void lra_rope_table_kernel(double theta, int head_dim, int n_pos, float* cs, float* sn) {
+    const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int half = head_dim / 2;
+    if (e >= (long long)n_pos * half) return;
+    const int pos = (int)(e / half), i = (int)(e % half);
+    const double ang = (double)pos * pow(theta, -2.0 * i / head_dim);
+    cs[e] = (float)cos(ang);
+    sn[e] = (float)sin(ang);
+}
+
+}  // namespace
+
+namespace lra {
+
+lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
+    if (a.n_tok == 0) return LRA_OK;
+    const dim3 grid((a.n_tok + TOK - 1) / TOK), block(64 * WAVES);
+    const bf16* x = (const bf16*)a.x;
+    const bf16* ak = (const bf16*)a.a_k;
+    const bf16* av = (const bf16*)a.a_v;
+    bf16* lk = (bf16*)a.l_k;
+    bf16* lv = (bf16*)a.l_v;
+    switch (a.rank) {
+        case 8: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<8>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, (long long)a.row_offset); break;
+        case 16: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<16>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, (long long)a.row_offset); break;
+        case 32: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<32>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, (long long)a.row_offset); break;
+        default: set_error("lr build: unsupported rank %d", a.rank); return LRA_ERR_UNSUPPORTED;
+    }
+    return check_launch("lra_lr_build_bf16_kernel");
+}
+
+lra_status launch_lr_build_f32(const LRBuildArgs& a, hipStream_t s) {
+    const long long n = (long long)a.n_tok * 2 * a.rank;
+    if (n == 0) return LRA_OK;
+    hipLaunchKernelGGL(lra_lr_build_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const float*)a.x, (const float*)a.a_k, (const float*)a.a_v, (float*)a.l_k,
+                       (float*)a.l_v, a.n_tok, a.d_model, a.rank, (long long)a.row_offset);
+    return check_launch("lra_lr_build_f32_kernel");
+}
+
+lra_status launch_rope_table(double theta, int head_dim, int n_pos, float* c, float* sn,
+                             hipStream_t st) {
+    const long long n = (long long)n_pos * (head_dim / 2);
+    if (n == 0) return LRA_OK;
+    hipLaunchKernelGGL(lra_rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       theta, head_dim, n_pos, c, sn);
+    return check_launch("lra_rope_table_kernel");
+}
+
+}  // namespace lra

@@ -1,0 +1,101 @@
+// Host-side interfaces between the C-ABI layer (api.hip) and the kernel
+// translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lra_attn.h"
+
+namespace lra {
+
+void set_error(const char* fmt, ...);
+lra_status check_launch(const char* what);
+
+// ----------------------------------------------------------------- decode
+// Work decomposition of one decode call.  A work unit is (context, row group,
+// KV head); a row group holds up to 16 query rows = rpg requests x g heads.
+// Each unit's keys are cut into chunks of `chunk` tokens (a multiple of 128);
+// one workgroup handles one (unit, chunk).
+struct DecodePlan {
+    int g;          // query heads per KV head
+    int rpg;        // requests per row group (16 / g)
+    int n_rg;       // row groups per context
+    int n_units;    // n_ctx * n_rg * H_kv
+    int chunk;      // tokens per workgroup
+    int n_split;    // chunks per unit at max_ctx_len
+    int grid;       // workgroups launched (multiple of 8)
+    size_t ws_counter_bytes;
+    size_t ws_part_bytes;
+    size_t ws_total;
+};
+
+bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, int max_ctx_len,
+                 DecodePlan* plan);
+
+struct DecodeArgs {
+    const void* q;
+    const int32_t* ctx_req_start;
+    const int32_t* req_agent;
+    const void* k_pool;
+    const void* v_pool;
+    const void* lk_pool;
+    const void* lv_pool;
+    const int32_t* block_table;
+    const int32_t* ctx_len;
+    const void* b_k;
+    const void* b_v;
+    void* out;
+    void* workspace;
+    int32_t n_req, n_ctx, n_pages, max_blocks, max_ctx_len, n_agents;
+    int32_t h_q, h_kv, head_dim, rank;
+    float scale;
+};
+
+lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+
+// ----------------------------------------------------------------- prefill
+struct PrefillArgs {
+    const void* q;
+    const int32_t* req_agent;
+    const void* k_base;
+    const void* v_base;
+    const void* l_k;
+    const void* l_v;
+    const void* b_k;
+    const void* b_v;
+    const float* rope_cos;
+    const float* rope_sin;
+    void* out;
+    int32_t n_req, q_len, kv_len, n_agents;
+    int32_t h_q, h_kv, head_dim, rank;
+    float scale;
+};
+
+lra_status launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+
+// ----------------------------------------------------------------- fp32 path
+// Straightforward fp32 kernels (one wavefront per query row) used for
+// dtype == LRA_F32: exact fp32 arithmetic for any supported shape.
+lra_status launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+lra_status launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+
+// ----------------------------------------------------------------- LR build
+struct LRBuildArgs {
+    const void* x;
+    const void* a_k;
+    const void* a_v;
+    void* l_k;
+    void* l_v;
+    int32_t n_tok, d_model, rank;
+    int64_t row_offset;
+};
+
+lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s);
+lra_status launch_lr_build_f32(const LRBuildArgs& a, hipStream_t s);
+
+lra_status launch_rope_table(double theta, int head_dim, int n_pos, float* c, float* s,
+                             hipStream_t st);
+
+}  // namespace lra

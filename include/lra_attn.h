@@ -1,0 +1,199 @@
+/*
+ * lra_attn.h — C ABI of the Flash-LoRA-Attention library for AMD MI355X (gfx950).
+ *
+ * Multi-LoRA agents share one base KV cache (K_base, V_base) and one low-rank
+ * (LR) cache (L_k = X A_k, L_v = X A_v under shared-A LoRA); each agent owns a
+ * small up-projection B_k, B_v.  The library computes
+ *
+ *     O = softmax(Q (K_base + L_k B_k)^T * scale) (V_base + L_v B_v)
+ *
+ * without expanding L B to head dimension in memory: the score uses
+ * Q K_base^T + (Q B_k^T) L_k^T and the value side P V_base + (P L_v) B_v, with
+ * the rank-r intermediate kept through the streaming pass and B_v applied once
+ * per query row at the end.
+ *
+ * Sources (LRAgent, arXiv 2602.01053v2, paperlayer.ai summary and the
+ * gist.science explainers; PReCache, arXiv 2609.34054, ai.info abstract and the
+ * rit.work blog):
+ *   - cache decomposition Y = X W0 + X A B ............. LRAgent App. A.3
+ *   - BaseShared / BaseLRShared (shared A => shared LR) LRAgent §3
+ *   - reordering O = P V_base + (P V_lr) B, online softmax over streamed
+ *     K/V blocks, one post-multiplication per query block  LRAgent §3, App. B
+ *   - key-side adapter rebuilt before RoPE ............. LRAgent App. D.1
+ *   - LR cache built for new context by X A ............ PReCache (PreLRShared)
+ *
+ * General conventions
+ *   - Every buffer is owned by the caller; the library never allocates, frees
+ *     or keeps a pointer after a call returns.  Device pointers must be 16-byte
+ *     aligned.  Output buffers must not alias inputs.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream).  They keep no global mutable state except the per-thread error
+ *     text returned by lra_last_error().
+ *   - Scalar arguments are validated before any HIP call; on failure nothing is
+ *     launched and a nonzero lra_status is returned.  Launch failures return
+ *     LRA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Element counts and layouts below are in elements of the storage type
+ *     (dims->dtype): LRA_BF16 = bfloat16 bits, LRA_F32 = IEEE float.
+ *     Accumulation is always fp32.  bf16 outputs are rounded to nearest even.
+ *   - Supported: head_dim in {64, 128}, rank in {8, 16, 32},
+ *     n_q_heads % n_kv_heads == 0, page_size == 16.  Query heads map to KV
+ *     head hq / (n_q_heads / n_kv_heads) (contiguous groups).
+ */
+#ifndef LRA_ATTN_H
+#define LRA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lra_status;
+#define LRA_OK 0
+#define LRA_ERR_NULL_PTR 1            /* a required pointer is NULL */
+#define LRA_ERR_BAD_SHAPE 2           /* inconsistent or out-of-range sizes */
+#define LRA_ERR_UNSUPPORTED 3         /* valid but not implemented (dtype, d, r, page) */
+#define LRA_ERR_MISALIGNED 4          /* a device pointer is not 16-byte aligned */
+#define LRA_ERR_WORKSPACE_TOO_SMALL 5 /* workspace_bytes below the queried size */
+#define LRA_ERR_HIP 6                 /* a HIP runtime call or launch failed */
+
+#define LRA_F32 0
+#define LRA_BF16 1
+
+#define LRA_ABI_VERSION 1
+
+typedef struct lra_dims {
+    int32_t n_q_heads;   /* H_q */
+    int32_t n_kv_heads;  /* H_kv; H_q % H_kv == 0 */
+    int32_t head_dim;    /* d: 64 or 128 */
+    int32_t rank;        /* r: 8, 16 or 32 */
+    int32_t dtype;       /* LRA_F32 or LRA_BF16, for every tensor of the call */
+    float softmax_scale; /* <= 0 selects 1/sqrt(head_dim) */
+} lra_dims;
+
+/* ABI version of the loaded library (LRA_ABI_VERSION it was built with). */
+int32_t lra_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* lra_status_str(lra_status status);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* lra_last_error(void);
+
+/*
+ * Paged decode: one new query token per request over its context's shared
+ * caches (LRAgent §3 BaseLRShared decode; App. B kernel).  Requests are grouped
+ * by context: the requests of context c are ctx_req_start[c] ..
+ * ctx_req_start[c+1]-1, and every request of a context reads that context's
+ * base and LR pages once per KV head (GQA and cross-agent sharing).
+ *
+ *   q              [n_req, H_q, d]                         device
+ *   ctx_req_start  [n_ctx + 1] int32, non-decreasing,      device
+ *                  ctx_req_start[0] == 0, [n_ctx] == n_req;
+ *                  no context may hold more than max_req_per_ctx requests
+ *   req_agent      [n_req] int32 in [0, n_agents)          device
+ *   k_pool         [n_pages, H_kv, d/8, page_size, 8]      device
+ *                  (key t of a page: its 8-element groups of dims are
+ *                  page_size*8 elements apart)
+ *   v_pool         [n_pages, H_kv, d, page_size]           device (dim-major)
+ *   lk_pool        [n_pages, page_size, r]                 device
+ *   lv_pool        [n_pages, r, page_size]                 device (rank-major)
+ *   block_table    [n_ctx, max_blocks] int32               device
+ *                  logical token t of context c is in page
+ *                  block_table[c][t / page_size], slot t % page_size; the base
+ *                  and LR pools share page ids.  Ids outside [0, n_pages) are
+ *                  clamped so reads stay in bounds (the result for that context
+ *                  is then unspecified).
+ *   ctx_len        [n_ctx] int32, 0 <= ctx_len[c] <= max_ctx_len,
+ *                  max_ctx_len <= max_blocks * page_size   device
+ *                  The newest token is part of the context; a context of
+ *                  length 0 yields zero output rows.
+ *   b_k, b_v       [n_agents, r, H_kv * d]; head h uses columns h*d .. h*d+d-1
+ *   out            [n_req, H_q, d]                          device
+ *   workspace      device scratch of at least
+ *                  lra_attn_decode_workspace_size(...) bytes.  It must be
+ *                  zero-filled before its first use; every completed call leaves
+ *                  its counters at zero again, so it can be reused by later
+ *                  calls on the same stream without clearing.  Calls that share
+ *                  one workspace must not run concurrently.
+ */
+size_t lra_attn_decode_workspace_size(const lra_dims* dims, int32_t n_req, int32_t n_ctx,
+                                      int32_t max_req_per_ctx, int32_t max_ctx_len);
+
+lra_status lra_attn_decode(const lra_dims* dims,
+                           const void* q, int32_t n_req,
+                           const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
+                           const int32_t* req_agent,
+                           const void* k_pool, const void* v_pool,
+                           const void* lk_pool, const void* lv_pool,
+                           int32_t n_pages, int32_t page_size,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* ctx_len, int32_t max_ctx_len,
+                           const void* b_k, const void* b_v, int32_t n_agents,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Chunked prefill over one shared context (LRAgent §3: agents compute only the
+ * newly appended context; App. B: accumulated length L = L_p + L_c; App. D.1:
+ * key adapter rebuilt before RoPE).  The q_len new tokens are the last q_len
+ * of the kv_len cached tokens (their base and LR rows are already written) and
+ * attend causally: new token i sits at position kv_len - q_len + i and sees
+ * keys 0 .. kv_len - q_len + i.
+ *
+ *   q          [n_req, q_len, H_q, d]          device
+ *   req_agent  [n_req] int32 in [0, n_agents)  device
+ *   k_base     [H_kv, kv_len, d]               device
+ *   v_base     [H_kv, kv_len, d]               device
+ *   l_k, l_v   [kv_len, r]                     device
+ *   b_k, b_v   [n_agents, r, H_kv * d]         device
+ *   rope_cos,
+ *   rope_sin   NULL (no rotation of the adapter key term) or both
+ *              [kv_len, d/2] fp32 device tables of cos/sin(pos * theta^(-2i/d))
+ *              (see lra_rope_table_build).  K_base is expected already rotated;
+ *              the kernel rotates only L_k B_k (rotate-half pairing i, i+d/2)
+ *              before adding it to K_base.
+ *   out        [n_req, q_len, H_q, d]          device
+ *   Requires 1 <= q_len <= kv_len.
+ */
+lra_status lra_attn_prefill(const lra_dims* dims,
+                            const void* q, int32_t n_req, int32_t q_len,
+                            const int32_t* req_agent,
+                            const void* k_base, const void* v_base, int32_t kv_len,
+                            const void* l_k, const void* l_v,
+                            const void* b_k, const void* b_v, int32_t n_agents,
+                            const float* rope_cos, const float* rope_sin,
+                            void* out, void* stream);
+
+/*
+ * Shared low-rank cache rows for new tokens (PReCache PreLRShared; LRAgent §3
+ * BaseLRShared with shared A):  L_k[row_offset + i] = x[i] A_k,
+ * L_v[row_offset + i] = x[i] A_v  for i < n_tok, i.e. L = X A.
+ *
+ *   x          [n_tok, d_model]   device
+ *   a_k, a_v   [rank, d_model]    device: the down-projections stored as
+ *              out x in (row t is column t of A), the usual layout of a LoRA
+ *              "A" weight
+ *   l_k, l_v   [>= row_offset + n_tok, rank], rows written in place  device
+ *   Requires d_model % 32 == 0.  bf16 results are rounded to nearest even.
+ */
+lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,
+                              const void* a_k, const void* a_v, int32_t rank,
+                              void* l_k, void* l_v, int64_t row_offset, void* stream);
+
+/*
+ * RoPE tables for the prefill: cos/sin of pos * theta^(-2i/d), pos in
+ * [0, n_pos), i in [0, head_dim/2), computed in fp64 and stored as fp32,
+ * row-major [n_pos, head_dim/2].  (LRAgent App. D.1 names RoPE; the frequency
+ * formula is the standard rotary one.)
+ */
+lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos,
+                                float* cos_out, float* sin_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRA_ATTN_H */

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry
+point, and rejects bad scalar arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_shared_base_amd as lra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lra_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lra.lib_path),
+                                reason="liblra_attn.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lra_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(lra.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(lra.lib_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = lra.load()
+    assert lra.abi_version() == 1
+    for s in range(7):
+        assert lib.lra_status_str(s).decode().startswith("LRA_")
+    assert b"unknown" in lib.lra_status_str(99)
+
+
+# Fake but 16-byte-aligned non-null addresses: validation must fail before any use.
+A = ctypes.c_void_p(0x100000)
+
+
+def dims(h_q=32, h_kv=8, d=128, r=16, dt=1, scale=0.0):
+    return lra.Dims(h_q, h_kv, d, r, dt, scale)
+
+
+def call_decode(dm, **over):
+    lib = lra.load()
+    # 4 contexts x 8192 tokens, 4 requests each: several chunks per unit, so the
+    # call needs a workspace and every case below fails validation before launch.
+    args = dict(q=A, n_req=16, crs=A, n_ctx=4, mrpc=4, agent=A, k=A, v=A, lk=A, lv=A,
+                n_pages=2048, page=16, bt=A, max_blocks=512, clen=A, max_ctx=8192, bk=A, bv=A,
+                n_agents=4, out=A, ws=A, ws_bytes=1 << 30)
+    args.update(over)
+    st = lib.lra_attn_decode(ctypes.byref(dm), args["q"], args["n_req"], args["crs"], args["n_ctx"],
+                             args["mrpc"], args["agent"], args["k"], args["v"], args["lk"],
+                             args["lv"], args["n_pages"], args["page"], args["bt"],
+                             args["max_blocks"], args["clen"], args["max_ctx"], args["bk"],
+                             args["bv"], args["n_agents"], args["out"], args["ws"],
+                             args["ws_bytes"], None)
+    return st, lib.lra_last_error().decode()
+
+
+@pytest.mark.parametrize("dm,over,want", [
+    (dims(d=96), {}, 3),
+    (dims(r=4), {}, 3),
+    (dims(dt=2), {}, 3),
+    (dims(h_q=30, h_kv=8), {}, 2),
+    (dims(h_q=0), {}, 2),
+    (dims(h_q=64, h_kv=2), {}, 3),          # g = 32 > 16 rows of one bf16 tile
+    (dims(scale=float("nan")), {}, 2),
+    (dims(), {"page": 32}, 3),
+    (dims(), {"n_req": -1}, 2),
+    (dims(), {"n_ctx": 0}, 2),
+    (dims(), {"mrpc": 0}, 2),
+    (dims(), {"mrpc": 17}, 2),
+    (dims(), {"n_pages": 0}, 2),
+    (dims(), {"max_ctx": 8193}, 2),          # > max_blocks * page
+    (dims(), {"max_ctx": -1}, 2),
+    (dims(), {"n_agents": 0}, 2),
+    (dims(), {"q": None}, 1),
+    (dims(), {"bt": None}, 1),
+    (dims(), {"out": None}, 1),
+    (dims(), {"k": ctypes.c_void_p(0x100008)}, 4),
+    (dims(), {"ws_bytes": 1}, 5),
+    (dims(), {"ws": None}, 1),
+])
+def test_decode_validation(dm, over, want):
+    st, msg = call_decode(dm, **over)
+    assert st == want, msg
+    assert msg
+
+
+def test_decode_null_dims():
+    lib = lra.load()
+    st = lib.lra_attn_decode(None, A, 1, A, 1, 1, A, A, A, A, A, 1, 16, A, 1, A, 16, A, A, 1, A,
+                             A, 0, None)
+    assert st == 1
+
+
+def call_prefill(dm, **over):
+    lib = lra.load()
+    a = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, kv_len=256, lk=A, lv=A, bk=A, bv=A,
+             n_agents=2, cos=None, sin=None, out=A)
+    a.update(over)
+    st = lib.lra_attn_prefill(ctypes.byref(dm), a["q"], a["n_req"], a["q_len"], a["agent"], a["k"],
+                              a["v"], a["kv_len"], a["lk"], a["lv"], a["bk"], a["bv"],
+                              a["n_agents"], a["cos"], a["sin"], a["out"], None)
+    return st, lib.lra_last_error().decode()
+
+
+@pytest.mark.parametrize("over,want", [
+    ({"q_len": 0}, 2),
+    ({"kv_len": 15}, 2),
+    ({"n_agents": 0}, 2),
+    ({"cos": A}, 1),
+    ({"v": None}, 1),
+    ({"lk": ctypes.c_void_p(0x100004)}, 4),
+    ({"n_req": -3}, 2),
+])
+def test_prefill_validation(over, want):
+    st, msg = call_prefill(dims(), **over)
+    assert st == want, msg
+
+
+def test_prefill_zero_requests_is_a_no_op():
+    assert call_prefill(dims(), n_req=0)[0] == 0
+
+
+def test_lr_build_validation():
+    lib = lra.load()
+
+    def call(**o):
+        a = dict(dt=1, x=A, n_tok=16, d_model=4096, ak=A, av=A, r=16, lk=A, lv=A, off=0)
+        a.update(o)
+        return lib.lra_lr_cache_build(a["dt"], a["x"], a["n_tok"], a["d_model"], a["ak"], a["av"],
+                                      a["r"], a["lk"], a["lv"], a["off"], None)
+
+    assert call(r=12) == 3
+    assert call(dt=5) == 3
+    assert call(d_model=100) == 3
+    assert call(d_model=0) == 2
+    assert call(n_tok=-1) == 2
+    assert call(off=-1) == 2
+    assert call(x=None) == 1
+    assert call(av=ctypes.c_void_p(0x100002)) == 4
+    assert call(n_tok=0) == 0
+
+
+def test_rope_table_validation():
+    lib = lra.load()
+    assert lib.lra_rope_table_build(-1.0, 128, 10, A, A, None) == 2
+    assert lib.lra_rope_table_build(1e4, 127, 10, A, A, None) == 2
+    assert lib.lra_rope_table_build(1e4, 128, 10, None, A, None) == 1
+    assert lib.lra_rope_table_build(1e4, 128, 0, A, A, None) == 0
+
+
+def test_workspace_size_queries():
+    lib = lra.load()
+    dm = dims()
+    # 4 contexts x 8192 tokens, 4 requests each: split into several chunks -> workspace needed
+    ws = lib.lra_attn_decode_workspace_size(ctypes.byref(dm), 16, 4, 4, 8192)
+    assert ws > 0
+    # the workspace grows with (d + r + 2) floats per partial row, never with kv_len * d
+    ws_small = lib.lra_attn_decode_workspace_size(ctypes.byref(dm), 16, 4, 4, 128)
+    assert ws_small == 0  # a single chunk per unit needs no partials
+    assert lib.lra_attn_decode_workspace_size(ctypes.byref(dims(dt=0)), 16, 4, 4, 8192) == 0
+    assert lib.lra_attn_decode_workspace_size(ctypes.byref(dims(d=96)), 16, 4, 4, 8192) == 0

@@ -1,0 +1,146 @@
+"""GPU parity of paged decode (lra_attn_decode) against the float64 oracle."""
+import os
+
+import numpy as np
+import pytest
+
+import workloads as w
+from gpu_helpers import (DELTA_REL_L2, DecodeDev, assert_parity, host, metrics, oracle_decode)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, requests=None, label=""):
+    d = DecodeDev(case)
+    got = host(d.run())
+    ref = oracle_decode(case, requests=requests)
+    sel = slice(None) if requests is None else list(requests)
+    print(f"[decode] {label or case.name}: ", end="", flush=True)
+    ma, rel = assert_parity(got[sel], ref[sel], case.dtype, label or case.name)
+    print(f"max-abs {ma:.2e} rel-L2 {rel:.2e} |O|inf {np.max(np.abs(ref[sel])):.3f}", flush=True)
+    return d, got, ref
+
+
+def test_cfg1_decode_fp32():
+    dec, _ = w.config1()
+    _check(dec)
+
+
+def test_cfg2_decode_bf16_full():
+    case = w.config2()
+    d, got, ref = _check(case)
+    # adapter contribution on its own (dropping the LR path would move rel-L2 ~0.2)
+    import torch
+    got0 = host(d.run(b_k=torch.zeros_like(d.b_k), b_v=torch.zeros_like(d.b_v)))
+    ref0 = oracle_decode(case, zero_b=True)
+    _, rel = metrics(got - got0, ref - ref0)
+    assert rel <= DELTA_REL_L2, f"adapter delta rel-L2 {rel:.3e}"
+
+
+def test_cfg2_decode_peaked_queries():
+    # Q x 8: scores with sd ~ 8, so max-abs is a meaningful check as well
+    case = w.make_decode(2, dtype="bf16", ctx_lens=[8192] * 4,
+                         reqs=[(b // 4, b % 4) for b in range(16)], n_agents=4, h_q=32, h_kv=8,
+                         d=128, r=16, q_sigma=8.0, name="cfg2 peaked (q sigma 8)")
+    _check(case)
+
+
+SMALL = [
+    # (label, h_q, h_kv, d, r, ctx_lens, reqs_per_ctx)
+    ("g4 d128 r16 ragged", 32, 8, 128, 16, [1, 17, 33, 100, 257, 1000], 2),
+    ("g1 d64 r8", 8, 8, 64, 8, [5, 16, 31, 129], 3),
+    ("g8 d128 r32", 16, 2, 128, 32, [15, 64, 200, 2049], 1),
+    ("g4 d64 r16 multi row-group", 4, 1, 64, 16, [300, 48], 6),
+    ("g2 d128 r8", 8, 4, 128, 8, [2, 1500], 5),
+    ("g16 d64 r32", 16, 1, 64, 32, [77, 4096], 1),
+]
+
+
+@pytest.mark.parametrize("label,h_q,h_kv,d,r,lens,rpc", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_small_shuffled(label, h_q, h_kv, d, r, lens, rpc):
+    n_agents = 3
+    reqs = [(c, (c + i) % n_agents) for c in range(len(lens)) for i in range(rpc)]
+    case = w.make_decode(17, dtype="bf16", ctx_lens=lens, reqs=reqs, n_agents=n_agents, h_q=h_q,
+                         h_kv=h_kv, d=d, r=r, shuffle=True, name=label)
+    _check(case)
+
+
+def test_decode_fp32_ragged():
+    reqs = [(0, 0), (0, 1), (1, 1), (2, 0)]
+    case = w.make_decode(19, dtype="f32", ctx_lens=[1, 45, 300], reqs=reqs, n_agents=2, h_q=8,
+                         h_kv=2, d=128, r=32, shuffle=True, b_sigma=0.1, name="fp32 ragged")
+    _check(case)
+
+
+def test_decode_split_count_invariance():
+    reqs = [(c, c % 3) for c in range(3) for _ in range(2)]
+    case = w.make_decode(23, dtype="bf16", ctx_lens=[3000, 1111, 4096], reqs=reqs, n_agents=3,
+                         h_q=32, h_kv=8, d=128, r=16, shuffle=True, name="split invariance")
+    d = DecodeDev(case)
+    outs = []
+    try:
+        for chunk in ("128", "384", "1024", "4096"):
+            os.environ["LRA_DECODE_CHUNK"] = chunk
+            outs.append(host(d.run()))
+    finally:
+        os.environ.pop("LRA_DECODE_CHUNK", None)
+    ref = oracle_decode(case)
+    for o in outs:
+        assert_parity(o, ref, "bf16", "split invariance")
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 4e-3
+
+
+def test_decode_workspace_reuse_and_empty_context():
+    import torch
+    reqs = [(0, 0), (1, 1), (1, 0), (2, 1)]
+    case = w.make_decode(29, dtype="bf16", ctx_lens=[5000, 0, 2500], reqs=reqs, n_agents=2,
+                         h_q=32, h_kv=8, d=128, r=16, shuffle=True, name="empty ctx")
+    d = DecodeDev(case)
+    import attention_shared_base_amd as lra
+    ws = torch.zeros(lra.decode_workspace_size(
+        n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=4, n_ctx=3,
+        max_req_per_ctx=d.max_req_per_ctx, max_ctx_len=d.max_ctx_len), dtype=torch.uint8,
+        device="cuda")
+    assert ws.numel() > 0
+    a = host(d.run(workspace=ws))
+    b = host(d.run(workspace=ws))
+    c = host(d.run(workspace=ws))
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert np.all(a[1:3] == 0.0)  # requests on the empty context
+    ref = oracle_decode(case, requests=[0, 3])
+    assert_parity(a[[0, 3]], ref[[0, 3]], "bf16", "non-empty contexts")
+
+
+def test_decode_row_sum_via_constant_values():
+    import torch
+    reqs = [(0, 0), (0, 1), (1, 1)]
+    case = w.make_decode(31, dtype="bf16", ctx_lens=[999, 4000], reqs=reqs, n_agents=2, h_q=32,
+                         h_kv=8, d=128, r=16, shuffle=True, name="row sum")
+    case.v_pool[:] = w.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    d = DecodeDev(case)
+    out = host(d.run(b_v=torch.zeros_like(d.b_v)))
+    assert np.max(np.abs(out - 1.0)) <= 2.0 ** -7
+
+
+def test_decode_agent_swap_and_bv_affinity():
+    import torch
+    reqs = [(0, 0), (0, 1)]
+    case = w.make_decode(37, dtype="bf16", ctx_lens=[2222], reqs=reqs, n_agents=2, h_q=32,
+                         h_kv=8, d=128, r=16, shuffle=True, name="agent swap")
+    case.q[1] = case.q[0]
+    d = DecodeDev(case)
+    base = host(d.run())
+    swapped = host(d.run(b_k=d.b_k.flip(0).contiguous(), b_v=d.b_v.flip(0).contiguous()))
+    assert np.array_equal(base[0], swapped[1]) and np.array_equal(base[1], swapped[0])
+    o0 = host(d.run(b_v=torch.zeros_like(d.b_v)))
+    o2 = host(d.run(b_v=(d.b_v.float() * 2).to(torch.bfloat16)))
+    # affine in B_v at fixed B_k (up to the bf16 rounding of the outputs)
+    assert np.max(np.abs((o2 - base) - (base - o0))) < 3 * 2.0 ** -8 * max(1.0, np.max(np.abs(o2)))
+
+
+def test_cfg4_paged_decode_sampled():
+    case = w.config4()
+    lens = case.ctx_len
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 18})
+    _check(case, requests=sample, label=f"cfg4 sampled requests {sample}")

@@ -112,7 +112,7 @@ class PrefillCase:
 class LRBuildCase:
     dtype: str
     x: np.ndarray    # [n_tok, d_model]
-    a_k: np.ndarray  # [d_model, r]
+    a_k: np.ndarray  # [r, d_model]  (LoRA A weight layout, out x in: L = X a_k^T)
     a_v: np.ndarray
     name: str = ""
 
@@ -186,8 +186,8 @@ def make_lr_build(seed, *, dtype, n_tok, d_model, r, a_sigma=None, name="", laye
     return LRBuildCase(
         dtype=dtype,
         x=draw(seed, TAG_X, (n_tok, d_model), 1.0, dtype, layer),
-        a_k=draw(seed, TAG_AK, (d_model, r), a_sigma, dtype, layer),
-        a_v=draw(seed, TAG_AV, (d_model, r), a_sigma, dtype, layer),
+        a_k=draw(seed, TAG_AK, (r, d_model), a_sigma, dtype, layer),
+        a_v=draw(seed, TAG_AV, (r, d_model), a_sigma, dtype, layer),
         name=name)
 
 

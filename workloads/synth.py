@@ -133,3 +133,19 @@ def paginate(kv, lr, page_ids, n_pages, page):
         kvp[page_ids[blk], :, :n, :] = kv[:, t0:t0 + n, :]
         lrp[page_ids[blk], :n, :] = lr[t0:t0 + n, :]
     return kvp, lrp
+
+
+def decode_device_layout(k_pool, v_pool, lk_pool, lv_pool):
+    """Reorder logical page pools into the decode kernel's page layouts.
+
+    Logical: K, V ``[n_pages, H_kv, page, d]``; L_k, L_v ``[n_pages, page, r]``.
+    Device:  K ``[n_pages, H_kv, d/8, page, 8]``, V ``[n_pages, H_kv, d, page]``,
+             L_k ``[n_pages, page, r]``, L_v ``[n_pages, r, page]``.
+    Pure data movement (same values, different order).
+    """
+    n_pages, h_kv, page, d = k_pool.shape
+    k = np.ascontiguousarray(k_pool.reshape(n_pages, h_kv, page, d // 8, 8).transpose(0, 1, 3, 2, 4))
+    v = np.ascontiguousarray(v_pool.transpose(0, 1, 3, 2))
+    lk = np.ascontiguousarray(lk_pool)
+    lv = np.ascontiguousarray(lv_pool.transpose(0, 2, 1))
+    return k, v, lk, lv
