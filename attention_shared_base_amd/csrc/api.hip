@@ -85,18 +85,17 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     const long long units = (long long)n_ctx * p->n_rg * d.n_kv_heads;
     if (units > (1 << 26)) return false;
     p->n_units = (int)units;
-    // Chunk length: enough workgroups to fill 256 CUs a few times over, each
-    // still streaming several 32-token steps per wavefront.
+    // Chunk length (tokens per workgroup, a power of two in [256, 2048] so the
+    // kernel's per-wavefront step count is a compile-time constant): enough
+    // workgroups to fill 256 CUs a few times over, each wavefront still
+    // streaming several 32-token steps.
     int chunk = env_int("LRA_DECODE_CHUNK", 0);
-    if (chunk <= 0) {
+    if (chunk != 256 && chunk != 512 && chunk != 1024 && chunk != 2048) {
         const int target = env_int("LRA_DECODE_TARGET_WG", 512);
-        long long c = ((long long)max_ctx_len * units + target - 1) / (target > 0 ? target : 512);
-        c = ((c + 127) / 128) * 128;
-        if (c < 128) c = 128;
-        if (c > 1024) c = 1024;
-        chunk = (int)c;
+        const long long c = ((long long)max_ctx_len * units + target - 1) / (target > 0 ? target : 512);
+        chunk = 256;
+        while (chunk < 1024 && chunk < c) chunk *= 2;
     }
-    chunk = ((chunk + 127) / 128) * 128;
     p->chunk = chunk;
     p->n_split = max_ctx_len > 0 ? (max_ctx_len + chunk - 1) / chunk : 1;
     const long long wgs = units * p->n_split;

@@ -20,7 +20,7 @@
 // wavefront streams 32 tokens (two 16-token pages) per step with its own
 // online-softmax state, and the four are merged through LDS.  When a unit has
 // several chunks, partial (m, l, O_base[d], O_lr[r]) rows go to the workspace
-// and the last workgroup to finish the unit merges them (log-sum-exp) and
+// and the last workgroup of the unit to finish merges them (log-sum-exp) and
 // applies B_v — never a [tokens, d] expansion of the adapter term.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16; 16 tokens x 16 rows per tile):
@@ -33,6 +33,8 @@
 // registers.  The page layouts of the boundary are chosen so every operand is
 // one direct, coalesced global load: K pages [d/8][16][8], V pages dim-major
 // [d][16], L_k [16][r], L_v rank-major [r][16].  No LDS in the streaming loop.
+#include <stdlib.h>
+
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -59,7 +61,7 @@ struct DecodeK {
     int32_t* ws_count;
     float* ws_part;
     int32_t n_ctx, n_pages, max_blocks, n_agents;
-    int32_t h_q, h_kv, g, rpg, n_rg, n_split, chunk;
+    int32_t h_q, h_kv, g, rpg, n_rg, n_split;
     float scale_log2;
 };
 
@@ -70,6 +72,22 @@ struct DecodeK {
 // elements on gfx950, so r <= 16 is zero-padded to k = 32 instead (slots 0-3
 // of each k-group carry ranks 4*q4 + v, slots 4-7 carry ranks 16 + 4*q4 + v
 // or zeros).
+
+template <int D, int R, int SP>
+__device__ __forceinline__ void finalize_rows_impl(const DecodeK& a, const float (*o)[SP],
+                                                   const float* L_row, int n, int cl, int nrows,
+                                                   int req0, int h);
+
+template <int D, int R, int SP>
+__device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)[SP], const float* L_row,
+                                              int n, int cl, int nrows, int req0, int h) {
+    finalize_rows_impl<D, R, SP>(a, o, L_row, n, cl, nrows, req0, h);
+}
+
+template <int D, int R, int SP>
+__device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
+                                               int n, int cl, float (*o_out)[SP], float* L_out,
+                                               float (*sm_w)[16]);
 
 template <int D, int R>
 struct Step {
@@ -82,24 +100,31 @@ struct Step {
     bf16x4 lv[2][NRT];
 };
 
-template <int D, int R>
+// SPW = 32-token steps per wavefront; a workgroup covers WAVES * SPW * 32 tokens.
+// DEPTH = step buffers per wavefront (DEPTH - 1 steps of loads in flight).
+template <int D, int R, int SPW, int DEPTH>
 __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
     constexpr int NJ = Step<D, R>::NJ;
     constexpr int NDT = Step<D, R>::NDT;
     constexpr int NRT = Step<D, R>::NRT;
     constexpr int DR = D + R;
     constexpr int SP = DR + 1;  // LDS row pitch (odd: no bank aliasing across rows)
+    constexpr int CHUNK = WAVES * SPW * KEYS_PER_STEP;
 
     __shared__ float sm_o[WAVES][ROWS][SP];
     __shared__ float sm_m[WAVES][ROWS];
     __shared__ float sm_l[WAVES][ROWS];
     __shared__ float sm_M[ROWS];
     __shared__ float sm_L[ROWS];
+    __shared__ float sm_w[64][ROWS];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform by construction; readfirstlane lets the compiler see it, so
+    // page-table reads become scalar loads that never wait on the vector loads
+    // in flight (a vector page-id load would force a full vmcnt(0) drain).
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15;  // row (S^T / O^T column) of this lane
     const int q4 = lane >> 4;   // k-group of this lane
 
@@ -136,10 +161,65 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         }
         return;
     }
-    const int n_active = (len + a.chunk - 1) / a.chunk;
+    const int n_active = (len + CHUNK - 1) / CHUNK;
     if (split >= n_active) return;
-    const int kbeg = split * a.chunk;
-    const int kend = min(len, kbeg + a.chunk);
+    const int kbeg = split * CHUNK;
+    const int kend = min(len, kbeg + CHUNK);
+
+    // ---- page ids of this wavefront's steps (scalar loads).  Pages past the
+    // chunk end are clamped to its last page: those steps load cached data and
+    // are never computed, so the loads can stay unconditional.
+    const int* bt = a.block_table + (size_t)ctx * a.max_blocks;
+    const int last_pg = (kend - 1) >> 4;
+    int pid[SPW][2];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int pg = (kbeg >> 4) + 2 * (wave + WAVES * i);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pid[i][t] = min(max(bt[min(pg + t, last_pg)], 0), a.n_pages - 1);
+    }
+
+    const size_t kv_page = (size_t)a.h_kv * D * PAGE;  // elements per page (all heads)
+    const bf16* kbase = a.k_pool + (size_t)h * D * PAGE;
+    const bf16* vbase = a.v_pool + (size_t)h * D * PAGE;
+
+    // Loads of one step: no data-dependent branches; dead slots are masked later.
+    auto load = [&](Step<D, R>& T, int i) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bf16* kp = kbase + (size_t)pid[i][t] * kv_page;
+            const bf16* vp = vbase + (size_t)pid[i][t] * kv_page;
+            const bf16* lkp = a.lk_pool + (size_t)pid[i][t] * PAGE * R;
+            const bf16* lvp = a.lv_pool + (size_t)pid[i][t] * PAGE * R;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                T.k[t][j] = ldg_stream((const bf16x8*)(kp + ((4 * j + q4) * PAGE + n16) * 8));
+            if constexpr (R == 32) {
+                T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)),
+                               ldg((const bf16x4*)(lkp + n16 * R + 16 + 4 * q4)));
+            } else if constexpr (R == 16) {
+                T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)), zero4());
+            } else {
+                T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * (q4 & 1))), zero4());
+                if (q4 >= 2) T.lk[t] = zero8();
+            }
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                T.v[t][dt] = ldg_stream((const bf16x4*)(vp + (16 * dt + n16) * PAGE + 4 * q4));
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int rank = min(16 * rt + n16, R - 1);
+                T.lv[t][rt] = ldg((const bf16x4*)(lvp + rank * PAGE + 4 * q4));
+            }
+        }
+    };
+
+    // ---- the first DEPTH-1 steps' loads go out before the prologue's dependent chain
+    Step<D, R> buf[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i)
+        if (i < SPW) load(buf[i], i);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- query operand (B of the score MFMA): lane holds dims 32j+8*q4.. of row n16
     const bool row_ok = n16 < nrows;
@@ -162,12 +242,15 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             const int rank = 16 * rt + n16;
-            const bf16* bp_ = a.b_k + ((size_t)agent * R + rank) * ((size_t)a.h_kv * D) +
+            const bf16* bp_ = a.b_k + ((size_t)agent * R + min(rank, R - 1)) * ((size_t)a.h_kv * D) +
                               (size_t)h * D + 8 * q4;
             f32x4 c = zf4();
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                c = mfma16x16x32(rank < R ? ldg((const bf16x8*)(bp_ + 32 * j)) : zero8(), qf[j], c);
+            for (int j = 0; j < NJ; ++j) {
+                bf16x8 bk = ldg((const bf16x8*)(bp_ + 32 * j));
+                if (rank >= R) bk = zero8();
+                c = mfma16x16x32(bk, qf[j], c);
+            }
             if (n16 / g == s) qbacc[rt] = c;
         }
     }
@@ -177,59 +260,6 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         qb[v] = (bf16)qbacc[0][v];
         qb[4 + v] = (R == 32) ? (bf16)qbacc[NRT - 1][v] : (bf16)0.0f;
     }
-
-    // ---- streaming loop
-    const int* bt = a.block_table + (size_t)ctx * a.max_blocks;
-    const int n_steps = (kend - kbeg + KEYS_PER_STEP - 1) / KEYS_PER_STEP;
-    const size_t kv_page = (size_t)a.h_kv * D * PAGE;  // elements per page (all heads)
-    const bf16* kbase = a.k_pool + (size_t)h * D * PAGE;
-    const bf16* vbase = a.v_pool + (size_t)h * D * PAGE;
-
-    auto load = [&](Step<D, R>& T, int st) {
-        const int key0 = kbeg + st * KEYS_PER_STEP;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int pg = (key0 >> 4) + t;
-            const bool live = pg * PAGE < kend;
-            int pid = live ? bt[pg] : 0;
-            pid = min(max(pid, 0), a.n_pages - 1);
-            const bf16* kp = kbase + (size_t)pid * kv_page;
-            const bf16* vp = vbase + (size_t)pid * kv_page;
-            const bf16* lkp = a.lk_pool + (size_t)pid * PAGE * R;
-            const bf16* lvp = a.lv_pool + (size_t)pid * PAGE * R;
-            if (live) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    T.k[t][j] = ldg_stream((const bf16x8*)(kp + ((4 * j + q4) * PAGE + n16) * 8));
-                if constexpr (R == 32) {
-                    const bf16x4 lo = ldg((const bf16x4*)(lkp + n16 * R + 4 * q4));
-                    const bf16x4 hi = ldg((const bf16x4*)(lkp + n16 * R + 16 + 4 * q4));
-                    T.lk[t] = cat4(lo, hi);
-                } else if constexpr (R == 16) {
-                    T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)), zero4());
-                } else {
-                    T.lk[t] = cat4(q4 < 2 ? ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)) : zero4(),
-                                   zero4());
-                }
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-                    T.v[t][dt] = ldg_stream((const bf16x4*)(vp + (16 * dt + n16) * PAGE + 4 * q4));
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) {
-                    const int rank = 16 * rt + n16;
-                    T.lv[t][rt] = rank < R ? ldg((const bf16x4*)(lvp + rank * PAGE + 4 * q4)) : zero4();
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) T.k[t][j] = zero8();
-                T.lk[t] = zero8();
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) T.v[t][dt] = zero4();
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) T.lv[t][rt] = zero4();
-            }
-        }
-    };
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -241,8 +271,7 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
     for (int rt = 0; rt < NRT; ++rt) acc_lr[rt] = zf4();
     const float sl2 = a.scale_log2;
 
-    auto compute = [&](Step<D, R>& T, int st) {
-        const int key0 = kbeg + st * KEYS_PER_STEP;
+    auto compute = [&](Step<D, R>& T, int key0) {
         f32x4 s[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -251,28 +280,39 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
             for (int j = 0; j < NJ; ++j) s[t] = mfma16x16x32(T.k[t][j], qf[j], s[t]);
             s[t] = mfma16x16x32(T.lk[t], qb, s[t]);
         }
-        const bool tail = key0 + KEYS_PER_STEP > kend;
+        // Tokens at or past the chunk end: score -inf, and their values zeroed
+        // (unused page slots may hold anything, even NaN bits, and 0 * NaN is
+        // NaN).  Branch-free on purpose: a branch here makes the compiler drain
+        // every load in flight before the value MFMAs.
         float x[8];
         float mx = -INFINITY;
+        uint32_t keep[2][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+            bool ok[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                float val = s[t][v] * sl2;
-                if (tail && key0 + 16 * t + 4 * q4 + v >= kend) val = -INFINITY;
+                ok[v] = key0 + 16 * t + 4 * q4 + v < kend;
+                const float val = ok[v] ? s[t][v] * sl2 : -INFINITY;
                 x[4 * t + v] = val;
                 mx = fmaxf(mx, val);
             }
+            keep[t][0] = (ok[0] ? 0x0000ffffu : 0u) | (ok[1] ? 0xffff0000u : 0u);
+            keep[t][1] = (ok[2] ? 0x0000ffffu : 0u) | (ok[3] ? 0xffff0000u : 0u);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);  // finite: every step holds a live token
-        const float alpha = fast_exp2(m_run - m_new);
+        // A step past the chunk end (all tokens dead) leaves the state as it
+        // is: alpha = 1 and p = 0, also while nothing has been seen yet.
+        const float m_new = fmaxf(m_run, mx);
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.0f : fast_exp2(m_run - m_new);
         m_run = m_new;
         float ps = 0.f;
         bf16x8 pb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float p = fast_exp2(x[i] - m_new);
+            const float p = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - m_new);
             ps += p;
             pb[i] = (bf16)p;
         }
@@ -281,42 +321,34 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) acc_lr[rt] *= alpha;
-        if (tail) {
-            // Tokens past the chunk end may hold anything (even NaN bits in
-            // unused page slots): zero their values so 0 * NaN cannot appear.
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    if (key0 + 16 * t + 4 * q4 + v >= kend) {
+            for (int dt = 0; dt < NDT; ++dt) T.v[t][dt] = and_mask(T.v[t][dt], keep[t][0], keep[t][1]);
 #pragma unroll
-                        for (int dt = 0; dt < NDT; ++dt) T.v[t][dt][v] = (bf16)0.0f;
+            for (int rt = 0; rt < NRT; ++rt) T.lv[t][rt] = and_mask(T.lv[t][rt], keep[t][0], keep[t][1]);
+        }
 #pragma unroll
-                        for (int rt = 0; rt < NRT; ++rt) T.lv[t][rt][v] = (bf16)0.0f;
-                    }
-                }
+        for (int rt = 0; rt < NRT; ++rt) {
+            bf16x8 lvop = cat4(T.lv[0][rt], T.lv[1][rt]);
+            if (16 * rt + n16 >= R) lvop = zero8();
+            acc_lr[rt] = mfma16x16x32(lvop, pb, acc_lr[rt]);
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma16x16x32(cat4(T.v[0][dt], T.v[1][dt]), pb, acc[dt]);
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-            acc_lr[rt] = mfma16x16x32(cat4(T.lv[0][rt], T.lv[1][rt]), pb, acc_lr[rt]);
     };
 
-    {
-        Step<D, R> A, B;
-        int st = wave;
-        if (st < n_steps) load(A, st);
-        while (st < n_steps) {
-            const int nx = st + WAVES;
-            if (nx < n_steps) load(B, nx);
-            compute(A, st);
-            if (nx >= n_steps) break;
-            const int nx2 = nx + WAVES;
-            if (nx2 < n_steps) load(A, nx2);
-            compute(B, nx);
-            st = nx2;
-        }
+    // ---- streaming: the loads of steps i+1 .. i+DEPTH-1 are in flight while step i
+    // computes (fully unrolled, so every buffer index is static and the step
+    // buffers live in VGPRs/AGPRs without copies).
+    // No branches in this loop and a scheduling barrier after each batch of
+    // loads: the compiler may neither sink the loads towards their use nor
+    // merge control flow (either makes it drain every load in flight).
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        if (i + DEPTH - 1 < SPW) load(buf[(i + DEPTH - 1) % DEPTH], i + DEPTH - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[i % DEPTH], kbeg + (wave + WAVES * i) * KEYS_PER_STEP);
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
@@ -368,72 +400,159 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         }
     }
 
-    if (a.n_split > 1) {
+    if (n_active > 1) {
         // ---- partial row -> workspace; the last workgroup of the unit merges.
+        //
+        // Cross-workgroup protocol without an L2 write-back: partials are
+        // written and read as agent-scope relaxed atomics (coherent across the
+        // XCDs' L2s), the workgroup-scope release waits until every store of
+        // this wavefront has completed at that coherence level, the barrier
+        // extends that to the whole workgroup, and only then is the counter
+        // bumped.  The workgroup that sees the count reach n_active - 1 reads
+        // every partial back with agent-scope loads.  (An agent-scope release
+        // fence instead would write back the whole L2 once per workgroup,
+        // which serialises across the GPU.)
         __syncthreads();
-        float* part = a.ws_part + ((size_t)unit * a.n_split + split) * ROWS * (DR + 2);
+        constexpr int PW = DR + 2;
+        float* part = a.ws_part + ((size_t)unit * a.n_split + split) * ROWS * PW;
         if (n < nrows) {
-            for (int c = cl; c < DR; c += 16) part[n * (DR + 2) + c] = sm_o[0][n][c];
+            for (int c = cl; c < DR; c += 16)
+                __hip_atomic_store(part + n * PW + c, sm_o[0][n][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (cl == 0) {
-                part[n * (DR + 2) + DR] = sm_M[n];
-                part[n * (DR + 2) + DR + 1] = sm_L[n];
+                __hip_atomic_store(part + n * PW + DR, sm_M[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(part + n * PW + DR + 1, sm_L[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         if (tid == 0) {
-            const int prev = atomicAdd(&a.ws_count[unit], 1);
-            sm_last = (prev == n_active - 1);
+            const int prev = __hip_atomic_fetch_add(a.ws_count + unit, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == n_active - 1;
         }
         __syncthreads();
         if (!sm_last) return;
-        __threadfence();
-        if (n < nrows) {
-            const float* p0 = a.ws_part + (size_t)unit * a.n_split * ROWS * (DR + 2) + n * (DR + 2);
-            const size_t sstride = (size_t)ROWS * (DR + 2);
-            float M = -INFINITY;
-            for (int sp = 0; sp < n_active; ++sp) M = fmaxf(M, p0[sp * sstride + DR]);
-            float L = 0.f;
-            for (int sp = 0; sp < n_active; ++sp) {
-                const float w = fast_exp2(p0[sp * sstride + DR] - M);
-                L += w * p0[sp * sstride + DR + 1];
-            }
-            for (int c = cl; c < DR; c += 16) {
-                float o = 0.f;
-                for (int sp = 0; sp < n_active; ++sp) {
-                    const float w = fast_exp2(p0[sp * sstride + DR] - M);
-                    o += w * p0[sp * sstride + c];
-                }
-                sm_o[0][n][c] = o;
-            }
-            if (cl == 0) {
-                sm_M[n] = M;
-                sm_L[n] = L;
-            }
-        }
-        if (tid == 0) a.ws_count[unit] = 0;  // leave the workspace clean for the next call
+        merge_partials<D, R, SP>(a, unit, n_active, nrows, n, cl, sm_o[0], sm_L, sm_w);
+        if (tid == 0) __hip_atomic_store(a.ws_count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-
-    // ---- epilogue: O = (O_base + O_lr B_v^(h)) / l, one post-multiplication per row
-    if (n < nrows) {
-        const int req = req0 + n / g;
-        int agent = a.req_agent[req];
-        agent = min(max(agent, 0), a.n_agents - 1);
-        const float L = sm_L[n];
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        const bf16* bv = a.b_v + (size_t)agent * R * a.h_kv * D + (size_t)h * D;
-        bf16* op = a.out + ((size_t)req * a.h_q + h * g + n % g) * D;
-        for (int c = cl; c < D; c += 16) {
-            float o = sm_o[0][n][c];
-#pragma unroll
-            for (int t = 0; t < R; ++t) o += sm_o[0][n][D + t] * (float)bv[(size_t)t * a.h_kv * D + c];
-            op[c] = (bf16)(o * inv);
-        }
-    }
+    finalize_rows<D, R, SP>(a, sm_o[0], sm_L, n, cl, nrows, req0, h);
 }
 
-template <int D, int R>
+// Log-sum-exp merge of the chunk partials of one work unit into o[row][0..DR)
+// and L[row]; sm_w is [GS][16] scratch.  Runs in the last workgroup to finish.
+template <int D, int R, int SP>
+__device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
+                                               int n, int cl, float (*o_out)[SP], float* L_out,
+                                               float (*sm_w)[ROWS]) {
+    constexpr int DR = D + R;
+    constexpr int PW = DR + 2;
+    constexpr int NC = (DR + 15) / 16;  // columns per thread
+    constexpr int GS = 64;              // chunks merged per pass
+    const bool row_ok = n < nrows;
+    const float* base = a.ws_part + (size_t)unit * a.n_split * ROWS * PW + n * PW;
+    const size_t sstride = (size_t)ROWS * PW;
+    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    float M = -INFINITY, L = 0.f;
+    float o[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) o[k] = 0.f;
+    for (int g0 = 0; g0 < n_active; g0 += GS) {
+        const int ns = min(GS, n_active - g0);
+        // the 16 threads of a row split the chunks for max and sum
+        float mv[GS / 16], lv[GS / 16];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < GS / 16; ++k) {
+            const int sp = cl + 16 * k;
+            const bool ok = row_ok && sp < ns;
+            mv[k] = ok ? ld(base + (g0 + sp) * sstride + DR) : -INFINITY;
+            lv[k] = ok ? ld(base + (g0 + sp) * sstride + DR + 1) : 0.f;
+            mloc = fmaxf(mloc, mv[k]);
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 16));
+        const float M_new = fmaxf(M, mloc);
+        const float resc = M == -INFINITY ? 0.f : fast_exp2(M - M_new);
+        float lloc = 0.f;
+#pragma unroll
+        for (int k = 0; k < GS / 16; ++k) {
+            const int sp = cl + 16 * k;
+            const float w = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - M_new);
+            lloc += w * lv[k];
+            if (sp < ns) sm_w[sp][n] = w;
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off, 16);
+        L = L * resc + lloc;
+        M = M_new;
+        __syncthreads();
+        if (row_ok) {
+#pragma unroll
+            for (int k = 0; k < NC; ++k) o[k] *= resc;
+            for (int sp0 = 0; sp0 < ns; sp0 += 4) {
+                float v[4][NC];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int k = 0; k < NC; ++k) {
+                        const int c = cl + 16 * k;
+                        v[u][k] = (sp0 + u < ns && c < DR) ? ld(base + (g0 + sp0 + u) * sstride + c) : 0.f;
+                    }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float w = sp0 + u < ns ? sm_w[sp0 + u][n] : 0.f;
+#pragma unroll
+                    for (int k = 0; k < NC; ++k) o[k] += w * v[u][k];
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int c = cl + 16 * k;
+        if (c < DR) o_out[n][c] = o[k];
+    }
+    if (cl == 0) L_out[n] = L;
+}
+
+// O = (O_base + O_lr B_v^(h)) / l for the rows of one work unit: the single
+// post-multiplication by B_v per query row.  `o` holds [O_base | O_lr] per row.
+template <int D, int R, int SP>
+__device__ __forceinline__ void finalize_rows_impl(const DecodeK& a, const float (*o)[SP],
+                                                   const float* L_row, int n, int cl, int nrows,
+                                                   int req0, int h) {
+    if (n >= nrows) return;
+    // thread (n, cl) owns D/16 contiguous output columns: one vector load of
+    // B_v per rank, one vector store
+    constexpr int CPT = D / 16;
+    typedef __bf16 bfv __attribute__((ext_vector_type(CPT)));
+    const int g = a.g;
+    const int req = req0 + n / g;
+    int agent = a.req_agent[req];
+    agent = min(max(agent, 0), a.n_agents - 1);
+    const float L = L_row[n];
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    const int c0 = cl * CPT;
+    const bf16* bv = a.b_v + (size_t)agent * R * a.h_kv * D + (size_t)h * D + c0;
+    float acc[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) acc[k] = o[n][c0 + k];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const bfv b = ldg((const bfv*)(bv + (size_t)t * a.h_kv * D));
+        const float w = o[n][D + t];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) acc[k] += w * (float)b[k];
+    }
+    bfv res;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) res[k] = (bf16)(acc[k] * inv);
+    *(bfv*)(a.out + ((size_t)req * a.h_q + h * g + n % g) * D + c0) = res;
+}
+
+template <int D, int R, int SPW, int DEPTH>
 lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
     DecodeK k;
     k.q = (const bf16*)a.q;
@@ -460,10 +579,34 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.rpg = p.rpg;
     k.n_rg = p.n_rg;
     k.n_split = p.n_split;
-    k.chunk = p.chunk;
     k.scale_log2 = a.scale * LRA_LOG2E;
-    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R>), dim3(p.grid), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH>), dim3(p.grid), dim3(256), 0, s, k);
     return lra::check_launch("lra_decode_bf16_kernel");
+}
+
+template <int D, int R, int DEPTH>
+lra_status launch_depth(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
+    switch (p.chunk) {
+        case 256: return launch_t<D, R, 2, (DEPTH < 2 ? DEPTH : 2)>(a, p, s);
+        case 512: return launch_t<D, R, 4, DEPTH>(a, p, s);
+        case 1024: return launch_t<D, R, 8, DEPTH>(a, p, s);
+        case 2048: return launch_t<D, R, 16, DEPTH>(a, p, s);
+        default:
+            lra::set_error("decode: unsupported chunk %d", p.chunk);
+            return LRA_ERR_UNSUPPORTED;
+    }
+}
+
+template <int D, int R>
+lra_status launch_dr(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
+    static const int depth = [] {
+        const char* e = getenv("LRA_DECODE_DEPTH");
+        const int v = e ? atoi(e) : 2;
+        return v == 2 || v == 3 || v == 4 ? v : 2;
+    }();
+    if (depth == 3) return launch_depth<D, R, 3>(a, p, s);
+    if (depth == 4) return launch_depth<D, R, 4>(a, p, s);
+    return launch_depth<D, R, 2>(a, p, s);
 }
 
 }  // namespace
@@ -473,7 +616,7 @@ namespace lra {
 lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
     const int d = a.head_dim, r = a.rank;
 #define LRA_CASE(D_, R_) \
-    if (d == D_ && r == R_) return launch_t<D_, R_>(a, p, s);
+    if (d == D_ && r == R_) return launch_dr<D_, R_>(a, p, s);
     LRA_CASE(128, 16)
     LRA_CASE(128, 32)
     LRA_CASE(128, 8)

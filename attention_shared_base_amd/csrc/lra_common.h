@@ -63,6 +63,15 @@ LRA_DEV bf16x4 zero4() {
 
 LRA_DEV f32x4 zf4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Bitwise AND of the four bf16 lanes with two 32-bit masks (elements 0-1 / 2-3).
+LRA_DEV bf16x4 and_mask(bf16x4 x, uint32_t lo, uint32_t hi) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 u = __builtin_bit_cast(u32x2, x);
+    u.x &= lo;
+    u.y &= hi;
+    return __builtin_bit_cast(bf16x4, u);
+}
+
 template <typename T>
 LRA_DEV T ldg(const T* p) { return *p; }
 

@@ -16,8 +16,9 @@ lra_status check_launch(const char* what);
 // ----------------------------------------------------------------- decode
 // Work decomposition of one decode call.  A work unit is (context, row group,
 // KV head); a row group holds up to 16 query rows = rpg requests x g heads.
-// Each unit's keys are cut into chunks of `chunk` tokens (a multiple of 128);
-// one workgroup handles one (unit, chunk).
+// Each unit's keys are cut into chunks of `chunk` tokens (256 .. 2048); one
+// workgroup handles one (unit, chunk), and the last workgroup of a unit with
+// several chunks merges their partials.
 struct DecodePlan {
     int g;          // query heads per KV head
     int rpg;        // requests per row group (16 / g)

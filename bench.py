@@ -1,0 +1,381 @@
+#!/usr/bin/env python3
+"""Throughput of Flash-LoRA-Attention on one MI355X.
+
+Primary line (the JSON ``value``): paged decode of 16 requests over 4 shared
+8192-token contexts (4 agents per context), LLaMA-3.1-8B attention shape
+(H_q 32, H_kv 8, d 128), rank 16, bf16 storage / fp32 accumulation, one
+attention layer.  One step = one ``lra_attn_decode`` call over one batch;
+value = requests (= new tokens) per second.  The roofline object is for that
+decode kernel (HBM bound): algorithmic bytes per launch / average launch time
+from HIP events on the launch stream.
+
+Extra legs in the same run (``extra``): chunked prefill with RoPE on the adapter
+key term (512 new tokens over 16384, 4 agents; TFLOP/s vs bf16 MFMA peak),
+paged decode over 32 shuffled contexts of 4k-64k tokens (GB/s vs HBM peak),
+and the LR-cache build of one 4096-token layer (GB/s).
+
+cpu_baseline: the float64 oracle on the host cores, on the primary workload's
+first input set (all 16 requests, repeated until >= 10 s), as requests/s.
+
+Inputs of sets that fit the 256 MB Infinity Cache are rotated over several
+independent buffer sets so timed calls read HBM, not the cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + HBM GB/s % peak; prefill TFLOP/s % MFMA peak (1 GPU)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+# ----------------------------------------------------------------------------- accounting
+
+def decode_bytes(ctx_len, n_req, n_agents_used, h_q, h_kv, d, r, esz=2, page=16):
+    """Algorithmic HBM bytes of one decode call.
+
+    Every context's base K/V (H_kv*d each) and shared LR rows (r each for L_k
+    and L_v) are read once — the agents of a context share them — plus the
+    queries, the referenced agents' B_k/B_v, the outputs and the index arrays
+    (block-table entries in use, lengths, request offsets, agent ids).
+    """
+    ctx_len = np.asarray(ctx_len, dtype=np.int64)
+    kv = int(ctx_len.sum()) * (2 * h_kv * d + 2 * r) * esz
+    q = n_req * h_q * d * esz
+    o = n_req * h_q * d * esz
+    b = n_agents_used * 2 * r * h_kv * d * esz
+    idx = int(((ctx_len + page - 1) // page).sum()) * 4 + len(ctx_len) * 4 + (len(ctx_len) + 1) * 4 \
+        + n_req * 4
+    return kv + q + o + b + idx
+
+
+def decode_bytes_unshared(ctx_len_per_req, h_q, h_kv, d, r, esz=2):
+    """Bytes if every request streamed its own full cache (no sharing): context only."""
+    return int(np.sum(ctx_len_per_req)) * (2 * h_kv * d + 2 * r) * esz
+
+
+def prefill_flops(n_req, q_len, kv_len, h_q, h_kv, d, r, rope):
+    """Algorithmic flops of one prefill call (causal-masked work not credited).
+
+    Per unmasked (row, key) pair: 4d (scores and values at head dimension) plus
+    the rank-r terms: 2r on the value side (P L_v) and, without RoPE, 2r on the
+    score side (qB . l_k).  With RoPE the adapter key is rebuilt at head
+    dimension instead: 2 r d per (key, KV head, request).  Per query row: 2 r d
+    for the single B_v post-multiplication, and without RoPE 2 r d for qB.
+    """
+    pairs = q_len * (kv_len - q_len) + q_len * (q_len + 1) // 2
+    rows = n_req * q_len * h_q
+    total = n_req * h_q * pairs * (4 * d + (2 * r if rope else 4 * r))
+    total += rows * 2 * r * d * (1 if rope else 2)
+    if rope:
+        total += kv_len * h_kv * n_req * 2 * r * d
+    return total
+
+
+def lr_build_bytes(n_tok, d_model, r, esz=2):
+    return (n_tok * d_model + 2 * r * d_model + 2 * n_tok * r) * esz
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+    if a.dtype == np.int32:
+        return torch.from_numpy(a).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def _randn_bf16(shape, sigma, gen):
+    import torch
+    x = torch.randn(shape, dtype=torch.float32, device="cuda", generator=gen)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(torch.bfloat16)
+
+
+def _time_calls(fn, n_sets, steps, warmup):
+    """Average time per call (ms) over `steps` calls, HIP events on the launch stream."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        fn(i % n_sets)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- legs
+
+class DecodeSet:
+    def __init__(self, case):
+        import workloads as w
+        k, v, lk, lv = w.decode_device_layout(case.k_pool, case.v_pool, case.lk_pool, case.lv_pool)
+        self.q, self.k, self.v, self.lk, self.lv = map(_dev, (case.q, k, v, lk, lv))
+        self.crs = _dev(case.ctx_req_start())
+        self.agent = _dev(case.req_agent)
+        self.bt = _dev(case.block_table)
+        self.clen = _dev(case.ctx_len)
+        self.b_k, self.b_v = _dev(case.b_k), _dev(case.b_v)
+        self.out = None
+
+
+def primary_decode(steps, warmup, n_sets):
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    cases = [w.config2(layer=i) for i in range(n_sets)]
+    sets = [DecodeSet(c) for c in cases]
+    c0 = cases[0]
+    mrpc = int(np.bincount(c0.req_ctx).max())
+    max_len = int(c0.ctx_len.max())
+    ws = torch.zeros(lra.decode_workspace_size(
+        n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=c0.n_req,
+        n_ctx=c0.n_ctx, max_req_per_ctx=mrpc, max_ctx_len=max_len), dtype=torch.uint8,
+        device="cuda")
+    for s in sets:
+        s.out = torch.empty_like(s.q)
+
+    def call(i):
+        s = sets[i]
+        lra.decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
+                   max_req_per_ctx=mrpc, max_ctx_len=max_len, out=s.out, workspace=ws)
+
+    ms = _time_calls(call, n_sets, steps, warmup)
+    nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, 16)
+    return cases[0], ms, nbytes
+
+
+def extra_paged_decode(steps, warmup):
+    """32 contexts of U[4096, 65536] tokens, shuffled 16-token pages, r 32 (5+ GB)."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    lens = w.config4_lengths()
+    table, n_pages = w.page_table(4, lens, shuffle=True, max_blocks=65536 // 16)
+    h_q, h_kv, d, r, n_req = 32, 8, 128, 32, 32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    k = _randn_bf16((n_pages, h_kv, d // 8, 16, 8), 1.0, g)
+    v = _randn_bf16((n_pages, h_kv, d, 16), 1.0, g)
+    lk = _randn_bf16((n_pages, 16, r), 1.0, g)
+    lv = _randn_bf16((n_pages, r, 16), 1.0, g)
+    q = _randn_bf16((n_req, h_q, d), 1.0, g)
+    b_k = _randn_bf16((8, r, h_kv * d), 0.05, g)
+    b_v = _randn_bf16((8, r, h_kv * d), 0.05, g)
+    crs = _dev(np.arange(33, dtype=np.int32))
+    agent = _dev((np.arange(32) % 8).astype(np.int32))
+    bt, clen = _dev(table), _dev(lens.astype(np.int32))
+    out = torch.empty_like(q)
+    max_len = int(lens.max())
+    ws = torch.zeros(lra.decode_workspace_size(
+        n_q_heads=h_q, n_kv_heads=h_kv, head_dim=d, rank=r, dtype=1, n_req=n_req, n_ctx=32,
+        max_req_per_ctx=1, max_ctx_len=max_len), dtype=torch.uint8, device="cuda")
+
+    def call(_):
+        lra.decode(q, crs, agent, k, v, lk, lv, bt, clen, b_k, b_v, max_req_per_ctx=1,
+                   max_ctx_len=max_len, out=out, workspace=ws)
+
+    ms = _time_calls(call, 1, steps, warmup)
+    nbytes = decode_bytes(lens, n_req, 8, h_q, h_kv, d, r)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "paged decode: 32 contexts of U[4096,65536] tokens (sum %d), shuffled "
+                        "16-token pages, 32 requests over 8 agents, Hq32 Hkv8 d128 r32, bf16"
+                        % int(lens.sum()),
+            "value": n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "algorithmic_bytes": nbytes}
+
+
+def extra_prefill_rope(steps, warmup, n_sets=2):
+    """512 new tokens over a 16384-token shared context, 4 agents, RoPE 5e5 on the adapter key."""
+    import torch
+    import attention_shared_base_amd as lra
+    n_req, q_len, kv_len, h_q, h_kv, d, r = 4, 512, 16896, 32, 8, 128, 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(
+            q=_randn_bf16((n_req, q_len, h_q, d), 1.0, g),
+            k=_randn_bf16((h_kv, kv_len, d), 1.0, g), v=_randn_bf16((h_kv, kv_len, d), 1.0, g),
+            lk=_randn_bf16((kv_len, r), 1.0, g), lv=_randn_bf16((kv_len, r), 1.0, g),
+            bk=_randn_bf16((4, r, h_kv * d), 0.05, g), bv=_randn_bf16((4, r, h_kv * d), 0.05, g)))
+    agent = _dev(np.arange(4, dtype=np.int32))
+    cos, sin = lra.rope_table(500000.0, d, kv_len)
+    for s in sets:
+        s["out"] = torch.empty_like(s["q"])
+
+    def call(i):
+        s = sets[i]
+        lra.prefill(s["q"], agent, s["k"], s["v"], s["lk"], s["lv"], s["bk"], s["bv"],
+                    rope_cos=cos, rope_sin=sin, out=s["out"])
+
+    ms = _time_calls(call, n_sets, steps, warmup)
+    fl = prefill_flops(n_req, q_len, kv_len, h_q, h_kv, d, r, rope=True)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": "chunked prefill: 512 new tokens over 16384 shared, 4 agents, RoPE "
+                        "theta 5e5 on the adapter key term, Hq32 Hkv8 d128 r16, bf16",
+            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None},
+            "algorithmic_flops": fl}
+
+
+def extra_lr_build(steps, warmup, n_sets=8):
+    import torch
+    import attention_shared_base_amd as lra
+    n_tok, d_model, r = 4096, 4096, 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    sets = [dict(x=_randn_bf16((n_tok, d_model), 1.0, g),
+                 ak=_randn_bf16((r, d_model), 1.0 / 64, g), av=_randn_bf16((r, d_model), 1.0 / 64, g),
+                 lk=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda"),
+                 lv=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda"))
+            for _ in range(n_sets)]
+
+    def call(i):
+        s = sets[i]
+        lra.lr_cache_build(s["x"], s["ak"], s["av"], s["lk"], s["lv"])
+
+    ms = _time_calls(call, n_sets, steps, warmup)
+    nbytes = lr_build_bytes(n_tok, d_model, r)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "LR-cache build L = X [A_k|A_v]: X [4096, 4096] bf16, r 16",
+            "value": gbs, "unit": "GB/s", "ms_per_call": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "algorithmic_bytes": nbytes}
+
+
+def cpu_baseline(case, min_seconds=10.0):
+    """The float64 oracle, as it stands, on the primary workload's first input set."""
+    import oracle
+    import workloads as w
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    args = [w.widen(x) for x in (case.q, case.k_pool, case.v_pool, case.lk_pool, case.lv_pool,
+                                 case.b_k, case.b_v)]
+    q, kp, vp, lkp, lvp, bk, bv = args
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode_paged(q, case.req_ctx, case.req_agent, kp, vp, lkp, lvp, case.block_table,
+                            case.ctx_len, bk, bv)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": reps * case.n_req / el, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"full decode call of the primary workload (16 requests x 8192 keys), "
+                      f"repeated {reps}x in {el:.1f} s, float64 NumPy"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill/paged/LR-build legs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_shared_base_amd as lra
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lra.load()
+
+    _log("primary: decode, 4 shared contexts x 8192 tokens, 16 requests")
+    case, ms, nbytes = primary_decode(args.steps, args.warmup, args.sets)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    value = case.n_req / (ms * 1e-3)
+    _log(f"primary: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, {value:.0f} tokens/s")
+
+    extra = {}
+    if not args.no_extra:
+        for name, fn in (("prefill_rope", lambda: extra_prefill_rope(max(5, args.steps // 10), 3)),
+                         ("paged_decode", lambda: extra_paged_decode(max(5, args.steps // 10), 3)),
+                         ("lr_build", lambda: extra_lr_build(args.steps, 10))):
+            _log(f"extra: {name}")
+            try:
+                extra[name] = fn()
+                _log(f"extra: {name}: {extra[name]['value']:.4g} {extra[name]['unit']}, "
+                     f"{extra[name]['roofline']['frac'] * 100:.1f}% of peak")
+            except lra.LraError as e:
+                extra[name] = {"error": str(e)}
+                _log(f"extra: {name}: {e}")
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("cpu baseline: oracle")
+        cpu = cpu_baseline(case)
+
+    unshared = decode_bytes_unshared(case.ctx_len[case.req_ctx], 32, 8, 128, 16)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) caches/queries, B ~ N(0,0.05^2)); no weights or datasets",
+        "config": {
+            "workload": "decode: 16 requests over 4 shared 8192-token contexts (4 agents per "
+                        "context), Hq32 Hkv8 d128 r16, bf16 storage / fp32 accumulation, one "
+                        "attention layer, 16-token pages",
+            "input_sets_rotated": args.sets,
+            "algorithmic_bytes_per_call": nbytes,
+            "bytes_if_agents_did_not_share": unshared,
+        },
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

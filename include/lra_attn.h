@@ -113,11 +113,16 @@ const char* lra_last_error(void);
  *   b_k, b_v       [n_agents, r, H_kv * d]; head h uses columns h*d .. h*d+d-1
  *   out            [n_req, H_q, d]                          device
  *   workspace      device scratch of at least
- *                  lra_attn_decode_workspace_size(...) bytes.  It must be
- *                  zero-filled before its first use; every completed call leaves
- *                  its counters at zero again, so it can be reused by later
- *                  calls on the same stream without clearing.  Calls that share
- *                  one workspace must not run concurrently.
+ *                  lra_attn_decode_workspace_size(...) bytes (0 when every
+ *                  context fits one workgroup's chunk of tokens; NULL is then
+ *                  accepted).  It holds per-chunk partial rows
+ *                  (m, l, O_base[d], O_lr[r]) and one counter per work unit;
+ *                  its size grows with the number of chunks, never with
+ *                  tokens x head_dim.  It must be zero-filled before its first
+ *                  use; every completed call leaves the counters at zero again,
+ *                  so later calls on the same stream can reuse it without
+ *                  clearing.  Calls that share one workspace must not run
+ *                  concurrently.
  */
 size_t lra_attn_decode_workspace_size(const lra_dims* dims, int32_t n_req, int32_t n_ctx,
                                       int32_t max_req_per_ctx, int32_t max_ctx_len);

@@ -79,7 +79,7 @@ def test_decode_split_count_invariance():
     d = DecodeDev(case)
     outs = []
     try:
-        for chunk in ("128", "384", "1024", "4096"):
+        for chunk in ("256", "512", "1024", "2048"):
             os.environ["LRA_DECODE_CHUNK"] = chunk
             outs.append(host(d.run()))
     finally:

@@ -130,10 +130,12 @@ class PreLRLayerCase:
 # generic builders
 
 
-def make_decode(seed, *, dtype, ctx_lens, reqs, n_agents, h_q, h_kv, d, r, page=PAGE,
-                shuffle=False, q_sigma=1.0, b_sigma=0.05, kv_sigma=1.0, l_sigma=1.0,
-                max_blocks=None, name="", layer=0):
-    """Paged decode inputs.  ``reqs`` is a list of ``(ctx, agent)`` sorted by ctx."""
+def page_table(seed, ctx_lens, *, shuffle, page=PAGE, max_blocks=None, layer=0):
+    """Block table ``[n_ctx, max_blocks]`` over a pool of exactly sum(ceil(len/page)) pages.
+
+    Contexts take consecutive pool pages in order, or (``shuffle``) the pages of a
+    random permutation of the pool.  Unused table entries are 0.
+    """
     ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
     n_ctx = len(ctx_lens)
     nblk = (ctx_lens + page - 1) // page
@@ -147,6 +149,16 @@ def make_decode(seed, *, dtype, ctx_lens, reqs, n_agents, h_q, h_kv, d, r, page=
     for c in range(n_ctx):
         table[c, :nblk[c]] = order[off:off + nblk[c]]
         off += int(nblk[c])
+    return table, n_pages
+
+
+def make_decode(seed, *, dtype, ctx_lens, reqs, n_agents, h_q, h_kv, d, r, page=PAGE,
+                shuffle=False, q_sigma=1.0, b_sigma=0.05, kv_sigma=1.0, l_sigma=1.0,
+                max_blocks=None, name="", layer=0):
+    """Paged decode inputs.  ``reqs`` is a list of ``(ctx, agent)`` sorted by ctx."""
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
+    table, n_pages = page_table(seed, ctx_lens, shuffle=shuffle, page=page,
+                                max_blocks=max_blocks, layer=layer)
     req_ctx = np.array([c for c, _ in reqs], dtype=np.int32)
     req_agent = np.array([a for _, a in reqs], dtype=np.int32)
     assert np.all(np.diff(req_ctx) >= 0), "requests must be grouped by context"
