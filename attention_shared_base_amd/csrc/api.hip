@@ -91,10 +91,13 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     // streaming several 32-token steps.
     int chunk = env_int("LRA_DECODE_CHUNK", 0);
     if (chunk != 256 && chunk != 512 && chunk != 1024 && chunk != 2048) {
-        const int target = env_int("LRA_DECODE_TARGET_WG", 512);
-        const long long c = ((long long)max_ctx_len * units + target - 1) / (target > 0 ? target : 512);
+        // ~one workgroup per CU at the longest context; longer chunks amortise
+        // each workgroup's fixed prologue/merge cost (measured best on MI355X:
+        // 1024 tokens for 4 x 8192-token contexts, 2048 for 4k-64k contexts).
+        const int target = env_int("LRA_DECODE_TARGET_WG", 256);
+        const long long c = ((long long)max_ctx_len * units + target - 1) / (target > 0 ? target : 256);
         chunk = 256;
-        while (chunk < 1024 && chunk < c) chunk *= 2;
+        while (chunk < 2048 && chunk < c) chunk *= 2;
     }
     p->chunk = chunk;
     p->n_split = max_ctx_len > 0 ? (max_ctx_len + chunk - 1) / chunk : 1;

@@ -12,7 +12,8 @@ from HIP events on the launch stream.
 Extra legs in the same run (``extra``): chunked prefill with RoPE on the adapter
 key term (512 new tokens over 16384, 4 agents; TFLOP/s vs bf16 MFMA peak),
 paged decode over 32 shuffled contexts of 4k-64k tokens (GB/s vs HBM peak),
-and the LR-cache build of one 4096-token layer (GB/s).
+the LR-cache build of one 4096-token layer (GB/s), and one whole PreLRShared
+step (32 layers x (LR build + 8 agents' prefill of 4096 over 131072), TFLOP/s).
 
 cpu_baseline: the float64 oracle on the host cores, on the primary workload's
 first input set (all 16 requests, repeated until >= 10 s), as requests/s.
@@ -120,6 +121,31 @@ def _time_calls(fn, n_sets, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16__decode_4ctx_x_8192_r16__hbm_traffic.txt")
+TRAFFIC_SOURCES = ("attention_shared_base_amd/csrc/decode_bf16.hip", "attention_shared_base_amd/csrc/api.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the primary decode kernel from the committed counter
+    summary, or None if the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for src in TRAFFIC_SOURCES:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest()[:16] != kv.get("source_sha256"):
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _log(msg):
@@ -270,6 +296,65 @@ def extra_lr_build(steps, warmup, n_sets=8):
             "algorithmic_bytes": nbytes}
 
 
+def extra_prelr_step(steps, warmup, n_layers=32):
+    """PreLRShared step: per layer, LR build of 4096 new rows, then 8 agents' prefill.
+
+    32 layers of LLaMA-3.1-8B attention shape, each with its own buffers: X
+    [4096, 4096], A_k/A_v [16, 4096], K_base/V_base [8, 135168, 128] (131072
+    old + 4096 new tokens), L_k/L_v [135168, 16] (old rows given, new rows built
+    in the step), per-agent Q [4096, 32, 128] and B [16, 1024].  Inputs are
+    drawn on the GPU (torch Philox) with the same distributions as the seeded
+    host generator; parity of this workload is covered by the tests.
+    """
+    import torch
+    import attention_shared_base_amd as lra
+    n_new, n_old, d_model, h_q, h_kv, d, r, n_ag = 4096, 131072, 4096, 32, 8, 128, 16, 8
+    kv_len = n_old + n_new
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    layers = []
+    for _ in range(n_layers):
+        lk = _randn_bf16((kv_len, r), 1.0, gen)
+        lv = _randn_bf16((kv_len, r), 1.0, gen)
+        layers.append(dict(
+            x=_randn_bf16((n_new, d_model), 1.0, gen),
+            ak=_randn_bf16((r, d_model), 1.0 / 64, gen), av=_randn_bf16((r, d_model), 1.0 / 64, gen),
+            k=_randn_bf16((h_kv, kv_len, d), 1.0, gen), v=_randn_bf16((h_kv, kv_len, d), 1.0, gen),
+            lk=lk, lv=lv, q=_randn_bf16((n_ag, n_new, h_q, d), 1.0, gen),
+            bk=_randn_bf16((n_ag, r, h_kv * d), 0.05, gen),
+            bv=_randn_bf16((n_ag, r, h_kv * d), 0.05, gen)))
+    agent = torch.arange(n_ag, dtype=torch.int32, device="cuda")
+    out = torch.empty((n_ag, n_new, h_q, d), dtype=torch.bfloat16, device="cuda")
+
+    def call(_):
+        for L in layers:
+            lra.lr_cache_build(L["x"], L["ak"], L["av"], L["lk"], L["lv"], row_offset=n_old)
+            lra.prefill(L["q"], agent, L["k"], L["v"], L["lk"], L["lv"], L["bk"], L["bv"], out=out)
+
+    ms = _time_calls(call, 1, steps, warmup)
+    fl = n_layers * (prefill_flops(n_ag, n_new, kv_len, h_q, h_kv, d, r, rope=False)
+                     + 2 * n_new * d_model * 2 * r)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": "PreLRShared step: 32 layers x (LR build X[4096,4096]·[A_k|A_v] r16, then "
+                        "8 agents' prefill of 4096 new tokens over 131072 shared), Hq32 Hkv8 d128, bf16",
+            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None},
+            "algorithmic_flops": fl}
+
+
+def copy_calibration(nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+
+
 def cpu_baseline(case, min_seconds=10.0):
     """The float64 oracle, as it stands, on the primary workload's first input set."""
     import oracle
@@ -305,8 +390,12 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
-    ap.add_argument("--no-extra", action="store_true", help="skip the prefill/paged/LR-build legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
+    ap.add_argument("--extra", default="prefill_rope,paged_decode,lr_build,prelr_step",
+                    help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -319,6 +408,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     lra.load()
 
     _log("primary: decode, 4 shared contexts x 8192 tokens, 16 requests")
@@ -329,9 +421,12 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name, fn in (("prefill_rope", lambda: extra_prefill_rope(max(5, args.steps // 10), 3)),
-                         ("paged_decode", lambda: extra_paged_decode(max(5, args.steps // 10), 3)),
-                         ("lr_build", lambda: extra_lr_build(args.steps, 10))):
+        legs = {"prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
+                "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
+                "lr_build": lambda: extra_lr_build(args.steps, 10),
+                "prelr_step": lambda: extra_prelr_step(1, 1)}
+        for name in [x for x in args.extra.split(",") if x]:
+            fn = legs[name]
             _log(f"extra: {name}")
             try:
                 extra[name] = fn()
@@ -370,7 +465,7 @@ def main():
             "bytes_if_agents_did_not_share": unshared,
         },
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "extra": extra,
     }
