@@ -72,8 +72,15 @@ LRA_DEV bf16x4 lds_read_tr(const bf16* p) {
 
 template <int D, int R, bool ROPE>
 __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
-    constexpr int KP = D + 16;                   // LDS row pitch (elements) of K and V tiles
-    constexpr int RP = R < 16 ? 16 : R;          // LDS row pitch of the L tiles
+    // LDS row pitches (elements), measured conflict-free on gfx950: 16-byte row
+    // reads need a pitch of 16 (mod 256) bytes, the transposing reads (two
+    // 16-lane groups side by side, 4 rows each) 64 (mod 256) bytes, and the
+    // 8-byte rank reads of 32 rows an odd number of 8-byte words.
+    constexpr int KP = D + 8;                    // K tile: 272 B for d = 128
+    constexpr int VP = D + 32;                   // V tile: 320 B for d = 128
+    constexpr int RW = R < 16 ? 16 : R;          // rank columns held per L row (zero padded)
+    constexpr int RP = RW + 4;                   // L_k tile: 40 B (r <= 16) / 72 B (r = 32)
+    constexpr int RV = RW;                       // L_v tile: transposing reads, contiguous rows
     constexpr int NKS = D / 16;                  // k-steps over head dim
     constexpr int NDT = D / 32;                  // 32-wide dim tiles
     constexpr int NKR = (R + 15) / 16;           // k-steps over rank
@@ -81,14 +88,14 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int ONES_T = R / 32;               // tile holding the ones row
     constexpr int ONES_M = R % 32;               // its row inside the tile
     constexpr int CH_K = KT * D / 8;             // 16-byte chunks per K (or V) tile
-    constexpr int CH_L = KT * RP / 8;            // 16-byte chunks per L tile
+    constexpr int CH_L = KT * RW / 8;            // 16-byte chunks per L tile
     constexpr int CH = 2 * CH_K + 2 * CH_L;
     constexpr int LPT = (CH + 511) / 512;        // chunks per thread
 
     __shared__ __attribute__((aligned(16))) bf16 sK[2][KT][KP];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][KT][KP];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2][KT][VP];
     __shared__ __attribute__((aligned(16))) bf16 sLk[2][KT][RP];
-    __shared__ __attribute__((aligned(16))) bf16 sLv[2][KT][RP];
+    __shared__ __attribute__((aligned(16))) bf16 sLv[2][KT][RV];
     __shared__ __attribute__((aligned(16))) bf16 sBk[ROPE ? R : 1][ROPE ? D : 1];
 
     const int tid = threadIdx.x;
@@ -139,8 +146,8 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
                     if (key < kv_len) v = ldg_stream((const bf16x8*)((c < CH_K ? kb : vb) + (size_t)key * D + col));
                 } else {
                     const int cc = (c - 2 * CH_K) % CH_L;
-                    const int key = key0 + cc / (RP / 8);
-                    const int col = (cc % (RP / 8)) * 8;
+                    const int key = key0 + cc / (RW / 8);
+                    const int col = (cc % (RW / 8)) * 8;
                     if (key < kv_len && col < R)
                         v = ldg((const bf16x8*)((c < 2 * CH_K + CH_L ? a.l_k : a.l_v) + (size_t)key * R + col));
                 }
@@ -153,14 +160,21 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         for (int u = 0; u < LPT; ++u) {
             const int c = tid + 512 * u;
             if (c < CH) {
-                if (c < 2 * CH_K) {
-                    const int cc = c % CH_K;
-                    bf16* dst = (c < CH_K ? &sK[buf][0][0] : &sV[buf][0][0]) + (cc / (D / 8)) * KP + (cc % (D / 8)) * 8;
-                    *(bf16x8*)dst = stage[u];
+                if (c < CH_K) {
+                    const int cc = c;
+                    *(bf16x8*)(&sK[buf][0][0] + (cc / (D / 8)) * KP + (cc % (D / 8)) * 8) = stage[u];
+                } else if (c < 2 * CH_K) {
+                    const int cc = c - CH_K;
+                    *(bf16x8*)(&sV[buf][0][0] + (cc / (D / 8)) * VP + (cc % (D / 8)) * 8) = stage[u];
+                } else if (c < 2 * CH_K + CH_L) {
+                    // 8-byte aligned rows: two 8-byte stores
+                    const int cc = c - 2 * CH_K;
+                    bf16* dst = &sLk[buf][0][0] + (cc / (RW / 8)) * RP + (cc % (RW / 8)) * 8;
+                    *(bf16x4*)dst = __builtin_shufflevector(stage[u], stage[u], 0, 1, 2, 3);
+                    *(bf16x4*)(dst + 4) = __builtin_shufflevector(stage[u], stage[u], 4, 5, 6, 7);
                 } else {
-                    const int cc = (c - 2 * CH_K) % CH_L;
-                    bf16* dst = (c < 2 * CH_K + CH_L ? &sLk[buf][0][0] : &sLv[buf][0][0]) + (cc / (RP / 8)) * RP + (cc % (RP / 8)) * 8;
-                    *(bf16x8*)dst = stage[u];
+                    const int cc = c - 2 * CH_K - CH_L;
+                    *(bf16x8*)(&sLv[buf][0][0] + (cc / (RW / 8)) * RV + (cc % (RW / 8)) * 8) = stage[u];
                 }
             }
         }
@@ -289,33 +303,44 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
                 }
             }
         }
-        // ---- online softmax (row = lane % 32; the two k-groups hold disjoint keys)
+        // ---- online softmax (row = lane % 32; the two k-groups hold disjoint keys).
+        // Tiles entirely below the causal diagonal of the workgroup's first token
+        // skip the mask.  The running max is updated lazily: only when some row's
+        // tile max exceeds it by more than 8 (log2 units) are the accumulators
+        // rescaled, so p = exp2(s*scale - m) <= 2^8 — exact after the final
+        // division, and bf16 / fp32 hold that range.  Rows past q_len (Q = 0) never
+        // reach the output.
+        const bool full = key0 + KT - 1 <= kv_len - q_len + tok_wg;
+        if (!full) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = key0 + 32 * mt + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    s[mt][v] = key <= qpos ? s[mt][v] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = key0 + 32 * mt + 8 * (v >> 2) + 4 * hh + (v & 3);
-                s[mt][v] = key <= qpos ? s[mt][v] * sl2 : -INFINITY;
-                mx = fmaxf(mx, s[mt][v]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const bool none = m_new == -INFINITY;
-        const float alpha = none ? 1.0f : fast_exp2(m_run - m_new);
-        m_run = m_new;
+            for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[mt][v], s[mt][v + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc_o[dt] *= alpha;
+#pragma unroll
+            for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] *= alpha;
+            m_run = m_new;
+        }
         bf16x8 pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xv = s[ks >> 1][8 * (ks & 1) + e];
-                pb[ks][e] = (bf16)(xv == -INFINITY ? 0.f : fast_exp2(xv - m_new));
-            }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc_o[dt] *= alpha;
-#pragma unroll
-        for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] *= alpha;
+            for (int e = 0; e < 8; ++e)
+                pb[ks][e] = (bf16)fast_exp2(__builtin_fmaf(s[ks >> 1][8 * (ks & 1) + e], sl2, -m_run));
 
         // ---- O^T += V^T P^T and O_lr^T += L_v^T P^T (16 keys per k-step)
 #pragma unroll
@@ -325,7 +350,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const bf16* vp = &sV[buf][srow][32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3)];
-                const bf16x8 va = cat4(lds_read_tr(vp), lds_read_tr(vp + 8 * KP));
+                const bf16x8 va = cat4(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
                 acc_o[dt] = mfma32x32x16(va, pb[ks], acc_o[dt]);
             }
 #pragma unroll
@@ -337,7 +362,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
                 // overwrote the inactive lanes' destination registers.
                 const int col = 32 * lt + 16 * (g16 & 1);
                 const bf16* lp = &sLv[buf][srow][(col < R ? col : 0) + 4 * (i16 & 3)];
-                bf16x8 la = cat4(lds_read_tr(lp), lds_read_tr(lp + 8 * RP));
+                bf16x8 la = cat4(lds_read_tr(lp), lds_read_tr(lp + 8 * RV));
                 const int m = 32 * lt + n32;
                 if (m >= R) la = m == R ? ones8() : zero8();
                 acc_lr[lt] = mfma32x32x16(la, pb[ks], acc_lr[lt]);
