@@ -16,8 +16,8 @@
 //
 // Decomposition: a workgroup = (request, KV head h, block of 8*TW new tokens);
 // its 8 wavefronts each own 32 rows = TW tokens x g query heads of h (GQA
-// packing: one K/V tile serves all g heads).  64-token K/V/L tiles stream
-// through double-buffered LDS.  All products run on v_mfma_f32_32x32x16_bf16:
+// packing: one K/V tile serves all g heads).  All products run on
+// v_mfma_f32_32x32x16_bf16:
 //
 //   S^T[key][row]  = K[key][dim] . Q^T[dim][row]  (+ L_k . qB^T, rank r)
 //   O^T[dim][row] += V^T[dim][key] . P^T[key][row]
@@ -28,6 +28,22 @@
 // already the P^T operand layout, so P stays in registers.  V^T and L_v^T
 // operands come from the row-major LDS tiles through the gfx950 transposing
 // read ds_read_b64_tr_b16 (16 lanes turn a 4 x 16 block into 16 columns of 4).
+//
+// Data movement.  64-key tiles go HBM -> LDS by buffer_load ... lds (no
+// register staging): one instruction moves 1 KB, lane i's 16 bytes landing at
+// 16*i, and keys past kv_len read as zero through the buffer range.  Each 1 KB
+// block of a K / V / cos / sin tile holds the rows key = i + NI*m of block i,
+// and consecutive blocks sit 1040 B (K, cos, sin) or 1088 B (V) apart: that
+// spreads the 16 rows a 16-lane row read touches over all 64 banks, and the
+// 4 rows of a transposing read over the four 64-byte bank quarters, with LDS
+// addresses that stay linear in the key (one base register per operand).
+// L tiles are chunk-major ([16-byte rank chunk][key]); the L_v tile carries
+// constant chunks after the ranks (the ones row, zeros) written once.
+//
+// Pipeline per tile t: K is loaded two tiles ahead and V one tile ahead, so
+// S(t+1) is on the matrix cores while the softmax of S(t) runs on the VALU,
+// followed by P(t)V(t) with the row max of S(t+1) in its shadow; one barrier
+// per tile (two with RoPE: raw K(t+2) lands, K'(t+2) is rebuilt in place).
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -54,49 +70,97 @@ struct PrefillK {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-LRA_DEV bf16x8 ones8() {
-    bf16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (bf16)1.0f;
-    return o;
-}
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Transposing LDS read: the 16 lanes of a group each name one 8-byte row piece
 // (lane a + 4*s -> row k0+s, columns n0+4a .. n0+4a+3); lane i of the group
 // receives column n0+i of rows k0 .. k0+3.
-LRA_DEV bf16x4 lds_read_tr(const bf16* p) {
+LRA_DEV bf16x4 lds_read_tr(const char* p) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): stride 0, reads past the end
+// return 0.
+LRA_DEV u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    u32x4 r;
+    r[0] = (uint32_t)p;
+    r[1] = (uint32_t)(p >> 32) & 0xffffu;
+    r[2] = bytes;
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One 1 KB HBM -> LDS block (buffer_load_dwordx4 ... lds): lane i reads 16
+// bytes at byte offset voff of the resource and they land at LDS address
+// lds + 16*i.  Issued from asm so that the compiler does not serialise the
+// transfer against unrelated LDS reads; completion is awaited explicitly
+// (wait_dma) before the barrier that publishes the tile.  M0 is restored.
+LRA_DEV void dma_1k(u32x4 r, uint32_t lds, uint32_t voff) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(0): this wavefront's LDS DMA has landed.
+LRA_DEV void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// v_max3_f32 (operands are finite or -inf; no NaN canonicalisation needed)
+LRA_DEV float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 template <int D, int R, bool ROPE>
 __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
-    // LDS row pitches (elements), measured conflict-free on gfx950: 16-byte row
-    // reads need a pitch of 16 (mod 256) bytes, the transposing reads (two
-    // 16-lane groups side by side, 4 rows each) 64 (mod 256) bytes, and the
-    // 8-byte rank reads of 32 rows an odd number of 8-byte words.
-    constexpr int KP = D + 8;                    // K tile: 272 B for d = 128
-    constexpr int VP = D + 32;                   // V tile: 320 B for d = 128
-    constexpr int RW = R < 16 ? 16 : R;          // rank columns held per L row (zero padded)
-    constexpr int RP = RW + 4;                   // L_k tile: 40 B (r <= 16) / 72 B (r = 32)
-    constexpr int RV = RW;                       // L_v tile: transposing reads, contiguous rows
-    constexpr int NKS = D / 16;                  // k-steps over head dim
-    constexpr int NDT = D / 32;                  // 32-wide dim tiles
-    constexpr int NKR = (R + 15) / 16;           // k-steps over rank
-    constexpr int NLT = (R + 1 + 31) / 32;       // rank tiles of O_lr incl. the ones row
-    constexpr int ONES_T = R / 32;               // tile holding the ones row
-    constexpr int ONES_M = R % 32;               // its row inside the tile
-    constexpr int CH_K = KT * D / 8;             // 16-byte chunks per K (or V) tile
-    constexpr int CH_L = KT * RW / 8;            // 16-byte chunks per L tile
-    constexpr int CH = 2 * CH_K + 2 * CH_L;
-    constexpr int LPT = (CH + 511) / 512;        // chunks per thread
+    constexpr int RB = 2 * D;                 // bytes per K / V row (and per cos / sin row)
+    constexpr int CPR = D / 8;                // 16-byte chunks per row
+    constexpr int NI = KT * RB / 1024;        // 1 KB blocks per tile
+    constexpr int NU = NI / WAVES;            // blocks per wavefront per tile
+    constexpr int KBS = 1024 + 16;            // block stride: K, cos, sin
+    constexpr int VBS = 1024 + 64;            // block stride: V, L_v chunks
+    constexpr int TK = NI * KBS;
+    constexpr int TV = NI * VBS;
+    constexpr int RW = R < 16 ? 16 : R;       // ranks held per L row (zero padded)
+    constexpr int NKS = D / 16;               // k-steps over head dim
+    constexpr int NDT = D / 32;               // 32-wide dim tiles
+    constexpr int NKR = RW / 16;              // k-steps over rank
+    constexpr int NLT = (R + 1 + 31) / 32;    // rank tiles of O_lr incl. the ones row
+    constexpr int ONES_T = R / 32;            // tile holding the ones row
+    constexpr int ONES_M = R % 32;            // its row inside the tile
+    constexpr int RCH = R / 8;                // 16-byte rank chunks per L row in HBM
+    constexpr int NLK = RW / 8;               // L_k chunks held
+    constexpr int NLV = 4 * NLT;              // L_v chunks held (ranks, ones row, zeros)
+    constexpr int TLK = NLK * 1024;
+    constexpr int TLV = NLV * VBS;
+    constexpr int OFF_K = 0;
+    constexpr int OFF_V = OFF_K + 2 * TK;
+    constexpr int OFF_LK = OFF_V + 2 * TV;
+    constexpr int OFF_LV = OFF_LK + 2 * TLK;
+    constexpr int OFF_CS = OFF_LV + 2 * TLV;  // RoPE: cos / sin tiles, two buffers
+    constexpr int LDS_BYTES = OFF_CS + (ROPE ? 4 * TK : 0);
+    constexpr int KMT = (32 / NI) * RB;       // K tile offset of keys 32..63
+    constexpr int VKS = (D == 128) ? RB : 2 * RB;   // V offset of the next 16 keys
+    constexpr int V8 = (D == 128) ? 8 * VBS : RB;   // V offset of rows +8
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static_assert(R % 8 == 0 && R <= 32, "rank 8, 16, 24 or 32");
+    static_assert(NU >= 1 && NI % WAVES == 0, "tile blocks divide over the wavefronts");
+    static_assert(RCH <= 4, "L_v DMA uses wavefronts 4..7");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) bf16 sK[2][KT][KP];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][KT][VP];
-    __shared__ __attribute__((aligned(16))) bf16 sLk[2][KT][RP];
-    __shared__ __attribute__((aligned(16))) bf16 sLv[2][KT][RV];
-    __shared__ __attribute__((aligned(16))) bf16 sBk[ROPE ? R : 1][ROPE ? D : 1];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -105,6 +169,8 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     const int hh = lane >> 5;   // k-group of this lane
     const int i16 = lane & 15;  // lane inside its 16-lane group (transposing reads)
     const int g16 = lane >> 4;  // 16-lane group
+    const int sa = i16 & 3;     // transposing read: 8-byte piece
+    const int ss = i16 >> 2;    // transposing read: row
 
     const int g = a.g;
     const int TW = 32 / g;  // tokens per wavefront
@@ -130,57 +196,64 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     const bf16* kb = a.k_base + (size_t)h * hstride;
     const bf16* vb = a.v_base + (size_t)h * hstride;
 
-    // ---- global -> register -> LDS tile copies (16-byte chunks)
-    bf16x8 stage[LPT];
-    auto gload = [&](int tile) {
-        const int key0 = tile * KT;
+    // ---- HBM -> LDS tile DMA.  Block i of a K / V / cos / sin tile: lane l carries
+    // row key = i + NI*(l / CPR), chunk l % CPR.  L chunk c: lane l carries key l.
+    uint32_t voff_row[NU];
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int c = tid + 512 * u;
-            bf16x8 v = zero8();
-            if (c < CH) {
-                if (c < 2 * CH_K) {
-                    const int cc = c % CH_K;
-                    const int key = key0 + cc / (D / 8);
-                    const int col = (cc % (D / 8)) * 8;
-                    if (key < kv_len) v = ldg_stream((const bf16x8*)((c < CH_K ? kb : vb) + (size_t)key * D + col));
-                } else {
-                    const int cc = (c - 2 * CH_K) % CH_L;
-                    const int key = key0 + cc / (RW / 8);
-                    const int col = (cc % (RW / 8)) * 8;
-                    if (key < kv_len && col < R)
-                        v = ldg((const bf16x8*)((c < 2 * CH_K + CH_L ? a.l_k : a.l_v) + (size_t)key * R + col));
-                }
+    for (int u = 0; u < NU; ++u)
+        voff_row[u] = (uint32_t)((wave + WAVES * u) + NI * (lane / CPR)) * RB + (lane % CPR) * 16;
+    const uint32_t voff_l = (uint32_t)lane * (2 * R);
+
+    auto dma_k = [&](int T, int b) {
+        const int key0 = T * KT;
+        const uint32_t rem = (uint32_t)(kv_len - key0);
+        const auto rk = make_rsrc(kb + (size_t)key0 * D, rem * RB);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) dma_1k(rk, smem_lds + OFF_K + b * TK + (wave + WAVES * u) * KBS, voff_row[u]);
+        if (wave < RCH)
+            dma_1k(make_rsrc(a.l_k + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LK + b * TLK + wave * 1024,
+                   voff_l + 16 * wave);
+        if constexpr (ROPE) {
+            const auto rc = make_rsrc(a.rope_cos + (size_t)key0 * (D / 2), rem * RB);
+            const auto rs = make_rsrc(a.rope_sin + (size_t)key0 * (D / 2), rem * RB);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                dma_1k(rc, smem_lds + OFF_CS + (2 * b) * TK + (wave + WAVES * u) * KBS, voff_row[u]);
+                dma_1k(rs, smem_lds + OFF_CS + (2 * b + 1) * TK + (wave + WAVES * u) * KBS, voff_row[u]);
             }
-            stage[u] = v;
         }
     };
-    auto lstore = [&](int buf) {
+    auto dma_v = [&](int T, int b) {
+        const int key0 = T * KT;
+        const uint32_t rem = (uint32_t)(kv_len - key0);
+        const auto rv = make_rsrc(vb + (size_t)key0 * D, rem * RB);
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int c = tid + 512 * u;
-            if (c < CH) {
-                if (c < CH_K) {
-                    const int cc = c;
-                    *(bf16x8*)(&sK[buf][0][0] + (cc / (D / 8)) * KP + (cc % (D / 8)) * 8) = stage[u];
-                } else if (c < 2 * CH_K) {
-                    const int cc = c - CH_K;
-                    *(bf16x8*)(&sV[buf][0][0] + (cc / (D / 8)) * VP + (cc % (D / 8)) * 8) = stage[u];
-                } else if (c < 2 * CH_K + CH_L) {
-                    // 8-byte aligned rows: two 8-byte stores
-                    const int cc = c - 2 * CH_K;
-                    bf16* dst = &sLk[buf][0][0] + (cc / (RW / 8)) * RP + (cc % (RW / 8)) * 8;
-                    *(bf16x4*)dst = __builtin_shufflevector(stage[u], stage[u], 0, 1, 2, 3);
-                    *(bf16x4*)(dst + 4) = __builtin_shufflevector(stage[u], stage[u], 4, 5, 6, 7);
-                } else {
-                    const int cc = c - 2 * CH_K - CH_L;
-                    *(bf16x8*)(&sLv[buf][0][0] + (cc / (RW / 8)) * RV + (cc % (RW / 8)) * 8) = stage[u];
-                }
-            }
-        }
+        for (int u = 0; u < NU; ++u) dma_1k(rv, smem_lds + OFF_V + b * TV + (wave + WAVES * u) * VBS, voff_row[u]);
+        const int c = wave - 4;
+        if (c >= 0 && c < RCH)
+            dma_1k(make_rsrc(a.l_v + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LV + b * TLV + c * VBS,
+                   voff_l + 16 * c);
     };
 
-    gload(0);
+    // constant chunks: L_v rank R = ones, further ranks zero; L_k padding zero
+    for (int e = tid; e < 2 * (NLV - RCH) * KT; e += 512) {
+        const int b = e / ((NLV - RCH) * KT);
+        const int c = RCH + (e / KT) % (NLV - RCH);
+        bf16x8 v = zero8();
+        if (c == RCH) v[0] = (bf16)1.0f;
+        *(bf16x8*)(smem + OFF_LV + b * TLV + c * VBS + (e % KT) * 16) = v;
+    }
+    if constexpr (NLK > RCH) {
+        for (int e = tid; e < 2 * (NLK - RCH) * KT; e += 512) {
+            const int b = e / ((NLK - RCH) * KT);
+            const int c = RCH + (e / KT) % (NLK - RCH);
+            *(bf16x8*)(smem + OFF_LK + b * TLK + c * 1024 + (e % KT) * 16) = zero8();
+        }
+    }
+
+    dma_k(0, 0);
+    dma_v(0, 0);
+    if (n_tiles > 1) dma_k(1, 1);
 
     // ---- query operand (B of S^T): lane holds dims 16*ks + 8*hh .. +7 of its row
     bf16x8 qf[NKS];
@@ -192,31 +265,135 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     const size_t bcols = (size_t)a.h_kv * D;
     const bf16* bk_ag = a.b_k + (size_t)agent * R * bcols + (size_t)h * D;
     const bf16* bv_ag = a.b_v + (size_t)agent * R * bcols + (size_t)h * D;
-    // rank carried by k-slot e of rank step kr for a lane in k-group hh
+
+    // Rank k-slots.  In the loop a lane of k-group hh carries ranks
+    // 16*kr + 8*hh .. +7 (one 16-byte L chunk).  The epilogue follows the O_lr
+    // accumulator layout instead: slot e of k-group hh is rank_of(kr, e).
     auto rank_of = [&](int kr, int e) { return 16 * kr + 8 * (e >> 2) + 4 * hh + (e & 3); };
 
-    // ---- qB^T = B_k^(h) Q^T (no RoPE): ranks on M, rows on N
+    // ---- qB^T = B_k^(h) Q^T (no RoPE).  A row rho takes rank 16kr + rho with
+    // bits 2 and 3 swapped, so that C lane (row, hh) slot e holds rank 16kr + 8hh + e.
     bf16x8 qbf[NKR];
     if constexpr (!ROPE) {
 #pragma unroll
         for (int kr = 0; kr < NKR; ++kr) {
             f32x16 c = {};
-            const int rank = 16 * kr + n32;  // A row: rank
+            const int rank = 16 * kr + ((n32 & 3) | ((n32 & 4) << 1) | ((n32 & 8) >> 1));
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 bf16x8 av = zero8();
                 if (n32 < 16 && rank < R) av = ldg((const bf16x8*)(bk_ag + (size_t)rank * bcols + 16 * ks + 8 * hh));
                 c = mfma32x32x16(av, qf[ks], c);
             }
-            // C lane holds ranks 16kr + 8(v/4) + 4hh + v%4 (v < 8 carry ranks < 16kr + 16)
 #pragma unroll
             for (int e = 0; e < 8; ++e) qbf[kr][e] = (bf16)c[e];
         }
     }
-    // ---- B_k^(h) of the RoPE key rebuild, staged once in LDS as [rank][dim]
+
+    // ---- RoPE key rebuild K' = K_base + rot_key(L_k B_k^(h)) of one buffer, in place.
+    // Wavefront -> key half kt, dim tile dt (paired with dt + D/64), and a part of
+    // the 8-dim groups b4.  x1/x2 = B_k^T L_k^T for dims 32dt.. and 32dt + D/2..
+    constexpr int HALF_T = D / 64;
+    const int rb_kt = wave & 1;
+    const int rb_dt = (wave >> 1) % HALF_T;
+    const int rb_part = (wave >> 1) / HALF_T;
+    bf16x8 bk1[NKR], bk2[NKR];
     if constexpr (ROPE) {
-        for (int e = tid; e < R * D; e += 512) sBk[e / D][e % D] = bk_ag[(size_t)(e / D) * bcols + e % D];
+#pragma unroll
+        for (int kr = 0; kr < NKR; ++kr)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int rk = 16 * kr + 8 * hh + e;
+                const bool ok = rk < R;
+                const bf16* bp = bk_ag + (size_t)(ok ? rk : 0) * bcols + 32 * rb_dt + n32;
+                bk1[kr][e] = ok ? bp[0] : (bf16)0.0f;
+                bk2[kr][e] = ok ? bp[D / 2] : (bf16)0.0f;
+            }
     }
+    auto rebuild = [&](int T, int b) {
+        const int key_l = 32 * rb_kt + n32;
+        f32x16 x1 = {}, x2 = {};
+#pragma unroll
+        for (int kr = 0; kr < NKR; ++kr) {
+            const bf16x8 lb = *(const bf16x8*)(smem + OFF_LK + b * TLK + (2 * kr + hh) * 1024 + key_l * 16);
+            x1 = mfma32x32x16(bk1[kr], lb, x1);
+            x2 = mfma32x32x16(bk2[kr], lb, x2);
+        }
+        char* krow = smem + OFF_K + b * TK + (key_l % NI) * KBS + (key_l / NI) * RB;
+        const char* crow = smem + OFF_CS + (2 * b) * TK + (key_l % NI) * KBS + (key_l / NI) * RB;
+        const char* srow = crow + TK;
+#pragma unroll
+        for (int j = 0; j < HALF_T; ++j) {
+            const int b4 = rb_part * HALF_T + j;
+            const int i0 = 32 * rb_dt + 8 * b4 + 4 * hh;
+            const f32x4 cs = *(const f32x4*)(crow + 4 * i0);
+            const f32x4 sn = *(const f32x4*)(srow + 4 * i0);
+            bf16x4* r1 = (bf16x4*)(krow + 2 * i0);
+            bf16x4* r2 = (bf16x4*)(krow + 2 * (i0 + D / 2));
+            bf16x4 k1 = *r1, k2 = *r2;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float u1 = x1[4 * b4 + c], u2 = x2[4 * b4 + c];
+                k1[c] = (bf16)((float)k1[c] + (u1 * cs[c] - u2 * sn[c]));
+                k2[c] = (bf16)((float)k2[c] + (u2 * cs[c] + u1 * sn[c]));
+            }
+            *r1 = k1;
+            *r2 = k2;
+        }
+        (void)T;
+    };
+
+    // ---- per-lane LDS operand bases (all further offsets are immediates)
+    const int lds_k = (n32 % NI) * KBS + (n32 / NI) * RB + 16 * hh;            // K row read
+    const int lds_lk = hh * 1024 + n32 * 16;                                   // L_k chunk read
+    const int lds_v = (4 * hh + ss) * VBS + 32 * (g16 & 1) + 8 * sa;           // V transposing read
+    const int lds_lv = (2 * (g16 & 1) + (sa >> 1)) * VBS + (4 * hh + ss) * 16 + 8 * (sa & 1);
+
+    auto s_tile = [&](int b, f32x16 (&s)[2]) {
+        const char* kp = smem + OFF_K + b * TK + lds_k;
+        const char* lp = smem + OFF_LK + b * TLK + lds_lk;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                s[mt] = mfma32x32x16(*(const bf16x8*)(kp + mt * KMT + ks * 32), qf[ks], s[mt]);
+        if constexpr (!ROPE) {
+#pragma unroll
+            for (int kr = 0; kr < NKR; ++kr)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    s[mt] = mfma32x32x16(*(const bf16x8*)(lp + kr * 2048 + mt * 512), qbf[kr], s[mt]);
+        }
+    };
+    // keys above the row's causal bound -> -inf
+    auto mask_tile = [&](int T, f32x16 (&s)[2]) {
+        const int lim = qpos - T * KT - 4 * hh;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                s[mt][v] = 32 * mt + 8 * (v >> 2) + (v & 3) > lim ? -INFINITY : s[mt][v];
+    };
+    // every key of the tile visible to the workgroup's first token
+    auto full_tile = [&](int T) { return T * KT + KT - 1 <= kv_len - q_len + tok_wg; };
+    const float sl2 = a.scale_log2;
+    // row max of a score tile, in log2 units
+    auto tile_max = [&](const f32x16 (&s)[2]) {
+        float m0 = max3(s[0][0], s[0][1], s[0][2]);
+        float m1 = max3(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) {
+            m0 = max3(m0, s[0][v], s[0][v + 1]);
+            m1 = max3(m1, s[1][v], s[1][v + 1]);
+        }
+        float m = max3(m0, m1, s[0][15]);
+        m = max3(m, s[1][15], s[1][15]);
+        // v_permlane32_swap of (m, m): lane l sees m of lanes l and l ^ 32
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        return max3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1])) * sl2;
+    };
 
     f32x16 acc_o[NDT];
     f32x16 acc_lr[NLT];
@@ -224,110 +401,84 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x16{};
 #pragma unroll
     for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] = f32x16{};
-    float m_run = -INFINITY;
-    const float sl2 = a.scale_log2;
 
-    lstore(0);
+    auto pv_tile = [&](int b, const bf16x8 (&pb)[4]) {
+        const char* vp = smem + OFF_V + b * TV + lds_v;
+        const char* lp = smem + OFF_LV + b * TLV + lds_lv;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const char* p = vp + ks * VKS + dt * 64;
+                acc_o[dt] = mfma32x32x16(cat4(lds_read_tr(p), lds_read_tr(p + V8)), pb[ks], acc_o[dt]);
+            }
+#pragma unroll
+            for (int lt = 0; lt < NLT; ++lt) {
+                const char* p = lp + lt * 4 * VBS + ks * 256;
+                acc_lr[lt] = mfma32x32x16(cat4(lds_read_tr(p), lds_read_tr(p + 128)), pb[ks], acc_lr[lt]);
+            }
+        }
+    };
+
+    // ---- prologue: tiles 0 (K, V) and 1 (K) resident, S(0) and its row max
+    wait_dma();
     __syncthreads();
+    if constexpr (ROPE) {
+        rebuild(0, 0);
+        if (n_tiles > 1) rebuild(1, 1);
+        __syncthreads();
+    }
+    f32x16 sA[2], sB[2];
+    s_tile(0, sA);
+    if (!full_tile(0)) mask_tile(0, sA);
+    // Running max, lazily updated: rescale only when a row's tile max exceeds it
+    // by more than 8 (log2 units), so p = exp2(s*scale - m) <= 2^8 -- exact after
+    // the final division, and bf16 / fp32 hold that range.  The floor keeps rows
+    // past q_len (Q = 0, everything masked) free of inf - inf.
+    float m_run = __builtin_fmaxf(tile_max(sA), -1e30f);
+    __syncthreads();  // every S(0) read done before K(2) lands in buffer 0
 
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        const int key0 = t * KT;
-        if (t + 1 < n_tiles) gload(t + 1);
+    // instruction counts of the two overlapped phases (scheduling hints only)
+    constexpr int NS_MFMA = 2 * NKS + (ROPE ? 0 : 2 * NKR);
+    constexpr int NP_MFMA = 4 * (NDT + NLT);
 
-        if constexpr (ROPE) {
-            // rebuild K'[key][dim] = K_base + rot_key(L_k B_k^(h)) in place, waves 0..2*D/64-1:
-            // wave -> (key tile kt, dim tile dt paired with dt + D/64)
-            constexpr int HALF_T = D / 64;
-            if (wave < 2 * HALF_T) {
-                const int kt = wave / HALF_T;
-                const int dt = wave % HALF_T;
-                f32x16 x1 = {}, x2 = {};
-#pragma unroll
-                for (int kr = 0; kr < NKR; ++kr) {
-                    // B_k^T operand: lane (dim 32dt + n32, k-group hh) -> ranks rank_of(kr, e)
-                    bf16x8 b1, b2;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int rk = min(rank_of(kr, e), R - 1);
-                        const bool ok = rank_of(kr, e) < R;
-                        b1[e] = ok ? sBk[rk][32 * dt + n32] : (bf16)0.0f;
-                        b2[e] = ok ? sBk[rk][32 * (dt + HALF_T) + n32] : (bf16)0.0f;
-                    }
-                    // L_k^T operand: lane (key n32, k-group hh) -> ranks rank_of(kr, e)
-                    const bf16* lp = &sLk[buf][32 * kt + n32][16 * kr + 4 * hh];
-                    bf16x8 lb = cat4(*(const bf16x4*)lp, *(const bf16x4*)(lp + 8));
-                    if (16 * kr + 4 * hh >= R) lb = zero8();
-                    x1 = mfma32x32x16(b1, lb, x1);
-                    x2 = mfma32x32x16(b2, lb, x2);
-                }
-                // C lane (key n32, hh): dims 32dt + 8(v/4) + 4hh + v%4 (x1) and +D/2 (x2)
-                const int key = key0 + 32 * kt + n32;
-                const int kc = min(key, kv_len - 1);
-#pragma unroll
-                for (int b4 = 0; b4 < 4; ++b4) {
-                    const int i0 = 32 * dt + 8 * b4 + 4 * hh;
-                    const f32x4 cs = *(const f32x4*)(a.rope_cos + (size_t)kc * (D / 2) + i0);
-                    const f32x4 sn = *(const f32x4*)(a.rope_sin + (size_t)kc * (D / 2) + i0);
-                    bf16* r1 = &sK[buf][32 * kt + n32][i0];
-                    bf16* r2 = r1 + D / 2;
-                    bf16x4 k1 = *(bf16x4*)r1, k2 = *(bf16x4*)r2;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float u1 = x1[4 * b4 + c], u2 = x2[4 * b4 + c];
-                        k1[c] = (bf16)((float)k1[c] + (u1 * cs[c] - u2 * sn[c]));
-                        k2[c] = (bf16)((float)k2[c] + (u2 * cs[c] + u1 * sn[c]));
-                    }
-                    *(bf16x4*)r1 = k1;
-                    *(bf16x4*)r2 = k2;
-                }
-            }
-            __syncthreads();
-        }
+    auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        const bool nxt = t + 1 < n_tiles;
+        if (t + 2 < n_tiles) dma_k(t + 2, B);
+        if (nxt) dma_v(t + 1, B ^ 1);
 
-        // ---- S^T for two 32-key halves
-        f32x16 s[2];
+        // phase 1: S(t+1) on the matrix cores (a stale buffer on the last tile:
+        // unused) while P(t) = exp2(S(t) * scale*log2e - m) runs on the VALU
+        s_tile(B ^ 1, sn);
+        bf16x8 pb[4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            s[mt] = f32x16{};
-            const bf16* kp = &sK[buf][32 * mt + n32][8 * hh];
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) s[mt] = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], s[mt]);
-            if constexpr (!ROPE) {
+            for (int e = 0; e < 8; ++e)
+                pb[ks][e] = (bf16)fast_exp2(__builtin_fmaf(sc[ks >> 1][8 * (ks & 1) + e], sl2, -m_run));
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
 #pragma unroll
-                for (int kr = 0; kr < NKR; ++kr) {
-                    const bf16* lp = &sLk[buf][32 * mt + n32][16 * kr + 4 * hh];
-                    bf16x8 lb = cat4(*(const bf16x4*)lp, *(const bf16x4*)(lp + 8));
-                    if (16 * kr + 4 * hh >= R) lb = zero8();
-                    s[mt] = mfma32x32x16(lb, qbf[kr], s[mt]);
-                }
-            }
+        for (int i = 0; i < NS_MFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU / transcendental
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
-        // ---- online softmax (row = lane % 32; the two k-groups hold disjoint keys).
-        // Tiles entirely below the causal diagonal of the workgroup's first token
-        // skip the mask.  The running max is updated lazily: only when some row's
-        // tile max exceeds it by more than 8 (log2 units) are the accumulators
-        // rescaled, so p = exp2(s*scale - m) <= 2^8 — exact after the final
-        // division, and bf16 / fp32 hold that range.  Rows past q_len (Q = 0) never
-        // reach the output.
-        const bool full = key0 + KT - 1 <= kv_len - q_len + tok_wg;
-        if (!full) {
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]));  // P(t) complete here
+
+        if (nxt && !full_tile(t + 1)) mask_tile(t + 1, sn);
+
+        // phase 2: O += P(t) V(t) on the matrix cores, row max of S(t+1) on the VALU
+        pv_tile(B, pb);
+        const float mx = tile_max(sn);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = key0 + 32 * mt + 8 * (v >> 2) + 4 * hh + (v & 3);
-                    s[mt][v] = key <= qpos ? s[mt][v] : -INFINITY;
-                }
+        for (int i = 0; i < NP_MFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[mt][v], s[mt][v + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
-            const float m_new = fmaxf(m_run, mx);
+        if (nxt && __builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+            const float m_new = __builtin_fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) acc_o[dt] *= alpha;
@@ -335,44 +486,18 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
             for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] *= alpha;
             m_run = m_new;
         }
-        bf16x8 pb[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pb[ks][e] = (bf16)fast_exp2(__builtin_fmaf(s[ks >> 1][8 * (ks & 1) + e], sl2, -m_run));
-
-        // ---- O^T += V^T P^T and O_lr^T += L_v^T P^T (16 keys per k-step)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int k0 = 32 * (ks >> 1) + 16 * (ks & 1) + 4 * hh;  // keys of slots 0..3; +8 for 4..7
-            const int srow = k0 + (i16 >> 2);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const bf16* vp = &sV[buf][srow][32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3)];
-                const bf16x8 va = cat4(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
-                acc_o[dt] = mfma32x32x16(va, pb[ks], acc_o[dt]);
-            }
-#pragma unroll
-            for (int lt = 0; lt < NLT; ++lt) {
-                // A rows m = 32lt + lane%32: ranks (< R) from L_v^T, then the ones
-                // row (m == R, giving sum_j p_j), then zeros.  The transposing read
-                // runs on every lane (rows >= R read an in-bounds dummy column and
-                // are overwritten after): under a lane-divergent branch it also
-                // overwrote the inactive lanes' destination registers.
-                const int col = 32 * lt + 16 * (g16 & 1);
-                const bf16* lp = &sLv[buf][srow][(col < R ? col : 0) + 4 * (i16 & 3)];
-                bf16x8 la = cat4(lds_read_tr(lp), lds_read_tr(lp + 8 * RV));
-                const int m = 32 * lt + n32;
-                if (m >= R) la = m == R ? ones8() : zero8();
-                acc_lr[lt] = mfma32x32x16(la, pb[ks], acc_lr[lt]);
-            }
-        }
-
-        if (t + 1 < n_tiles) {
-            lstore(buf ^ 1);
-        }
+        wait_dma();
         __syncthreads();
+        if constexpr (ROPE) {
+            if (t + 2 < n_tiles) {
+                rebuild(t + 2, B);
+                __syncthreads();
+            }
+        }
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, 0, sA, sB);
+        if (t + 1 < n_tiles) step(t + 1, 1, sB, sA);
     }
 
     // ---- epilogue: l from the ones row; O^T += B_v^T O_lr^T; divide; store
@@ -441,6 +566,11 @@ lra_status launch_t(const lra::PrefillArgs& p, hipStream_t s) {
     const int tw = 32 / k.g;
     k.n_qblk = (p.q_len + WAVES * tw - 1) / (WAVES * tw);
     k.scale_log2 = p.scale * LRA_LOG2E;
+    // tiles are addressed through 32-bit buffer ranges of kv_len rows of 2*D bytes
+    if ((long long)p.kv_len * 2 * D > 0x7fffffffLL) {
+        lra::set_error("prefill: kv_len %d too long for 32-bit tile addressing", p.kv_len);
+        return LRA_ERR_BAD_SHAPE;
+    }
     const long long grid = (long long)p.n_req * p.h_kv * k.n_qblk;
     if (grid > 0x7fffffffLL) {
         lra::set_error("prefill: grid of %lld workgroups too large", grid);
