@@ -44,6 +44,8 @@
 // S(t+1) is on the matrix cores while the softmax of S(t) runs on the VALU,
 // followed by P(t)V(t) with the row max of S(t+1) in its shadow; one barrier
 // per tile (two with RoPE: raw K(t+2) lands, K'(t+2) is rebuilt in place).
+#include <type_traits>
+
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -442,37 +444,49 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int NS_MFMA = 2 * NKS + (ROPE ? 0 : 2 * NKR);
     constexpr int NP_MFMA = 4 * (NDT + NLT);
 
-    auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const bool nxt = t + 1 < n_tiles;
-        if (t + 2 < n_tiles) dma_k(t + 2, B);
-        if (nxt) dma_v(t + 1, B ^ 1);
-
-        // phase 1: S(t+1) on the matrix cores (a stale buffer on the last tile:
-        // unused) while P(t) = exp2(S(t) * scale*log2e - m) runs on the VALU
-        s_tile(B ^ 1, sn);
-        bf16x8 pb[4];
+    // phase 1 of tile t: S(t+1) from K buffer kb on the matrix cores (a stale
+    // buffer on the last tile: unused) while P(t) = exp2(S(t)*scale*log2e - m)
+    // of keys 0 .. 16*n_exp - 1 runs on the VALU
+    auto exp_p = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4], int ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pb[ks][e] = (bf16)fast_exp2(__builtin_fmaf(sc[ks >> 1][8 * (ks & 1) + e], sl2, -m_run));
+    };
+    auto phase1 = [&](int kb, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pb)[4], auto n_exp_c) {
+        constexpr int n_exp = decltype(n_exp_c)::value;
+        s_tile(kb, sn);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pb[ks][e] = (bf16)fast_exp2(__builtin_fmaf(sc[ks >> 1][8 * (ks & 1) + e], sl2, -m_run));
+            if (ks < n_exp) exp_p(sc, pb, ks);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
 #pragma unroll
         for (int i = 0; i < NS_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU / transcendental
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 2 * n_exp - 1, 0);  // VALU / transcendental
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               // DS read
         }
-        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]));  // P(t) complete here
-
+    };
+    // phase 2 of tile t: O += P(t) V(t) from V buffer vb on the matrix cores
+    // (exp of keys 16*n_done.. first), row max of S(t+1) on the VALU, then the
+    // lazy rescale
+    auto phase2 = [&](int t, int vb, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pb)[4], auto n_done_c) {
+        constexpr int n_done = decltype(n_done_c)::value;
+        const bool nxt = t + 1 < n_tiles;
         if (nxt && !full_tile(t + 1)) mask_tile(t + 1, sn);
-
-        // phase 2: O += P(t) V(t) on the matrix cores, row max of S(t+1) on the VALU
-        pv_tile(B, pb);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            if (ks >= n_done) exp_p(sc, pb, ks);
+        pv_tile(vb, pb);
         const float mx = tile_max(sn);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < NP_MFMA; ++i) {
+        for (int i = 0; i < NP_MFMA / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, n_done < 4 ? 4 : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int i = NP_MFMA / 2; i < NP_MFMA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -486,6 +500,17 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
             for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] *= alpha;
             m_run = m_new;
         }
+    };
+
+    // one tile per barrier interval: K(t+2) and V(t+1) land while tile t runs
+    using I2 = std::integral_constant<int, 2>;
+    bf16x8 pb[4];
+    auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        if (t + 2 < n_tiles) dma_k(t + 2, B);
+        if (t + 1 < n_tiles) dma_v(t + 1, B ^ 1);
+        phase1(B ^ 1, sc, sn, pb, I2{});
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]));  // keys 0..31 of P(t) complete here
+        phase2(t, B, sc, sn, pb, I2{});
         wait_dma();
         __syncthreads();
         if constexpr (ROPE) {
