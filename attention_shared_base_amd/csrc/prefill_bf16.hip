@@ -427,7 +427,6 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     __syncthreads();
     if constexpr (ROPE) {
         rebuild(0, 0);
-        if (n_tiles > 1) rebuild(1, 1);
         __syncthreads();
     }
     f32x16 sA[2], sB[2];
@@ -502,27 +501,71 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         }
     };
 
-    // one tile per barrier interval: K(t+2) and V(t+1) land while tile t runs
     using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
     bf16x8 pb[4];
-    auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        if (t + 2 < n_tiles) dma_k(t + 2, B);
-        if (t + 1 < n_tiles) dma_v(t + 1, B ^ 1);
-        phase1(B ^ 1, sc, sn, pb, I2{});
-        asm volatile("" ::"v"(pb[0]), "v"(pb[1]));  // keys 0..31 of P(t) complete here
-        phase2(t, B, sc, sn, pb, I2{});
+    if constexpr (!ROPE) {
+        // one tile per barrier interval: K(t+2) and V(t+1) land while tile t runs
+        auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+            if (t + 2 < n_tiles) dma_k(t + 2, B);
+            if (t + 1 < n_tiles) dma_v(t + 1, B ^ 1);
+            phase1(B ^ 1, sc, sn, pb, I2{});
+            asm volatile("" ::"v"(pb[0]), "v"(pb[1]));  // keys 0..31 of P(t) complete here
+            phase2(t, B, sc, sn, pb, I2{});
+            wait_dma();
+            __syncthreads();
+        };
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(t, 0, sA, sB);
+            if (t + 1 < n_tiles) step(t + 1, 1, sB, sA);
+        }
+    } else {
+        // RoPE: the key tile has to be rebuilt (K' = K + rot(L_k B_k)) between its
+        // arrival and its score MFMAs.  Step t runs
+        //   A: O += P(t-1) V(t-1) on the matrix cores, with the row max of S(t)
+        //      and the rebuild of K'(t+1) on the VALU;  barrier;
+        //   B: S(t+1) from K'(t+1) on the matrix cores, P(t) on the VALU.
+        // Step t loads K(t+2) (with its L_k rows and cos / sin tiles) and V(t).
+        // step 0: no P V yet
+        if (n_tiles > 2) dma_k(2, 0);
+        rebuild(1, 1);  // a stale buffer when n_tiles == 1: never read
+        __syncthreads();
+        phase1(1, sA, sB, pb, I4{});
         wait_dma();
         __syncthreads();
-        if constexpr (ROPE) {
-            if (t + 2 < n_tiles) {
-                rebuild(t + 2, B);
-                __syncthreads();
+        auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+            if (t + 2 < n_tiles) dma_k(t + 2, B);
+            dma_v(t, B);
+            if (!full_tile(t)) mask_tile(t, sc);
+            pv_tile(B ^ 1, pb);
+            const float mx = tile_max(sc);
+            rebuild(t + 1, B ^ 1);  // a stale buffer on the last tile: never read
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NP_MFMA + 2 * NKR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+                const float m_new = __builtin_fmaxf(m_run, mx);
+                const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) acc_o[dt] *= alpha;
+#pragma unroll
+                for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] *= alpha;
+                m_run = m_new;
+            }
+            __syncthreads();
+            phase1(B ^ 1, sc, sn, pb, I4{});
+            wait_dma();
+            __syncthreads();
+        };
+        for (int t = 1; t < n_tiles; t += 2) {
+            step(t, 1, sB, sA);
+            if (t + 1 < n_tiles) step(t + 1, 0, sA, sB);
         }
-    };
-    for (int t = 0; t < n_tiles; t += 2) {
-        step(t, 0, sA, sB);
-        if (t + 1 < n_tiles) step(t + 1, 1, sB, sA);
+        pv_tile((n_tiles - 1) & 1, pb);
     }
 
     // ---- epilogue: l from the ones row; O^T += B_v^T O_lr^T; divide; store
