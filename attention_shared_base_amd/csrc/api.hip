@@ -85,19 +85,19 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     const long long units = (long long)n_ctx * p->n_rg * d.n_kv_heads;
     if (units > (1 << 26)) return false;
     p->n_units = (int)units;
-    // Chunk length (tokens per workgroup, a power of two in [256, 2048] so the
+    // Chunk length (tokens per workgroup, a power of two in [256, 4096] so the
     // kernel's per-wavefront step count is a compile-time constant): enough
     // workgroups to fill 256 CUs a few times over, each wavefront still
     // streaming several 32-token steps.
     int chunk = env_int("LRA_DECODE_CHUNK", 0);
-    if (chunk != 256 && chunk != 512 && chunk != 1024 && chunk != 2048) {
+    if (chunk != 256 && chunk != 512 && chunk != 1024 && chunk != 2048 && chunk != 4096) {
         // ~one workgroup per CU at the longest context; longer chunks amortise
         // each workgroup's fixed prologue/merge cost (measured best on MI355X:
-        // 1024 tokens for 4 x 8192-token contexts, 2048 for 4k-64k contexts).
+        // 1024 tokens for 4 x 8192-token contexts, 4096 for 4k-64k contexts).
         const int target = env_int("LRA_DECODE_TARGET_WG", 256);
         const long long c = ((long long)max_ctx_len * units + target - 1) / (target > 0 ? target : 256);
         chunk = 256;
-        while (chunk < 2048 && chunk < c) chunk *= 2;
+        while (chunk < 4096 && chunk < c) chunk *= 2;
     }
     p->chunk = chunk;
     p->n_split = max_ctx_len > 0 ? (max_ctx_len + chunk - 1) / chunk : 1;

@@ -42,7 +42,6 @@ namespace {
 
 constexpr int PAGE = 16;
 constexpr int ROWS = 16;
-constexpr int WAVES = 4;
 constexpr int KEYS_PER_STEP = 32;  // two pages per wavefront step
 
 struct DecodeK {
@@ -73,21 +72,21 @@ struct DecodeK {
 // of each k-group carry ranks 4*q4 + v, slots 4-7 carry ranks 16 + 4*q4 + v
 // or zeros).
 
-template <int D, int R, int SP>
-__device__ __forceinline__ void finalize_rows_impl(const DecodeK& a, const float (*o)[SP],
-                                                   const float* L_row, int n, int cl, int nrows,
-                                                   int req0, int h);
+// B_v^(h) columns c0 .. c0 + D/16 - 1 of every rank, for one output thread
+template <int D, int R>
+struct BvCols {
+    typedef __bf16 vec __attribute__((ext_vector_type(D / 16)));
+    vec r[R];
+};
 
 template <int D, int R, int SP>
 __device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)[SP], const float* L_row,
-                                              int n, int cl, int nrows, int req0, int h) {
-    finalize_rows_impl<D, R, SP>(a, o, L_row, n, cl, nrows, req0, h);
-}
+                                              int n, int cl, int nrows, int req0, int h,
+                                              const BvCols<D, R>& bv);
 
 template <int D, int R, int SP>
 __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
-                                               int n, int cl, float (*o_out)[SP], float* L_out,
-                                               float (*sm_w)[16]);
+                                               int n, int cl, float (*o_out)[SP], float* L_out);
 
 template <int D, int R>
 struct Step {
@@ -100,10 +99,11 @@ struct Step {
     bf16x4 lv[2][NRT];
 };
 
-// SPW = 32-token steps per wavefront; a workgroup covers WAVES * SPW * 32 tokens.
-// DEPTH = step buffers per wavefront (DEPTH - 1 steps of loads in flight).
-template <int D, int R, int SPW, int DEPTH>
-__global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
+// WAVES wavefronts per workgroup; SPW = 32-token steps per wavefront; a
+// workgroup covers WAVES * SPW * 32 tokens.  DEPTH = step buffers per
+// wavefront (DEPTH - 1 steps of loads in flight).
+template <int D, int R, int SPW, int DEPTH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) {
     constexpr int NJ = Step<D, R>::NJ;
     constexpr int NDT = Step<D, R>::NDT;
     constexpr int NRT = Step<D, R>::NRT;
@@ -116,7 +116,6 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
     __shared__ float sm_l[WAVES][ROWS];
     __shared__ float sm_M[ROWS];
     __shared__ float sm_L[ROWS];
-    __shared__ float sm_w[64][ROWS];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
@@ -127,6 +126,13 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15;  // row (S^T / O^T column) of this lane
     const int q4 = lane >> 4;   // k-group of this lane
+
+    // all kernel arguments in one scalar round trip (the compiler would otherwise
+    // fetch them piecemeal between the dependent loads below)
+    asm volatile("" ::"s"(a.k_pool), "s"(a.v_pool), "s"(a.lk_pool), "s"(a.lv_pool), "s"(a.block_table),
+                 "s"(a.ctx_len), "s"(a.ctx_req_start), "s"(a.q), "s"(a.b_k), "s"(a.req_agent));
+    asm volatile("" ::"s"(a.n_ctx), "s"(a.n_pages), "s"(a.max_blocks), "s"(a.n_agents), "s"(a.h_q),
+                 "s"(a.h_kv), "s"(a.g), "s"(a.rpg), "s"(a.n_rg), "s"(a.n_split));
 
     // XCD-aware placement: workgroup b runs on XCD b % 8; remap so that the
     // KV heads of one (context, chunk) — which share its L_k/L_v pages — are
@@ -143,14 +149,32 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
     if (ctx >= a.n_ctx) return;
     const int unit = (ctx * a.n_rg + rg) * a.h_kv + h;
 
+    // ---- every scalar load the step addresses depend on goes out at once,
+    // before any branch on their values: request range and length of the
+    // context, and the raw page-table entries of this wavefront's steps (rows
+    // clamped to the table; pages past the chunk end are replaced below).
+    const int* bt = a.block_table + (size_t)ctx * a.max_blocks;
+    const int kbeg = split * CHUNK;
     const int rs0 = a.ctx_req_start[ctx];
     const int rs1 = a.ctx_req_start[ctx + 1];
+    const int len_raw = a.ctx_len[ctx];
+    const int first_raw = bt[min(kbeg >> 4, a.max_blocks - 1)];
+    int praw[SPW][2];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            praw[i][t] = bt[min((kbeg >> 4) + 2 * (wave + WAVES * i) + t, a.max_blocks - 1)];
+    asm volatile("" ::"s"(rs0), "s"(rs1), "s"(len_raw), "s"(first_raw));
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) asm volatile("" ::"s"(praw[i][0]), "s"(praw[i][1]));
+
     const int req0 = rs0 + rg * a.rpg;
     const int nreq = min(a.rpg, rs1 - req0);
     if (nreq <= 0) return;
     const int g = a.g;
     const int nrows = nreq * g;
-    const int len = min(a.ctx_len[ctx], a.max_blocks * PAGE);
+    const int len = min(len_raw, a.max_blocks * PAGE);
 
     if (len <= 0) {  // empty context: defined as zero output
         if (split == 0) {
@@ -163,20 +187,19 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
     }
     const int n_active = (len + CHUNK - 1) / CHUNK;
     if (split >= n_active) return;
-    const int kbeg = split * CHUNK;
     const int kend = min(len, kbeg + CHUNK);
 
-    // ---- page ids of this wavefront's steps (scalar loads).  Pages past the
-    // chunk end are clamped to its last page: those steps load cached data and
-    // are never computed, so the loads can stay unconditional.
-    const int* bt = a.block_table + (size_t)ctx * a.max_blocks;
+    // ---- page ids of this wavefront's steps.  Pages past the chunk end take
+    // the chunk's first page: those steps load cached data and are never
+    // computed, so the loads can stay unconditional.
     const int last_pg = (kend - 1) >> 4;
     int pid[SPW][2];
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int pg = (kbeg >> 4) + 2 * (wave + WAVES * i);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) pid[i][t] = min(max(bt[min(pg + t, last_pg)], 0), a.n_pages - 1);
+        for (int t = 0; t < 2; ++t)
+            pid[i][t] = min(max(pg + t <= last_pg ? praw[i][t] : first_raw, 0), a.n_pages - 1);
     }
 
     const size_t kv_page = (size_t)a.h_kv * D * PAGE;  // elements per page (all heads)
@@ -214,6 +237,12 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         }
     };
 
+    // agent ids of the group's first four requests: requested before the step
+    // loads, so that waiting for them does not wait for those
+    int agent0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) agent0[u] = a.req_agent[req0 + min(u, nreq - 1)];
+
     // ---- the first DEPTH-1 steps' loads go out before the prologue's dependent chain
     Step<D, R> buf[DEPTH];
 #pragma unroll
@@ -221,38 +250,59 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         if (i < SPW) load(buf[i], i);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- query operand (B of the score MFMA): lane holds dims 32j+8*q4.. of row n16
+    // ---- query operand (B of the score MFMA): lane holds dims 32j+8*q4.. of row
+    // n16.  Loaded unconditionally (rows past nrows read row 0 and are zeroed
+    // just before use): a branch here would drain the step loads in flight.
     const bool row_ok = n16 < nrows;
     bf16x8 qf[NJ];
     {
-        const bf16* qp = a.q + ((size_t)(req0 + n16 / g) * a.h_q + h * g + n16 % g) * D + 8 * q4;
+        const int qr = row_ok ? n16 : 0;
+        const bf16* qp = a.q + ((size_t)(req0 + qr / g) * a.h_q + h * g + qr % g) * D + 8 * q4;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) qf[j] = row_ok ? ldg((const bf16x8*)(qp + 32 * j)) : zero8();
+        for (int j = 0; j < NJ; ++j) qf[j] = ldg((const bf16x8*)(qp + 32 * j));
     }
 
     // ---- pre-projection qB = q B_k^(h)T, one MFMA tile per request of the group.
     // C lane layout: rank 16*rt + 4*q4 + v of row n16 — already the B operand
-    // layout of the rank-r score MFMA.
+    // layout of the rank-r score MFMA.  The agent ids of up to four requests
+    // are fetched together, then all their B_k rows: two memory round trips in
+    // all, overlapping the first step's loads.
     f32x4 qbacc[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) qbacc[rt] = zf4();
-    for (int s = 0; s < nreq; ++s) {
-        int agent = a.req_agent[req0 + s];
-        agent = min(max(agent, 0), a.n_agents - 1);
+    const size_t bcols = (size_t)a.h_kv * D;
+    for (int s0 = 0; s0 < nreq; s0 += 4) {
+        int agent[4];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            const int rank = 16 * rt + n16;
-            const bf16* bp_ = a.b_k + ((size_t)agent * R + min(rank, R - 1)) * ((size_t)a.h_kv * D) +
-                              (size_t)h * D + 8 * q4;
-            f32x4 c = zf4();
+        for (int u = 0; u < 4; ++u) agent[u] = s0 == 0 ? agent0[u] : a.req_agent[req0 + min(s0 + u, nreq - 1)];
+        asm volatile("" ::"s"(agent[0]), "s"(agent[1]), "s"(agent[2]), "s"(agent[3]));
+        bf16x8 bk[4][NRT][NJ];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                bf16x8 bk = ldg((const bf16x8*)(bp_ + 32 * j));
-                if (rank >= R) bk = zero8();
-                c = mfma16x16x32(bk, qf[j], c);
+        for (int u = 0; u < 4; ++u) {
+            const int ag = min(max(agent[u], 0), a.n_agents - 1);
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int rank = 16 * rt + n16;
+                const bf16* bp_ = a.b_k + ((size_t)ag * R + min(rank, R - 1)) * bcols + (size_t)h * D + 8 * q4;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bk[u][rt][j] = ldg((const bf16x8*)(bp_ + 32 * j));
             }
-            if (n16 / g == s) qbacc[rt] = c;
         }
+        __builtin_amdgcn_sched_barrier(0);  // every B_k load issued before the first wait
+        if (s0 == 0) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) qf[j] = row_ok ? qf[j] : zero8();
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                f32x4 c = zf4();
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    c = mfma16x16x32(16 * rt + n16 < R ? bk[u][rt][j] : zero8(), qf[j], c);
+                if (n16 / g == s0 + u) qbacc[rt] = c;
+            }
     }
     bf16x8 qb;
 #pragma unroll
@@ -373,7 +423,7 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
 
     const int n = tid >> 4;   // row handled by this thread in the epilogues
     const int cl = tid & 15;  // column phase
-    {
+    if (tid < ROWS * 16) {
         float mw[WAVES];
         float M = -INFINITY;
 #pragma unroll
@@ -398,6 +448,19 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
             sm_M[n] = M;
             sm_L[n] = L;
         }
+    }
+
+    // B_v^(h) columns of this thread's output row, fetched now: they are needed
+    // only by the workgroup that finalizes, but their latency then overlaps the
+    // partial stores and the counter round trip instead of following them.
+    BvCols<D, R> bvc;
+    if (n < nrows) {
+        int agent = a.req_agent[req0 + n / g];
+        agent = min(max(agent, 0), a.n_agents - 1);
+        const bf16* bv = a.b_v + (size_t)agent * R * a.h_kv * D + (size_t)h * D + cl * (D / 16);
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+            bvc.r[t] = ldg((const typename BvCols<D, R>::vec*)(bv + (size_t)t * a.h_kv * D));
     }
 
     if (n_active > 1) {
@@ -432,24 +495,26 @@ __global__ __launch_bounds__(256) void lra_decode_bf16_kernel(DecodeK a) {
         }
         __syncthreads();
         if (!sm_last) return;
-        merge_partials<D, R, SP>(a, unit, n_active, nrows, n, cl, sm_o[0], sm_L, sm_w);
+        merge_partials<D, R, SP>(a, unit, n_active, nrows, n, cl, sm_o[0], sm_L);
         if (tid == 0) __hip_atomic_store(a.ws_count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    finalize_rows<D, R, SP>(a, sm_o[0], sm_L, n, cl, nrows, req0, h);
+    finalize_rows<D, R, SP>(a, sm_o[0], sm_L, n, cl, nrows, req0, h, bvc);
 }
 
 // Log-sum-exp merge of the chunk partials of one work unit into o[row][0..DR)
-// and L[row]; sm_w is [GS][16] scratch.  Runs in the last workgroup to finish.
+// and L[row].  Runs in the last workgroup to finish.  Thread (row n, phase cl)
+// owns columns cl, cl + 16, ...; the partials of up to GB chunks (their maxima,
+// sums and columns) are requested together, so a merge of <= GB chunks waits
+// for one memory round trip.
 template <int D, int R, int SP>
 __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
-                                               int n, int cl, float (*o_out)[SP], float* L_out,
-                                               float (*sm_w)[ROWS]) {
+                                               int n, int cl, float (*o_out)[SP], float* L_out) {
     constexpr int DR = D + R;
     constexpr int PW = DR + 2;
     constexpr int NC = (DR + 15) / 16;  // columns per thread
-    constexpr int GS = 64;              // chunks merged per pass
-    const bool row_ok = n < nrows;
+    constexpr int GB = 8;               // chunks per batch
+    if (n >= nrows) return;
     const float* base = a.ws_part + (size_t)unit * a.n_split * ROWS * PW + n * PW;
     const size_t sstride = (size_t)ROWS * PW;
     auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
@@ -457,57 +522,35 @@ __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n
     float o[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) o[k] = 0.f;
-    for (int g0 = 0; g0 < n_active; g0 += GS) {
-        const int ns = min(GS, n_active - g0);
-        // the 16 threads of a row split the chunks for max and sum
-        float mv[GS / 16], lv[GS / 16];
-        float mloc = -INFINITY;
+    for (int g0 = 0; g0 < n_active; g0 += GB) {
+        float mv[GB], lv[GB], ov[GB][NC];
 #pragma unroll
-        for (int k = 0; k < GS / 16; ++k) {
-            const int sp = cl + 16 * k;
-            const bool ok = row_ok && sp < ns;
-            mv[k] = ok ? ld(base + (g0 + sp) * sstride + DR) : -INFINITY;
-            lv[k] = ok ? ld(base + (g0 + sp) * sstride + DR + 1) : 0.f;
-            mloc = fmaxf(mloc, mv[k]);
-        }
+        for (int u = 0; u < GB; ++u) {
+            const bool ok = g0 + u < n_active;
+            const float* p = base + (size_t)(ok ? g0 + u : g0) * sstride;
+            mv[u] = ok ? ld(p + DR) : -INFINITY;
+            lv[u] = ok ? ld(p + DR + 1) : 0.f;
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 16));
-        const float M_new = fmaxf(M, mloc);
-        const float resc = M == -INFINITY ? 0.f : fast_exp2(M - M_new);
-        float lloc = 0.f;
-#pragma unroll
-        for (int k = 0; k < GS / 16; ++k) {
-            const int sp = cl + 16 * k;
-            const float w = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - M_new);
-            lloc += w * lv[k];
-            if (sp < ns) sm_w[sp][n] = w;
-        }
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off, 16);
-        L = L * resc + lloc;
-        M = M_new;
-        __syncthreads();
-        if (row_ok) {
-#pragma unroll
-            for (int k = 0; k < NC; ++k) o[k] *= resc;
-            for (int sp0 = 0; sp0 < ns; sp0 += 4) {
-                float v[4][NC];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int k = 0; k < NC; ++k) {
-                        const int c = cl + 16 * k;
-                        v[u][k] = (sp0 + u < ns && c < DR) ? ld(base + (g0 + sp0 + u) * sstride + c) : 0.f;
-                    }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float w = sp0 + u < ns ? sm_w[sp0 + u][n] : 0.f;
-#pragma unroll
-                    for (int k = 0; k < NC; ++k) o[k] += w * v[u][k];
-                }
+            for (int k = 0; k < NC; ++k) {
+                const int c = cl + 16 * k;
+                ov[u][k] = (ok && c < DR) ? ld(p + c) : 0.f;
             }
         }
-        __syncthreads();
+        float M_new = M;
+#pragma unroll
+        for (int u = 0; u < GB; ++u) M_new = fmaxf(M_new, mv[u]);
+        const float resc = M == -INFINITY ? 0.f : fast_exp2(M - M_new);
+        L *= resc;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) o[k] *= resc;
+#pragma unroll
+        for (int u = 0; u < GB; ++u) {
+            const float w = mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - M_new);
+            L += w * lv[u];
+#pragma unroll
+            for (int k = 0; k < NC; ++k) o[k] += w * ov[u][k];
+        }
+        M = M_new;
     }
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
@@ -518,41 +561,35 @@ __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n
 }
 
 // O = (O_base + O_lr B_v^(h)) / l for the rows of one work unit: the single
-// post-multiplication by B_v per query row.  `o` holds [O_base | O_lr] per row.
+// post-multiplication by B_v per query row.  `o` holds [O_base | O_lr] per row;
+// thread (n, cl) owns D/16 contiguous output columns (one vector store).
 template <int D, int R, int SP>
-__device__ __forceinline__ void finalize_rows_impl(const DecodeK& a, const float (*o)[SP],
-                                                   const float* L_row, int n, int cl, int nrows,
-                                                   int req0, int h) {
+__device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)[SP], const float* L_row,
+                                              int n, int cl, int nrows, int req0, int h,
+                                              const BvCols<D, R>& bv) {
     if (n >= nrows) return;
-    // thread (n, cl) owns D/16 contiguous output columns: one vector load of
-    // B_v per rank, one vector store
     constexpr int CPT = D / 16;
-    typedef __bf16 bfv __attribute__((ext_vector_type(CPT)));
     const int g = a.g;
     const int req = req0 + n / g;
-    int agent = a.req_agent[req];
-    agent = min(max(agent, 0), a.n_agents - 1);
     const float L = L_row[n];
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     const int c0 = cl * CPT;
-    const bf16* bv = a.b_v + (size_t)agent * R * a.h_kv * D + (size_t)h * D + c0;
     float acc[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) acc[k] = o[n][c0 + k];
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-        const bfv b = ldg((const bfv*)(bv + (size_t)t * a.h_kv * D));
         const float w = o[n][D + t];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) acc[k] += w * (float)b[k];
+        for (int k = 0; k < CPT; ++k) acc[k] += w * (float)bv.r[t][k];
     }
-    bfv res;
+    typename BvCols<D, R>::vec res;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) res[k] = (bf16)(acc[k] * inv);
-    *(bfv*)(a.out + ((size_t)req * a.h_q + h * g + n % g) * D + c0) = res;
+    *(typename BvCols<D, R>::vec*)(a.out + ((size_t)req * a.h_q + h * g + n % g) * D + c0) = res;
 }
 
-template <int D, int R, int SPW, int DEPTH>
+template <int D, int R, int SPW, int DEPTH, int W>
 lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
     DecodeK k;
     k.q = (const bf16*)a.q;
@@ -580,21 +617,26 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.n_rg = p.n_rg;
     k.n_split = p.n_split;
     k.scale_log2 = a.scale * LRA_LOG2E;
-    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH>), dim3(p.grid), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W>), dim3(p.grid), dim3(64 * W), 0, s, k);
     return lra::check_launch("lra_decode_bf16_kernel");
 }
 
-template <int D, int R, int DEPTH>
+template <int D, int R, int DEPTH, int W>
 lra_status launch_depth(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
+    // chunk = W * SPW * 32 tokens
+    constexpr int S256 = 256 / (32 * W);
     switch (p.chunk) {
-        case 256: return launch_t<D, R, 2, (DEPTH < 2 ? DEPTH : 2)>(a, p, s);
-        case 512: return launch_t<D, R, 4, DEPTH>(a, p, s);
-        case 1024: return launch_t<D, R, 8, DEPTH>(a, p, s);
-        case 2048: return launch_t<D, R, 16, DEPTH>(a, p, s);
-        default:
-            lra::set_error("decode: unsupported chunk %d", p.chunk);
-            return LRA_ERR_UNSUPPORTED;
+        case 256:
+            if constexpr (S256 >= 1) return launch_t<D, R, S256, (DEPTH < S256 ? DEPTH : S256 < 2 ? 2 : DEPTH), W>(a, p, s);
+            break;
+        case 512: return launch_t<D, R, 512 / (32 * W), DEPTH, W>(a, p, s);
+        case 1024: return launch_t<D, R, 1024 / (32 * W), DEPTH, W>(a, p, s);
+        case 2048: return launch_t<D, R, 2048 / (32 * W), DEPTH, W>(a, p, s);
+        case 4096: return launch_t<D, R, 4096 / (32 * W), DEPTH, W>(a, p, s);
+        default: break;
     }
+    lra::set_error("decode: unsupported chunk %d", p.chunk);
+    return LRA_ERR_UNSUPPORTED;
 }
 
 template <int D, int R>
@@ -602,11 +644,19 @@ lra_status launch_dr(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStre
     static const int depth = [] {
         const char* e = getenv("LRA_DECODE_DEPTH");
         const int v = e ? atoi(e) : 2;
-        return v == 2 || v == 3 || v == 4 ? v : 2;
+        return v == 2 || v == 3 ? v : 2;
     }();
-    if (depth == 3) return launch_depth<D, R, 3>(a, p, s);
-    if (depth == 4) return launch_depth<D, R, 4>(a, p, s);
-    return launch_depth<D, R, 2>(a, p, s);
+    static const int waves = [] {
+        const char* e = getenv("LRA_DECODE_WAVES");
+        const int v = e ? atoi(e) : 4;
+        return v == 8 ? 8 : 4;
+    }();
+    if (waves == 8) {
+        if (depth == 3) return launch_depth<D, R, 3, 8>(a, p, s);
+        return launch_depth<D, R, 2, 8>(a, p, s);
+    }
+    if (depth == 3) return launch_depth<D, R, 3, 4>(a, p, s);
+    return launch_depth<D, R, 2, 4>(a, p, s);
 }
 
 }  // namespace

@@ -79,7 +79,7 @@ def test_decode_split_count_invariance():
     d = DecodeDev(case)
     outs = []
     try:
-        for chunk in ("256", "512", "1024", "2048"):
+        for chunk in ("256", "512", "1024", "2048", "4096"):
             os.environ["LRA_DECODE_CHUNK"] = chunk
             outs.append(host(d.run()))
     finally:
