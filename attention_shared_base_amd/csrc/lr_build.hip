@@ -11,7 +11,9 @@
 // interleaved 32-wide slices of d_model (so together they stream each X row
 // contiguously) and each accumulates the full 16 x 2r tile with
 // v_mfma_f32_16x16x32_bf16; the eight partial tiles are summed in LDS and
-// rounded once to bf16.
+// rounded once to bf16.  Every wavefront issues the X and A loads of up to 16
+// of its slices (8 for r = 32) before the first MFMA, so the whole product waits for about
+// one memory round trip instead of one per slice.
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -28,8 +30,9 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
                                                                 bf16* __restrict__ l_v,
                                                                 int n_tok, int d_model,
                                                                 long long row_offset) {
-    constexpr int NT = (2 * R + 15) / 16;  // 16-column output tiles
+    constexpr int NT = 2 * R / 16;  // 16-column output tiles (R = 8, 16, 32)
     constexpr int NC = NT * 16;
+    constexpr int BATCH = R == 32 ? 8 : 16;  // k-slices per wavefront in flight
     __shared__ float sm[WAVES][TOK][NC + 1];
 
     const int tid = threadIdx.x;
@@ -37,32 +40,44 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
     const int l16 = lane & 15, kq = lane >> 4;
     const int tok0 = blockIdx.x * TOK;
 
-    const bool tok_ok = tok0 + l16 < n_tok;
-    const bf16* xp = x + (size_t)(tok0 + l16) * d_model + 8 * kq;
+    // rows past n_tok read a valid row; their results are never stored
+    const bf16* xp = x + (size_t)min(tok0 + l16, n_tok - 1) * d_model + 8 * kq;
     const bf16* wp[NT];
-    bool col_ok[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int col = nt * 16 + l16;
-        col_ok[nt] = col < 2 * R;
-        const bf16* base = col < R ? a_k + (size_t)col * d_model
-                                   : a_v + (size_t)(col_ok[nt] ? col - R : 0) * d_model;
-        wp[nt] = base + 8 * kq;
+        wp[nt] = (col < R ? a_k + (size_t)col * d_model : a_v + (size_t)(col - R) * d_model) + 8 * kq;
     }
 
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = zf4();
 
+    // A wavefront takes two adjacent 32-wide slices at a time, so that its two
+    // loads per token cover one whole 128-byte line of X.  Every workgroup reads
+    // all of A_k and A_v; each starts at its own slice offset so that they do
+    // not all request the same A lines (one L2 channel) at once.
     const int n_steps = d_model / 32;
-#pragma unroll 4
-    for (int st = wave; st < n_steps; st += WAVES) {
-        const int k = st * 32;
-        const bf16x8 xa = tok_ok ? ldg_stream((const bf16x8*)(xp + k)) : zero8();
+    const int rot = (int)((blockIdx.x * 16u) % (unsigned)n_steps) & ~1;
+    for (int s0 = 2 * wave; s0 < n_steps; s0 += BATCH * WAVES) {
+        bf16x8 xa[BATCH], wb[BATCH][NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8 wb = col_ok[nt] ? ldg((const bf16x8*)(wp[nt] + k)) : zero8();
-            acc[nt] = mfma16x16x32(xa, wb, acc[nt]);
+        for (int u = 0; u < BATCH; ++u) {
+            int sl = min(s0 + (u >> 1) * 2 * WAVES + (u & 1), n_steps - 1) + rot;
+            sl = sl >= n_steps ? sl - n_steps : sl;
+            const int k = sl * 32;
+            xa[u] = ldg((const bf16x8*)(xp + k));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) wb[u][nt] = ldg((const bf16x8*)(wp[nt] + k));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the batch in flight before the first wait
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            // slices past d_model contribute zero (branch-free: a branch here
+            // would drain the loads in flight)
+            const bf16x8 xv = s0 + (u >> 1) * 2 * WAVES + (u & 1) < n_steps ? xa[u] : zero8();
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x32(xv, wb[u][nt], acc[nt]);
         }
     }
     // C lane layout: tokens 4*kq + v, column l16 of each tile
