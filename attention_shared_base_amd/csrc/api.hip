@@ -104,8 +104,16 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     const long long wgs = units * p->n_split;
     if (wgs > 0x7ffffff0LL) return false;
     p->grid = (int)((wgs + 7) / 8 * 8);
+    // Persistent workgroups (a queue of the chunks that exist) once the grid
+    // would take several rounds of the GPU: the workgroup prologue and merge
+    // tail then stop being paid per launch round, and missing chunks of
+    // shorter contexts cost nothing.  Needs the workspace queue words and the
+    // per-context prefix sums in LDS.
+    const int per = env_int("LRA_DECODE_PERSISTENT", -1);
+    p->persistent = p->n_split > 1 && n_ctx <= 1024 && (per == 1 || (per != 0 && wgs > 4 * 256));
     const int dr2 = d.head_dim + d.rank + 2;
-    p->ws_counter_bytes = ((size_t)p->n_units * sizeof(int32_t) + 255) / 256 * 256;
+    // per-unit merge counters, then the queue head and the workgroups-done count
+    p->ws_counter_bytes = ((size_t)(p->n_units + 2) * sizeof(int32_t) + 255) / 256 * 256;
     p->ws_part_bytes = p->n_split > 1 ? (size_t)p->n_units * p->n_split * 16 * dr2 * sizeof(float) : 0;
     p->ws_total = p->n_split > 1 ? p->ws_counter_bytes + p->ws_part_bytes : 0;
     return true;

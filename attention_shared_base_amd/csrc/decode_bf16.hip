@@ -61,8 +61,13 @@ struct DecodeK {
     float* ws_part;
     int32_t n_ctx, n_pages, max_blocks, n_agents;
     int32_t h_q, h_kv, g, rpg, n_rg, n_split;
+    int32_t n_units;
+    int32_t persistent;  // 1: workgroups pull (context, row group, head, chunk) items from a queue
     float scale_log2;
 };
+
+// Persistent mode keeps the per-context item prefix sums in LDS.
+constexpr int MAX_CTX_PERSISTENT = 1024;
 
 // The rank-r score term uses the same v_mfma_f32_16x16x32_bf16 as the base
 // term it accumulates onto.  Every accumulator chain in this file stays on one
@@ -117,6 +122,8 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     __shared__ float sm_M[ROWS];
     __shared__ float sm_L[ROWS];
     __shared__ int sm_last;
+    __shared__ int sm_pref[MAX_CTX_PERSISTENT + 1];
+    __shared__ int sm_item;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -134,19 +141,8 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     asm volatile("" ::"s"(a.n_ctx), "s"(a.n_pages), "s"(a.max_blocks), "s"(a.n_agents), "s"(a.h_q),
                  "s"(a.h_kv), "s"(a.g), "s"(a.rpg), "s"(a.n_rg), "s"(a.n_split));
 
-    // XCD-aware placement: workgroup b runs on XCD b % 8; remap so that the
-    // KV heads of one (context, chunk) — which share its L_k/L_v pages — are
-    // consecutive on one XCD and hit the same L2.
-    const int nb = gridDim.x;
-    const int b = blockIdx.x;
-    const int bp = (b & 7) * (nb >> 3) + (b >> 3);
-    const int h = bp % a.h_kv;
-    int rest = bp / a.h_kv;
-    const int split = rest % a.n_split;
-    rest /= a.n_split;
-    const int rg = rest % a.n_rg;
-    const int ctx = rest / a.n_rg;
-    if (ctx >= a.n_ctx) return;
+    // ---- one work item: chunk `split` of row group rg of context ctx, KV head h
+    auto process = [&](const int ctx, const int rg, const int h, const int split) __attribute__((always_inline)) {
     const int unit = (ctx * a.n_rg + rg) * a.h_kv + h;
 
     // ---- every scalar load the step addresses depend on goes out at once,
@@ -500,6 +496,89 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     }
     __syncthreads();
     finalize_rows<D, R, SP>(a, sm_o[0], sm_L, n, cl, nrows, req0, h, bvc);
+    };
+
+    if (!a.persistent) {
+        // one item per workgroup.  XCD-aware placement: workgroup b runs on XCD
+        // b % 8; remap so that the KV heads of one (context, chunk) — which
+        // share its L_k/L_v pages — are consecutive on one XCD and hit the same L2.
+        const int nb = gridDim.x;
+        const int b = blockIdx.x;
+        const int bp = (b & 7) * (nb >> 3) + (b >> 3);
+        const int h = bp % a.h_kv;
+        int rest = bp / a.h_kv;
+        const int split = rest % a.n_split;
+        rest /= a.n_split;
+        const int rg = rest % a.n_rg;
+        const int ctx = rest / a.n_rg;
+        if (ctx < a.n_ctx) process(ctx, rg, h, split);
+        return;
+    }
+
+    // ---- persistent: one workgroup per CU pulls items from a queue in the
+    // workspace.  Items are only the chunks that exist (a context of length len
+    // has ceil(len / CHUNK) chunks per row group and KV head; an empty one has
+    // one item, which writes its zero rows), enumerated context by context,
+    // then chunk, row group, head.  The next item's index is requested when an
+    // item starts, so the queue's round trip overlaps the item.
+    int* queue = a.ws_count + a.n_units;  // [0] next item, [1] workgroups done
+    if (wave == 0) {
+        int run = 0;
+        for (int base = 0; base < a.n_ctx; base += 64) {
+            const int c = base + lane;
+            int v = 0;
+            if (c < a.n_ctx) {
+                const int len = min(a.ctx_len[c], a.max_blocks * PAGE);
+                v = (len > 0 ? (len + CHUNK - 1) / CHUNK : 1) * a.n_rg * a.h_kv;
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(v, off);
+                if (lane >= off) v += t;
+            }
+            if (c < a.n_ctx) sm_pref[c + 1] = run + v;
+            run += __shfl(v, 63);
+        }
+        if (lane == 0) {
+            sm_pref[0] = 0;
+            sm_item = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    const int total = sm_pref[a.n_ctx];
+    int item = sm_item;
+    while (item < total) {
+        int next = 0;
+        if (tid == 0) next = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int ctx = 0;
+        for (int base = 0; base < a.n_ctx; base += 64) {
+            const int c = base + lane;
+            const bool hit = c < a.n_ctx && sm_pref[c] <= item && item < sm_pref[c + 1];
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
+            if (m != 0) {
+                ctx = base + __builtin_ctzll(m);
+                break;
+            }
+        }
+        ctx = __builtin_amdgcn_readfirstlane(ctx);
+        const int local = item - sm_pref[ctx];
+        const int h = local % a.h_kv;
+        const int rest = local / a.h_kv;
+        process(ctx, rest % a.n_rg, h, rest / a.n_rg);
+        __syncthreads();  // every thread is done with this item's LDS
+        if (tid == 0) sm_item = next;
+        __syncthreads();
+        item = sm_item;
+    }
+    // the last workgroup out resets the queue (no grab can follow: every
+    // workgroup's final grab returned before it got here)
+    if (tid == 0) {
+        const int done = __hip_atomic_fetch_add(queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (int)gridDim.x - 1) {
+            __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // Log-sum-exp merge of the chunk partials of one work unit into o[row][0..DR)
@@ -616,8 +695,21 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.rpg = p.rpg;
     k.n_rg = p.n_rg;
     k.n_split = p.n_split;
+    k.n_units = p.n_units;
+    k.persistent = p.persistent;
     k.scale_log2 = a.scale * LRA_LOG2E;
-    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W>), dim3(p.grid), dim3(64 * W), 0, s, k);
+    int grid = p.grid;
+    if (p.persistent) {
+        // one workgroup per CU of the current device
+        int dev = 0, n_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0) {
+            lra::set_error("decode: cannot query the device's compute units");
+            return LRA_ERR_HIP;
+        }
+        grid = min(n_cu, p.grid);
+    }
+    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W>), dim3(grid), dim3(64 * W), 0, s, k);
     return lra::check_launch("lra_decode_bf16_kernel");
 }
 

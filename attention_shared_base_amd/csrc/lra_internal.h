@@ -26,7 +26,8 @@ struct DecodePlan {
     int n_units;    // n_ctx * n_rg * H_kv
     int chunk;      // tokens per workgroup
     int n_split;    // chunks per unit at max_ctx_len
-    int grid;       // workgroups launched (multiple of 8)
+    int persistent; // 1: one workgroup per CU pulls items from a queue in the workspace
+    int grid;       // workgroups launched (multiple of 8; non-persistent mode)
     size_t ws_counter_bytes;
     size_t ws_part_bytes;
     size_t ws_total;

@@ -116,8 +116,11 @@ const char* lra_last_error(void);
  *                  lra_attn_decode_workspace_size(...) bytes (0 when every
  *                  context fits one workgroup's chunk of tokens; NULL is then
  *                  accepted).  It holds per-chunk partial rows
- *                  (m, l, O_base[d], O_lr[r]) and one counter per work unit;
- *                  its size grows with the number of chunks, never with
+ *                  (m, l, O_base[d], O_lr[r]), one counter per work unit and
+ *                  the two words of the chunk queue that persistent
+ *                  workgroups (one per compute unit, chosen when the chunks
+ *                  outnumber the GPU several times over) pull from; its size
+ *                  grows with the number of chunks, never with
  *                  tokens x head_dim.  It must be zero-filled before its first
  *                  use; every completed call leaves the counters at zero again,
  *                  so later calls on the same stream can reuse it without

@@ -144,3 +144,35 @@ def test_cfg4_paged_decode_sampled():
     lens = case.ctx_len
     sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 18})
     _check(case, requests=sample, label=f"cfg4 sampled requests {sample}")
+
+
+def test_decode_persistent_queue():
+    """Persistent workgroups pulling chunks from the workspace queue give the same rows as
+    one workgroup per chunk, twice in a row on one workspace (the queue words return to 0)."""
+    reqs = [(c, c % 3) for c in range(5) for _ in range(2)] + [(5, 1)]
+    case = w.make_decode(31, dtype="bf16", ctx_lens=[3000, 1, 9000, 0, 4500, 700], reqs=reqs,
+                         n_agents=3, h_q=32, h_kv=8, d=128, r=32, shuffle=True, name="persistent")
+    import torch
+    import attention_shared_base_amd as lra
+    d = DecodeDev(case)
+    live = [i for i, (c, _) in enumerate(reqs) if c != 3]  # context 3 is empty
+    ref = oracle_decode(case, requests=live)
+    outs = []
+    try:
+        os.environ["LRA_DECODE_CHUNK"] = "512"
+        n_ws = lra.decode_workspace_size(n_q_heads=32, n_kv_heads=8, head_dim=128, rank=32, dtype=1,
+                                         n_req=len(reqs), n_ctx=6, max_req_per_ctx=d.max_req_per_ctx,
+                                         max_ctx_len=d.max_ctx_len)
+        ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
+        for per in ("0", "1", "1"):
+            os.environ["LRA_DECODE_PERSISTENT"] = per
+            outs.append(host(d.run(workspace=ws)))
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0  # counters and queue back at zero
+    finally:
+        os.environ.pop("LRA_DECODE_CHUNK", None)
+        os.environ.pop("LRA_DECODE_PERSISTENT", None)
+    for o in outs:
+        assert_parity(o[live], ref[live], "bf16", "persistent")
+        assert np.all(o[[6, 7]] == 0.0)  # requests on the empty context
+    assert np.array_equal(outs[1], outs[2])
+    assert np.max(np.abs(outs[1] - outs[0])) < 4e-3
