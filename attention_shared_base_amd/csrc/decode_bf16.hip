@@ -142,8 +142,16 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                  "s"(a.h_kv), "s"(a.g), "s"(a.rpg), "s"(a.n_rg), "s"(a.n_split));
 
     // ---- one work item: chunk `split` of row group rg of context ctx, KV head h
-    auto process = [&](const int ctx, const int rg, const int h, const int split) __attribute__((always_inline)) {
+    // `queue`: persistent mode's queue (NULL otherwise); the next item's index is
+    // requested into *next once this item's streaming is done, so the round trip
+    // overlaps the merge tail without reserving work early
+    auto process = [&](const int ctx, const int rg, const int h, const int split, int* queue,
+                       int* next) __attribute__((always_inline)) {
     const int unit = (ctx * a.n_rg + rg) * a.h_kv + h;
+    auto grab_next = [&]() {
+        if (queue != nullptr && tid == 0)
+            *next = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
 
     // ---- every scalar load the step addresses depend on goes out at once,
     // before any branch on their values: request range and length of the
@@ -167,7 +175,10 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 
     const int req0 = rs0 + rg * a.rpg;
     const int nreq = min(a.rpg, rs1 - req0);
-    if (nreq <= 0) return;
+    if (nreq <= 0) {
+        grab_next();
+        return;
+    }
     const int g = a.g;
     const int nrows = nreq * g;
     const int len = min(len_raw, a.max_blocks * PAGE);
@@ -179,10 +190,14 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                 a.out[((size_t)(req0 + n / g) * a.h_q + h * g + n % g) * D + c] = (bf16)0.0f;
             }
         }
+        grab_next();
         return;
     }
     const int n_active = (len + CHUNK - 1) / CHUNK;
-    if (split >= n_active) return;
+    if (split >= n_active) {
+        grab_next();
+        return;
+    }
     const int kend = min(len, kbeg + CHUNK);
 
     // ---- page ids of this wavefront's steps.  Pages past the chunk end take
@@ -398,6 +413,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    grab_next();
 
     // ---- merge the four wavefronts through LDS
 #pragma unroll
@@ -511,7 +527,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         rest /= a.n_split;
         const int rg = rest % a.n_rg;
         const int ctx = rest / a.n_rg;
-        if (ctx < a.n_ctx) process(ctx, rg, h, split);
+        if (ctx < a.n_ctx) process(ctx, rg, h, split, nullptr, nullptr);
         return;
     }
 
@@ -520,7 +536,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     // has ceil(len / CHUNK) chunks per row group and KV head; an empty one has
     // one item, which writes its zero rows), enumerated context by context,
     // then chunk, row group, head.  The next item's index is requested when an
-    // item starts, so the queue's round trip overlaps the item.
+    // item's streaming ends, so the queue's round trip overlaps its merge tail.
     int* queue = a.ws_count + a.n_units;  // [0] next item, [1] workgroups done
     if (wave == 0) {
         int run = 0;
@@ -548,8 +564,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     const int total = sm_pref[a.n_ctx];
     int item = sm_item;
     while (item < total) {
-        int next = 0;
-        if (tid == 0) next = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int next = total;
         int ctx = 0;
         for (int base = 0; base < a.n_ctx; base += 64) {
             const int c = base + lane;
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         const int local = item - sm_pref[ctx];
         const int h = local % a.h_kv;
         const int rest = local / a.h_kv;
-        process(ctx, rest % a.n_rg, h, rest / a.n_rg);
+        process(ctx, rest % a.n_rg, h, rest / a.n_rg, queue, &next);
         __syncthreads();  // every thread is done with this item's LDS
         if (tid == 0) sm_item = next;
         __syncthreads();
