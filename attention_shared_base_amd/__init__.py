@@ -67,7 +67,7 @@ def load():
     lib.lra_attn_decode.restype = I32
     lib.lra_attn_decode.argtypes = [
         ctypes.POINTER(Dims), P, I32, P, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, I32,
-        P, P, I32, P, P, ctypes.c_size_t, P]
+        P, P, I32, P, P, P, P, ctypes.c_size_t, P]
     lib.lra_attn_prefill.restype = I32
     lib.lra_attn_prefill.argtypes = [
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, P, P]
@@ -132,14 +132,16 @@ def decode_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, dtype, n_req
 
 
 def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table, ctx_len,
-           b_k, b_v, *, max_req_per_ctx, max_ctx_len, out=None, workspace=None,
-           softmax_scale=0.0, stream=None):
+           b_k, b_v, *, max_req_per_ctx, max_ctx_len, rope_cos=None, rope_sin=None, out=None,
+           workspace=None, softmax_scale=0.0, stream=None):
     """Paged decode (``lra_attn_decode``).  Layouts as in include/lra_attn.h:
 
     q [n_req, H_q, d]; k_pool [n_pages, H_kv, d/8, 16, 8]; v_pool [n_pages, H_kv, d, 16];
     lk_pool [n_pages, 16, r]; lv_pool [n_pages, r, 16]; block_table [n_ctx, max_blocks];
-    ctx_len [n_ctx]; ctx_req_start [n_ctx+1]; req_agent [n_req]; b_k, b_v [n_agents, r, H_kv*d].
-    ``workspace`` (uint8, zero-filled before first use) is allocated when not given.
+    ctx_len [n_ctx]; ctx_req_start [n_ctx+1]; req_agent [n_req]; b_k, b_v [n_agents, r, H_kv*d];
+    optional RoPE tables rope_cos, rope_sin [>= max(max_ctx_len, 1), d/2] fp32 rotate the
+    adapter key term.  ``workspace`` (uint8, zero-filled before first use) is allocated
+    when not given.
     """
     import torch
     lib = load()
@@ -165,6 +167,12 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
           "b_k/b_v must be [n_agents, r, H_kv*d]")
     _need(ctx_req_start.shape == (n_ctx + 1,) and ctx_len.shape == (n_ctx,)
           and req_agent.shape == (n_req,), "index array shapes")
+    _need((rope_cos is None) == (rope_sin is None), "rope_cos and rope_sin go together")
+    if rope_cos is not None:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            _contig(name, t)
+            _need(t.dtype == torch.float32 and t.shape[0] >= max(max_ctx_len, 1)
+                  and t.shape[1] == d // 2, f"{name} must be fp32 [>=max_ctx_len, d/2]")
     if out is None:
         out = torch.empty_like(q)
     _contig("out", out)
@@ -178,7 +186,7 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
         ctypes.byref(dims), _ptr(q), n_req, _ptr(ctx_req_start), n_ctx, max_req_per_ctx,
         _ptr(req_agent), _ptr(k_pool), _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, page,
         _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
-        _ptr(out), _ptr(workspace), wsz, _stream(q, stream)))
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(out), _ptr(workspace), wsz, _stream(q, stream)))
     return out
 
 

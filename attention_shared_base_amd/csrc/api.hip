@@ -155,7 +155,8 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
                            const void* lk_pool, const void* lv_pool, int32_t n_pages,
                            int32_t page_size, const int32_t* block_table, int32_t max_blocks,
                            const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
-                           const void* b_v, int32_t n_agents, void* out, void* workspace,
+                           const void* b_v, int32_t n_agents, const float* rope_cos,
+                           const float* rope_sin, void* out, void* workspace,
                            size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
@@ -186,6 +187,10 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
     REQUIRE_PTR(b_k);
     REQUIRE_PTR(b_v);
     REQUIRE_PTR(out);
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return fail(LRA_ERR_NULL_PTR, "rope_cos and rope_sin must be both NULL or both set");
+    if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin)))
+        return fail(LRA_ERR_MISALIGNED, "rope tables are not 16-byte aligned");
 
     lra::DecodeArgs a;
     a.q = q;
@@ -199,6 +204,8 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
     a.ctx_len = ctx_len;
     a.b_k = b_k;
     a.b_v = b_v;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
     a.out = out;
     a.workspace = workspace;
     a.n_req = n_req;

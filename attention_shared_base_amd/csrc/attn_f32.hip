@@ -5,7 +5,7 @@
 // the bf16 kernels (LRAgent, arXiv 2602.01053v2, §3 and App. B): scores from
 // q . k_base_j plus the pre-projected query against the shared rank-r row
 // l_k_j (or, with RoPE, against the rebuilt key k_base_j + rot(l_k_j B_k^(h)),
-// App. D.1), online softmax over 64-token chunks, value accumulation at head
+// App. D.1, in decode and prefill alike), online softmax over 64-token chunks, value accumulation at head
 // dimension for V_base and at rank r for L_v, and one B_v post-multiplication.
 #include "lra_common.h"
 #include "lra_internal.h"
@@ -168,7 +168,8 @@ __global__ __launch_bounds__(64) void lra_decode_f32_kernel(F32K a) {
     }
     int agent = min(max(a.req_agent[req], 0), a.n_agents - 1);
     Paged acc{&a, a.block_table + (size_t)ctx * a.max_blocks, h};
-    row_attend(a, acc, a.q + ((size_t)req * a.h_q + hq) * a.d, agent, h, len - 1, orow, false);
+    row_attend(a, acc, a.q + ((size_t)req * a.h_q + hq) * a.d, agent, h, len - 1, orow,
+               a.rope_cos != nullptr);
 }
 
 // grid: n_req * q_len * H_q blocks of 64 threads
@@ -198,6 +199,8 @@ F32K common(const lra::DecodeArgs& d) {
     k.ctx_len = d.ctx_len;
     k.b_k = (const float*)d.b_k;
     k.b_v = (const float*)d.b_v;
+    k.rope_cos = d.rope_cos;
+    k.rope_sin = d.rope_sin;
     k.out = (float*)d.out;
     k.n_req = d.n_req;
     k.n_ctx = d.n_ctx;

@@ -33,8 +33,18 @@
 // registers.  The page layouts of the boundary are chosen so every operand is
 // one direct, coalesced global load: K pages [d/8][16][8], V pages dim-major
 // [d][16], L_k [16][r], L_v rank-major [r][16].  No LDS in the streaming loop.
-#include <stdlib.h>
-
+//
+// RoPE on the adapter key (LRAgent App. D.1).  When the model rotates keys,
+// the adapter term must be rotated with its key's position before it meets
+// the query, s_j = q . (k_base_j + rot_j(l_k_j B_k^(h))), so the key side
+// cannot stay at rank r: per page and per request of the group the kernel
+// rebuilds dK^T = B_k^(h)T L_k^T on the matrix cores (lane = token, 4 dims per
+// 16-dim tile), rotates the pairs (i, i + d/2) lane-locally with the page's
+// cos/sin rows, rounds the rotated term to bf16 and adds its product with the
+// query rows of that request to the base scores.  The rebuilt key never
+// leaves registers; the value side is unchanged.  B_k^(h) of every request
+// in the group is staged once per work item in LDS, already in the operand
+// layout.
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -64,6 +74,9 @@ struct DecodeK {
     int32_t n_units;
     int32_t persistent;  // 1: workgroups pull (context, row group, head, chunk) items from a queue
     float scale_log2;
+    const float* rope_cos;  // RoPE: [rope_rows, D/2] tables of the keys' positions
+    const float* rope_sin;
+    int32_t rope_rows;
 };
 
 // Persistent mode keeps the per-context item prefix sums in LDS.
@@ -104,10 +117,17 @@ struct Step {
     bf16x4 lv[2][NRT];
 };
 
+// RoPE: cos, sin of one step's keys (page t, token n16), dims 16*ht + 4*q4 .. +3
+template <int D>
+struct StepRope {
+    f32x4 cs[2][D / 32][2];
+};
+
 // WAVES wavefronts per workgroup; SPW = 32-token steps per wavefront; a
 // workgroup covers WAVES * SPW * 32 tokens.  DEPTH = step buffers per
-// wavefront (DEPTH - 1 steps of loads in flight).
-template <int D, int R, int SPW, int DEPTH, int WAVES>
+// wavefront (DEPTH - 1 steps of loads in flight).  ROPE: rotate the adapter
+// key term (rebuilt per request) instead of the rank-r score term.
+template <int D, int R, int SPW, int DEPTH, int WAVES, bool ROPE>
 __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) {
     constexpr int NJ = Step<D, R>::NJ;
     constexpr int NDT = Step<D, R>::NDT;
@@ -116,7 +136,17 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     constexpr int SP = DR + 1;  // LDS row pitch (odd: no bank aliasing across rows)
     constexpr int CHUNK = WAVES * SPW * KEYS_PER_STEP;
 
-    __shared__ float sm_o[WAVES][ROWS][SP];
+    // RoPE: B_k^(h)T operands of up to ROWS requests (one per row when g = 1),
+    // [request][dim tile][lane] x BKW bytes.  They are needed only while
+    // streaming and the wavefront merge buffer only after it, so the two share
+    // one LDS block (a barrier separates the uses).
+    constexpr int BKW = R == 32 ? 16 : 8;
+    constexpr int SMO_BYTES = WAVES * ROWS * SP * 4;
+    constexpr int BK_BYTES = ROPE ? ROWS * NDT * 64 * BKW : 0;
+    __shared__ __attribute__((aligned(16))) char sm_raw[SMO_BYTES > BK_BYTES ? SMO_BYTES : BK_BYTES];
+    float(*const sm_o)[ROWS][SP] = reinterpret_cast<float(*)[ROWS][SP]>(sm_raw);
+    char* const sm_bk = sm_raw;
+    __shared__ int sm_pid[ROPE ? CHUNK / PAGE : 1];
     __shared__ float sm_m[WAVES][ROWS];
     __shared__ float sm_l[WAVES][ROWS];
     __shared__ float sm_M[ROWS];
@@ -163,15 +193,17 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     const int rs1 = a.ctx_req_start[ctx + 1];
     const int len_raw = a.ctx_len[ctx];
     const int first_raw = bt[min(kbeg >> 4, a.max_blocks - 1)];
-    int praw[SPW][2];
+    // (RoPE: the first step only; its stream reads later steps' ids as it goes)
+    constexpr int NPRE = ROPE ? 1 : SPW;
+    int praw[NPRE][2];
 #pragma unroll
-    for (int i = 0; i < SPW; ++i)
+    for (int i = 0; i < NPRE; ++i)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
             praw[i][t] = bt[min((kbeg >> 4) + 2 * (wave + WAVES * i) + t, a.max_blocks - 1)];
     asm volatile("" ::"s"(rs0), "s"(rs1), "s"(len_raw), "s"(first_raw));
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) asm volatile("" ::"s"(praw[i][0]), "s"(praw[i][1]));
+    for (int i = 0; i < NPRE; ++i) asm volatile("" ::"s"(praw[i][0]), "s"(praw[i][1]));
 
     const int req0 = rs0 + rg * a.rpg;
     const int nreq = min(a.rpg, rs1 - req0);
@@ -204,27 +236,37 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     // the chunk's first page: those steps load cached data and are never
     // computed, so the loads can stay unconditional.
     const int last_pg = (kend - 1) >> 4;
-    int pid[SPW][2];
+    auto page_of = [&](int i, int t, int raw) {
+        const int pg = (kbeg >> 4) + 2 * (wave + WAVES * i) + t;
+        return min(max(pg <= last_pg ? raw : first_raw, 0), a.n_pages - 1);
+    };
+    int pid[NPRE][2];
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int pg = (kbeg >> 4) + 2 * (wave + WAVES * i);
+    for (int i = 0; i < NPRE; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-            pid[i][t] = min(max(pg + t <= last_pg ? praw[i][t] : first_raw, 0), a.n_pages - 1);
+        for (int t = 0; t < 2; ++t) pid[i][t] = page_of(i, t, praw[i][t]);
+    // RoPE stream: the chunk's raw page ids are staged in LDS with the B_k
+    // operands (one vector load per thread) and read back per step
+    if constexpr (ROPE) {
+        if (tid < CHUNK / PAGE) sm_pid[tid] = bt[min((kbeg >> 4) + tid, a.max_blocks - 1)];
     }
+    auto page_now = [&](int i, int t) {
+        const int raw = __builtin_amdgcn_readfirstlane(sm_pid[2 * (wave + WAVES * i) + t]);
+        return page_of(i, t, raw);
+    };
 
     const size_t kv_page = (size_t)a.h_kv * D * PAGE;  // elements per page (all heads)
     const bf16* kbase = a.k_pool + (size_t)h * D * PAGE;
     const bf16* vbase = a.v_pool + (size_t)h * D * PAGE;
 
     // Loads of one step: no data-dependent branches; dead slots are masked later.
-    auto load = [&](Step<D, R>& T, int i) {
+    auto load = [&](Step<D, R>& T, const int (&pids)[2]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const bf16* kp = kbase + (size_t)pid[i][t] * kv_page;
-            const bf16* vp = vbase + (size_t)pid[i][t] * kv_page;
-            const bf16* lkp = a.lk_pool + (size_t)pid[i][t] * PAGE * R;
-            const bf16* lvp = a.lv_pool + (size_t)pid[i][t] * PAGE * R;
+            const bf16* kp = kbase + (size_t)pids[t] * kv_page;
+            const bf16* vp = vbase + (size_t)pids[t] * kv_page;
+            const bf16* lkp = a.lk_pool + (size_t)pids[t] * PAGE * R;
+            const bf16* lvp = a.lv_pool + (size_t)pids[t] * PAGE * R;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 T.k[t][j] = ldg_stream((const bf16x8*)(kp + ((4 * j + q4) * PAGE + n16) * 8));
@@ -247,6 +289,30 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
             }
         }
     };
+    // RoPE tables of step i's keys: the key's position in its context is its
+    // token index; tokens past the chunk end read the last valid row (unused).
+    // One buffer: step i+1's rows are requested when step i is done with its own.
+    // Rows are read through a buffer range starting at the page's first key, so
+    // the per-step address stays scalar; rows past the table read as zero.
+    const uint32_t rope_voff = (uint32_t)(n16 * (D / 2) + 4 * q4) * 4;
+    auto load_rope = [&](StepRope<D>& C, int i) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row0 = kbeg + (wave + WAVES * i) * KEYS_PER_STEP + PAGE * t;
+            const uint32_t bytes = (uint32_t)max(a.rope_rows - row0, 0) * (D / 2) * 4;
+            const __amdgpu_buffer_rsrc_t rc =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a.rope_cos + (size_t)row0 * (D / 2)), (short)0, bytes, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a.rope_sin + (size_t)row0 * (D / 2)), (short)0, bytes, 0x00020000);
+#pragma unroll
+            for (int ht = 0; ht < D / 32; ++ht) {
+                C.cs[t][ht][0] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, rope_voff + 64 * ht, 0, 0));
+                C.cs[t][ht][1] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, rope_voff + 64 * ht, 0, 0));
+            }
+        }
+    };
 
     // agent ids of the group's first four requests: requested before the step
     // loads, so that waiting for them does not wait for those
@@ -258,7 +324,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     Step<D, R> buf[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH - 1; ++i)
-        if (i < SPW) load(buf[i], i);
+        if (i < NPRE) load(buf[i], pid[i]);
+    StepRope<D> rope_buf;
+    if constexpr (ROPE) load_rope(rope_buf, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- query operand (B of the score MFMA): lane holds dims 32j+8*q4.. of row
@@ -266,11 +334,20 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     // just before use): a branch here would drain the step loads in flight.
     const bool row_ok = n16 < nrows;
     bf16x8 qf[NJ];
+    // RoPE: the same query rows with the dims of k-step j in the order of the
+    // rebuilt key operand: slots 0-3 = dims 32j + 4*q4 .., slots 4-7 = 32j + 16 + 4*q4 ..
+    bf16x8 qfp[NJ];
     {
         const int qr = row_ok ? n16 : 0;
-        const bf16* qp = a.q + ((size_t)(req0 + qr / g) * a.h_q + h * g + qr % g) * D + 8 * q4;
+        const bf16* qp = a.q + ((size_t)(req0 + qr / g) * a.h_q + h * g + qr % g) * D;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) qf[j] = ldg((const bf16x8*)(qp + 32 * j));
+        for (int j = 0; j < NJ; ++j) qf[j] = ldg((const bf16x8*)(qp + 32 * j + 8 * q4));
+        if constexpr (ROPE) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                qfp[j] = cat4(ldg((const bf16x4*)(qp + 32 * j + 4 * q4)),
+                              ldg((const bf16x4*)(qp + 32 * j + 16 + 4 * q4)));
+        }
     }
 
     // ---- pre-projection qB = q B_k^(h)T, one MFMA tile per request of the group.
@@ -282,6 +359,53 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) qbacc[rt] = zf4();
     const size_t bcols = (size_t)a.h_kv * D;
+    if constexpr (ROPE) {
+        // ---- RoPE: stage B_k^(h)T of every request of the group in LDS as the A
+        // operand of dK^T = B_k^(h)T L_k^T: entry (request u, dim tile, lane l)
+        // holds dim 16*tile + l%16, ranks 4*(l/16) + v in slots 0-3 and
+        // 16 + 4*(l/16) + v in slots 4-7 (rank 32 only) — the rank order of the
+        // L_k operand.  Each thread fetches 16-byte pieces of B_k rows (8 dims of
+        // one rank) for four requests at a time, then scatters them.
+        constexpr int PIECES = R * D / 8;  // per request
+        constexpr int PPT = (PIECES + 64 * WAVES - 1) / (64 * WAVES);
+        for (int s0 = 0; s0 < nreq; s0 += 4) {
+            int agent[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) agent[u] = s0 == 0 ? agent0[u] : a.req_agent[req0 + min(s0 + u, nreq - 1)];
+            asm volatile("" ::"s"(agent[0]), "s"(agent[1]), "s"(agent[2]), "s"(agent[3]));
+            bf16x8 raw[4][PPT];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ag = min(max(agent[u], 0), a.n_agents - 1);
+#pragma unroll
+                for (int k = 0; k < PPT; ++k) {
+                    const int pc = min(tid + 64 * WAVES * k, PIECES - 1);
+                    const int rank = pc / (D / 8), c0 = 8 * (pc % (D / 8));
+                    raw[u][k] = ldg((const bf16x8*)(a.b_k + ((size_t)ag * R + rank) * bcols + (size_t)h * D + c0));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // every B_k load issued before the first wait
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int k = 0; k < PPT; ++k) {
+                    const int pc = tid + 64 * WAVES * k;
+                    if (s0 + u < nreq && pc < PIECES) {
+                        const int rank = pc / (D / 8), c0 = 8 * (pc % (D / 8));
+                        const int slot = (rank & 3) + (rank >= 16 ? 4 : 0);
+                        const int grp = (rank & 15) >> 2;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int c = c0 + e;
+                            const int l = (c & 15) + 16 * grp;
+                            *(bf16*)(sm_bk + (((s0 + u) * NDT + (c >> 4)) * 64 + l) * BKW + 2 * slot) = raw[u][k][e];
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    } else {
     for (int s0 = 0; s0 < nreq; s0 += 4) {
         int agent[4];
 #pragma unroll
@@ -315,6 +439,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                 if (n16 / g == s0 + u) qbacc[rt] = c;
             }
     }
+    }
     bf16x8 qb;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -332,6 +457,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     for (int rt = 0; rt < NRT; ++rt) acc_lr[rt] = zf4();
     const float sl2 = a.scale_log2;
 
+    const int my_req = n16 / g;  // request (within the group) of this lane's row
     auto compute = [&](Step<D, R>& T, int key0) {
         f32x4 s[2];
 #pragma unroll
@@ -339,7 +465,50 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
             s[t] = zf4();
 #pragma unroll
             for (int j = 0; j < NJ; ++j) s[t] = mfma16x16x32(T.k[t][j], qf[j], s[t]);
-            s[t] = mfma16x16x32(T.lk[t], qb, s[t]);
+            if constexpr (!ROPE) s[t] = mfma16x16x32(T.lk[t], qb, s[t]);
+        }
+        if constexpr (ROPE) {
+            // adapter key term of each request: dK^T = B_k^(h)T L_k^T (lane =
+            // token n16, dims 16*tile + 4*q4 + v), rotated by the token's
+            // position, rounded to bf16, contracted with the query rows (all
+            // rows computed, only the request's rows kept)
+            for (int u = 0; u < nreq; ++u) {
+                const char* bkp = sm_bk + (u * NDT * 64 + lane) * BKW;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 dk[NDT];
+#pragma unroll
+                    for (int tile = 0; tile < NDT; ++tile) {
+                        bf16x8 bop;
+                        if constexpr (R == 32) {
+                            bop = *(const bf16x8*)(bkp + tile * 64 * BKW);
+                        } else {
+                            bop = cat4(*(const bf16x4*)(bkp + tile * 64 * BKW), zero4());
+                            if (R == 8 && q4 >= 2) bop = zero8();
+                        }
+                        dk[tile] = mfma16x16x32(bop, T.lk[t], zf4());
+                    }
+#pragma unroll
+                    for (int ht = 0; ht < NDT / 2; ++ht) {
+                        const f32x4 c = rope_buf.cs[t][ht][0], sn = rope_buf.cs[t][ht][1];
+                        const f32x4 x1 = dk[ht], x2 = dk[ht + NDT / 2];
+                        dk[ht] = x1 * c - x2 * sn;
+                        dk[ht + NDT / 2] = x2 * c + x1 * sn;
+                    }
+                    f32x4 acc_u = s[t];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        bf16x8 op;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            op[v] = (bf16)dk[2 * j][v];
+                            op[4 + v] = (bf16)dk[2 * j + 1][v];
+                        }
+                        acc_u = mfma16x16x32(op, qfp[j], acc_u);
+                    }
+                    if (my_req == u) s[t] = acc_u;
+                }
+            }
         }
         // Tokens at or past the chunk end: score -inf, and their values zeroed
         // (unused page slots may hold anything, even NaN bits, and 0 * NaN is
@@ -405,17 +574,39 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     // No branches in this loop and a scheduling barrier after each batch of
     // loads: the compiler may neither sink the loads towards their use nor
     // merge control flow (either makes it drain every load in flight).
+    if constexpr (!ROPE) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        if (i + DEPTH - 1 < SPW) load(buf[(i + DEPTH - 1) % DEPTH], i + DEPTH - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(buf[i % DEPTH], kbeg + (wave + WAVES * i) * KEYS_PER_STEP);
+        for (int i = 0; i < SPW; ++i) {
+            if (i + DEPTH - 1 < SPW) load(buf[(i + DEPTH - 1) % DEPTH], pid[i + DEPTH - 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(buf[i % DEPTH], kbeg + (wave + WAVES * i) * KEYS_PER_STEP);
+        }
+    } else {
+        // RoPE: each step carries the per-request key rebuild, so the stream is a
+        // runtime loop over step pairs (bounded registers and code size).  Loads
+        // stay unconditional: past the last step they repeat it (never used).
+        static_assert(DEPTH == 2 && SPW % 2 == 0, "RoPE stream: two step buffers, even step count");
+        auto rstep = [&](int i, Step<D, R>& cur, Step<D, R>& nxt) {
+            const int in = min(i + 1, SPW - 1);
+            const int pn[2] = {page_now(in, 0), page_now(in, 1)};
+            load(nxt, pn);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cur, kbeg + (wave + WAVES * i) * KEYS_PER_STEP);
+            load_rope(rope_buf, in);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+#pragma unroll 1
+        for (int i = 0; i < SPW; i += 2) {
+            rstep(i, buf[0], buf[1]);
+            rstep(i + 1, buf[1], buf[0]);
+        }
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     grab_next();
 
     // ---- merge the four wavefronts through LDS
+    if constexpr (ROPE) __syncthreads();  // every B_k operand read before sm_o (same LDS) is written
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -683,8 +874,10 @@ __device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)
     *(typename BvCols<D, R>::vec*)(a.out + ((size_t)req * a.h_q + h * g + n % g) * D + c0) = res;
 }
 
-template <int D, int R, int SPW, int DEPTH, int W>
+template <int D, int R, int SPW, bool ROPE>
 lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
+    constexpr int DEPTH = 2;  // one step of loads in flight per wavefront
+    constexpr int W = 4;      // wavefronts per workgroup
     DecodeK k;
     k.q = (const bf16*)a.q;
     k.ctx_req_start = a.ctx_req_start;
@@ -713,6 +906,9 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.n_units = p.n_units;
     k.persistent = p.persistent;
     k.scale_log2 = a.scale * LRA_LOG2E;
+    k.rope_cos = a.rope_cos;
+    k.rope_sin = a.rope_sin;
+    k.rope_rows = a.max_ctx_len;
     int grid = p.grid;
     if (p.persistent) {
         // one workgroup per CU of the current device
@@ -724,46 +920,23 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
         }
         grid = min(n_cu, p.grid);
     }
-    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W>), dim3(grid), dim3(64 * W), 0, s, k);
+    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W, ROPE>), dim3(grid), dim3(64 * W), 0, s, k);
     return lra::check_launch("lra_decode_bf16_kernel");
 }
 
-template <int D, int R, int DEPTH, int W>
-lra_status launch_depth(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
-    // chunk = W * SPW * 32 tokens
-    constexpr int S256 = 256 / (32 * W);
+template <int D, int R, bool ROPE>
+lra_status launch_dr(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
+    // chunk = 4 wavefronts x SPW steps x 32 tokens
     switch (p.chunk) {
-        case 256:
-            if constexpr (S256 >= 1) return launch_t<D, R, S256, (DEPTH < S256 ? DEPTH : S256 < 2 ? 2 : DEPTH), W>(a, p, s);
-            break;
-        case 512: return launch_t<D, R, 512 / (32 * W), DEPTH, W>(a, p, s);
-        case 1024: return launch_t<D, R, 1024 / (32 * W), DEPTH, W>(a, p, s);
-        case 2048: return launch_t<D, R, 2048 / (32 * W), DEPTH, W>(a, p, s);
-        case 4096: return launch_t<D, R, 4096 / (32 * W), DEPTH, W>(a, p, s);
+        case 256: return launch_t<D, R, 2, ROPE>(a, p, s);
+        case 512: return launch_t<D, R, 4, ROPE>(a, p, s);
+        case 1024: return launch_t<D, R, 8, ROPE>(a, p, s);
+        case 2048: return launch_t<D, R, 16, ROPE>(a, p, s);
+        case 4096: return launch_t<D, R, 32, ROPE>(a, p, s);
         default: break;
     }
     lra::set_error("decode: unsupported chunk %d", p.chunk);
     return LRA_ERR_UNSUPPORTED;
-}
-
-template <int D, int R>
-lra_status launch_dr(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
-    static const int depth = [] {
-        const char* e = getenv("LRA_DECODE_DEPTH");
-        const int v = e ? atoi(e) : 2;
-        return v == 2 || v == 3 ? v : 2;
-    }();
-    static const int waves = [] {
-        const char* e = getenv("LRA_DECODE_WAVES");
-        const int v = e ? atoi(e) : 4;
-        return v == 8 ? 8 : 4;
-    }();
-    if (waves == 8) {
-        if (depth == 3) return launch_depth<D, R, 3, 8>(a, p, s);
-        return launch_depth<D, R, 2, 8>(a, p, s);
-    }
-    if (depth == 3) return launch_depth<D, R, 3, 4>(a, p, s);
-    return launch_depth<D, R, 2, 4>(a, p, s);
 }
 
 }  // namespace
@@ -772,8 +945,9 @@ namespace lra {
 
 lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
     const int d = a.head_dim, r = a.rank;
+    const bool rope = a.rope_cos != nullptr;
 #define LRA_CASE(D_, R_) \
-    if (d == D_ && r == R_) return launch_dr<D_, R_>(a, p, s);
+    if (d == D_ && r == R_) return rope ? launch_dr<D_, R_, true>(a, p, s) : launch_dr<D_, R_, false>(a, p, s);
     LRA_CASE(128, 16)
     LRA_CASE(128, 32)
     LRA_CASE(128, 8)

@@ -75,6 +75,20 @@ LRA_DEV bf16x4 and_mask(bf16x4 x, uint32_t lo, uint32_t hi) {
 template <typename T>
 LRA_DEV T ldg(const T* p) { return *p; }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): stride 0, reads past the end
+// return 0.
+LRA_DEV u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    u32x4 r;
+    r[0] = (uint32_t)p;
+    r[1] = (uint32_t)(p >> 32) & 0xffffu;
+    r[2] = bytes;
+    r[3] = 0x00020000u;
+    return r;
+}
+
 // Streaming (read-once) load: bypasses reuse in the caches it can.
 template <typename T>
 LRA_DEV T ldg_stream(const T* p) { return __builtin_nontemporal_load(p); }

@@ -48,6 +48,8 @@ struct DecodeArgs {
     const int32_t* ctx_len;
     const void* b_k;
     const void* b_v;
+    const float* rope_cos;  // NULL: no RoPE on the adapter key; else [max_ctx_len, d/2]
+    const float* rope_sin;
     void* out;
     void* workspace;
     int32_t n_req, n_ctx, n_pages, max_blocks, max_ctx_len, n_agents;

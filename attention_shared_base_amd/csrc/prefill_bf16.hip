@@ -82,20 +82,6 @@ LRA_DEV bf16x4 lds_read_tr(const char* p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over [base, base + bytes): stride 0, reads past the end
-// return 0.
-LRA_DEV u32x4 make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t p = (uint64_t)base;
-    u32x4 r;
-    r[0] = (uint32_t)p;
-    r[1] = (uint32_t)(p >> 32) & 0xffffu;
-    r[2] = bytes;
-    r[3] = 0x00020000u;
-    return r;
-}
-
 // One 1 KB HBM -> LDS block (buffer_load_dwordx4 ... lds): lane i reads 16
 // bytes at byte offset voff of the resource and they land at LDS address
 // lds + 16*i.  Issued from asm so that the compiler does not serialise the

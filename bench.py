@@ -167,7 +167,7 @@ class DecodeSet:
         self.out = None
 
 
-def primary_decode(steps, warmup, n_sets):
+def primary_decode(steps, warmup, n_sets, rope_theta=None):
     import torch
     import attention_shared_base_amd as lra
     import workloads as w
@@ -182,14 +182,20 @@ def primary_decode(steps, warmup, n_sets):
         device="cuda")
     for s in sets:
         s.out = torch.empty_like(s.q)
+    cos = sin = None
+    if rope_theta is not None:
+        cos, sin = lra.rope_table(rope_theta, 128, max_len)
 
     def call(i):
         s = sets[i]
         lra.decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
-                   max_req_per_ctx=mrpc, max_ctx_len=max_len, out=s.out, workspace=ws)
+                   max_req_per_ctx=mrpc, max_ctx_len=max_len, rope_cos=cos, rope_sin=sin,
+                   out=s.out, workspace=ws)
 
     ms = _time_calls(call, n_sets, steps, warmup)
     nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, 16)
+    if rope_theta is not None:
+        nbytes += 2 * max_len * 64 * 4  # the cos / sin rows, read once
     return cases[0], ms, nbytes
 
 

@@ -62,7 +62,7 @@ typedef int32_t lra_status;
 #define LRA_F32 0
 #define LRA_BF16 1
 
-#define LRA_ABI_VERSION 1
+#define LRA_ABI_VERSION 2
 
 typedef struct lra_dims {
     int32_t n_q_heads;   /* H_q */
@@ -111,6 +111,15 @@ const char* lra_last_error(void);
  *                  The newest token is part of the context; a context of
  *                  length 0 yields zero output rows.
  *   b_k, b_v       [n_agents, r, H_kv * d]; head h uses columns h*d .. h*d+d-1
+ *   rope_cos,
+ *   rope_sin       NULL (no rotation of the adapter key term) or both
+ *                  [max(max_ctx_len, 1), d/2] fp32 device tables of
+ *                  cos/sin(pos * theta^(-2i/d)) (lra_rope_table_build); the
+ *                  key at token index j of a context has position j.  K_base
+ *                  is expected already rotated; the adapter key term
+ *                  L_k B_k is rebuilt at head dimension for each request and
+ *                  rotated (rotate-half pairing i, i+d/2) before it meets the
+ *                  query (LRAgent App. D.1), never stored.
  *   out            [n_req, H_q, d]                          device
  *   workspace      device scratch of at least
  *                  lra_attn_decode_workspace_size(...) bytes (0 when every
@@ -140,6 +149,7 @@ lra_status lra_attn_decode(const lra_dims* dims,
                            const int32_t* block_table, int32_t max_blocks,
                            const int32_t* ctx_len, int32_t max_ctx_len,
                            const void* b_k, const void* b_v, int32_t n_agents,
+                           const float* rope_cos, const float* rope_sin,
                            void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -192,7 +202,7 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
                               void* l_k, void* l_v, int64_t row_offset, void* stream);
 
 /*
- * RoPE tables for the prefill: cos/sin of pos * theta^(-2i/d), pos in
+ * RoPE tables for prefill and decode: cos/sin of pos * theta^(-2i/d), pos in
  * [0, n_pos), i in [0, head_dim/2), computed in fp64 and stored as fp32,
  * row-major [n_pos, head_dim/2].  (LRAgent App. D.1 names RoPE; the frequency
  * formula is the standard rotary one.)

@@ -250,15 +250,17 @@ def gather_pages(kv_pool, l_pool, table_row, length):
 
 
 def decode_paged(q, req_ctx, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table,
-                 ctx_len, b_k, b_v, *, scale=None, requests=None):
+                 ctx_len, b_k, b_v, *, rope=None, scale=None, requests=None):
     """Decode: one new query token per request over its context's shared caches.
 
     ``q`` ``[n_req, H_q, d]``; request ``i`` reads context ``req_ctx[i]`` (its
     base and LR pages) with agent ``req_agent[i]``'s ``B_k``/``B_v``
     (``b_k``, ``b_v``: ``[n_agents, r, H_kv*d]``).  The newest token is part of
-    the context, so the query sees all ``ctx_len[c]`` keys.  ``requests``
-    optionally restricts which requests are evaluated (rows of the output for
-    the others are left as NaN).
+    the context, so the query sees all ``ctx_len[c]`` keys.  ``rope`` is
+    ``(cos, sin)`` ``[>= max ctx_len, d/2]``: the adapter key term of the key at
+    token index ``j`` of a context is rotated by row ``j`` (App. D.1, as in
+    prefill).  ``requests`` optionally restricts which requests are evaluated
+    (rows of the output for the others are left as NaN).
     """
     q = _f64(q)
     n_req, h_q, d = q.shape
@@ -270,7 +272,7 @@ def decode_paged(q, req_ctx, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
         kb, lk = gather_pages(k_pool, lk_pool, block_table[c], n)
         vb, lv = gather_pages(v_pool, lv_pool, block_table[c], n)
         out[i] = attention_materialised(q[i][None], kb, vb, lk, lv, _f64(b_k[a]), _f64(b_v[a]),
-                                        q_pos=[n - 1], scale=scale)[0]
+                                        q_pos=[n - 1], rope=rope, scale=scale)[0]
     return out
 
 

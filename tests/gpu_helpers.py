@@ -73,24 +73,38 @@ class DecodeDev:
         counts = np.bincount(case.req_ctx, minlength=case.n_ctx)
         self.max_req_per_ctx = int(max(1, counts.max()))
         self.max_ctx_len = int(case.ctx_len.max())
+        self._rope = {}
 
-    def run(self, out=None, workspace=None, b_k=None, b_v=None, q=None):
+    def rope(self, theta):
+        """fp32 RoPE tables [max(max_ctx_len, 1), d/2] built on the GPU (cached per theta)."""
         import attention_shared_base_amd as lra
+        if theta not in self._rope:
+            self._rope[theta] = lra.rope_table(theta, self.case.d, max(self.max_ctx_len, 1))
+        return self._rope[theta]
+
+    def run(self, out=None, workspace=None, b_k=None, b_v=None, q=None, rope_theta=None):
+        import attention_shared_base_amd as lra
+        cos = sin = None
+        if rope_theta is not None:
+            cos, sin = self.rope(rope_theta)
         return lra.decode(self.q if q is None else q, self.crs, self.agent, self.k, self.v,
                           self.lk, self.lv, self.bt, self.clen,
                           self.b_k if b_k is None else b_k, self.b_v if b_v is None else b_v,
                           max_req_per_ctx=self.max_req_per_ctx, max_ctx_len=self.max_ctx_len,
-                          out=out, workspace=workspace)
+                          rope_cos=cos, rope_sin=sin, out=out, workspace=workspace)
 
 
-def oracle_decode(case: w.DecodeCase, requests=None, zero_b=False):
+def oracle_decode(case: w.DecodeCase, requests=None, zero_b=False, rope_theta=None):
     import oracle
     bk = np.zeros_like(w.widen(case.b_k)) if zero_b else w.widen(case.b_k)
     bv = np.zeros_like(w.widen(case.b_v)) if zero_b else w.widen(case.b_v)
+    rope = None
+    if rope_theta is not None:
+        rope = oracle.rope_tables(max(int(case.ctx_len.max()), 1), case.d, rope_theta)
     return oracle.decode_paged(w.widen(case.q), case.req_ctx, case.req_agent,
                                w.widen(case.k_pool), w.widen(case.v_pool), w.widen(case.lk_pool),
                                w.widen(case.lv_pool), case.block_table, case.ctx_len, bk, bv,
-                               requests=requests)
+                               rope=rope, requests=requests)
 
 
 # ------------------------------------------------------------------ prefill

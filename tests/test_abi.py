@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = lra.load()
-    assert lra.abi_version() == 1
+    assert lra.abi_version() == 2
     for s in range(7):
         assert lib.lra_status_str(s).decode().startswith("LRA_")
     assert b"unknown" in lib.lra_status_str(99)
@@ -53,14 +53,14 @@ def call_decode(dm, **over):
     # call needs a workspace and every case below fails validation before launch.
     args = dict(q=A, n_req=16, crs=A, n_ctx=4, mrpc=4, agent=A, k=A, v=A, lk=A, lv=A,
                 n_pages=2048, page=16, bt=A, max_blocks=512, clen=A, max_ctx=8192, bk=A, bv=A,
-                n_agents=4, out=A, ws=A, ws_bytes=1 << 30)
+                n_agents=4, cos=None, sin=None, out=A, ws=A, ws_bytes=1 << 30)
     args.update(over)
     st = lib.lra_attn_decode(ctypes.byref(dm), args["q"], args["n_req"], args["crs"], args["n_ctx"],
                              args["mrpc"], args["agent"], args["k"], args["v"], args["lk"],
                              args["lv"], args["n_pages"], args["page"], args["bt"],
                              args["max_blocks"], args["clen"], args["max_ctx"], args["bk"],
-                             args["bv"], args["n_agents"], args["out"], args["ws"],
-                             args["ws_bytes"], None)
+                             args["bv"], args["n_agents"], args["cos"], args["sin"], args["out"],
+                             args["ws"], args["ws_bytes"], None)
     return st, lib.lra_last_error().decode()
 
 
@@ -87,6 +87,8 @@ def call_decode(dm, **over):
     (dims(), {"k": ctypes.c_void_p(0x100008)}, 4),
     (dims(), {"ws_bytes": 1}, 5),
     (dims(), {"ws": None}, 1),
+    (dims(), {"cos": A}, 1),                 # rope tables go in pairs
+    (dims(), {"cos": A, "sin": ctypes.c_void_p(0x100004)}, 4),
 ])
 def test_decode_validation(dm, over, want):
     st, msg = call_decode(dm, **over)
@@ -96,8 +98,8 @@ def test_decode_validation(dm, over, want):
 
 def test_decode_null_dims():
     lib = lra.load()
-    st = lib.lra_attn_decode(None, A, 1, A, 1, 1, A, A, A, A, A, 1, 16, A, 1, A, 16, A, A, 1, A,
-                             A, 0, None)
+    st = lib.lra_attn_decode(None, A, 1, A, 1, 1, A, A, A, A, A, 1, 16, A, 1, A, 16, A, A, 1, None,
+                             None, A, A, 0, None)
     assert st == 1
 
 
