@@ -241,6 +241,22 @@ def extra_paged_decode(steps, warmup):
             "algorithmic_bytes": nbytes}
 
 
+def extra_decode_rope(steps, warmup, base_ms):
+    """The primary decode workload with RoPE (theta 5e5) on the adapter key term: each
+    request's key adapter is rebuilt at head dimension and rotated per page."""
+    case, ms, nbytes = primary_decode(steps, warmup, 4, rope_theta=500000.0)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "decode with RoPE on the adapter key: 16 requests over 4 shared 8192-token "
+                    "contexts, Hq32 Hkv8 d128 r16, theta 5e5, bf16",
+        "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+        "time_vs_no_rope": ms / base_ms,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "algorithmic_bytes": nbytes,
+    }
+
+
 def extra_prefill_rope(steps, warmup, n_sets=2):
     """512 new tokens over a 16384-token shared context, 4 agents, RoPE 5e5 on the adapter key."""
     import torch
@@ -397,7 +413,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="prefill_rope,paged_decode,lr_build,prelr_step",
+    ap.add_argument("--extra", default="decode_rope,prefill_rope,paged_decode,lr_build,prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -427,7 +443,8 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        legs = {"prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
+        legs = {"decode_rope": lambda: extra_decode_rope(args.steps, args.warmup, ms),
+                "prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
                 "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
                 "lr_build": lambda: extra_lr_build(args.steps, 10),
                 "prelr_step": lambda: extra_prelr_step(1, 1)}
