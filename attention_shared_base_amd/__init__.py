@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
-    "lr_cache_build", "rope_table", "abi_version", "EXPORTED_SYMBOLS",
+    "lr_cache_build", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +26,7 @@ LRA_F32, LRA_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "lra_abi_version", "lra_status_str", "lra_last_error", "lra_attn_decode_workspace_size",
     "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build", "lra_rope_table_build",
+    "lra_naive_expand_pages",
 )
 
 
@@ -75,6 +76,10 @@ def load():
     lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, P, P, ctypes.c_int64, P]
     lib.lra_rope_table_build.restype = I32
     lib.lra_rope_table_build.argtypes = [ctypes.c_double, I32, I32, P, P, P]
+    lib.lra_naive_expand_pages.restype = I32
+    lib.lra_naive_expand_pages.argtypes = [
+        ctypes.POINTER(Dims), I32, P, I32, P, P, P, P, P, I32, I32, P, I32, P, P, P, I32, P, P,
+        I32, P]
     _lib = lib
     return lib
 
@@ -258,3 +263,54 @@ def rope_table(theta, head_dim, n_pos, device="cuda", stream=None):
     _check(lib.lra_rope_table_build(float(theta), head_dim, n_pos, _ptr(cos), _ptr(sin),
                                     _stream(cos, stream)))
     return cos, sin
+
+
+def naive_decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table,
+                 ctx_len, b_k, b_v, *, max_req_per_ctx, max_ctx_len, scratch=None,
+                 softmax_scale=0.0, stream=None):
+    """Measurement baseline (not the method): ``lra_naive_expand_pages`` writes each
+    request's K_base + L_k B_k and V_base + L_v B_v to pages of its own, then
+    ``lra_attn_decode`` runs plain attention over them (one context per request,
+    B = 0).  ``scratch`` (a dict, filled on first use and reusable while the shapes
+    stay the same) holds those buffers.  Returns the output [n_req, H_q, d]."""
+    import torch
+    lib = load()
+    n_req, h_q, d = q.shape
+    n_pages, h_kv = k_pool.shape[:2]
+    r = lk_pool.shape[2]
+    n_ctx, max_blocks = block_table.shape
+    n_agents = b_k.shape[0]
+    out_blocks = max(1, -(-max_ctx_len // 16))
+    _need(out_blocks <= max_blocks, "max_ctx_len exceeds the block table")
+    sc = scratch if scratch is not None else {}
+    if sc.get("key") != (n_req, h_kv, d, r, out_blocks, str(q.dtype)):
+        dev = q.device
+        sc.clear()
+        sc["key"] = (n_req, h_kv, d, r, out_blocks, str(q.dtype))
+        sc["k"] = torch.empty((n_req * out_blocks,) + tuple(k_pool.shape[1:]), dtype=q.dtype, device=dev)
+        sc["v"] = torch.empty((n_req * out_blocks,) + tuple(v_pool.shape[1:]), dtype=q.dtype, device=dev)
+        sc["lk"] = torch.zeros((n_req * out_blocks, 16, r), dtype=q.dtype, device=dev)
+        sc["lv"] = torch.zeros((n_req * out_blocks, r, 16), dtype=q.dtype, device=dev)
+        sc["bz"] = torch.zeros((1, r, h_kv * d), dtype=q.dtype, device=dev)
+        sc["agent0"] = torch.zeros(n_req, dtype=torch.int32, device=dev)
+        sc["crs"] = torch.arange(n_req + 1, dtype=torch.int32, device=dev)
+        sc["bt"] = torch.arange(n_req * out_blocks, dtype=torch.int32, device=dev).view(n_req, out_blocks)
+        req_ctx = torch.searchsorted(ctx_req_start[1:].to(torch.int64),
+                                     torch.arange(n_req, device=dev), right=True)
+        sc["len"] = ctx_len.to(torch.int64)[req_ctx].to(torch.int32).contiguous()
+        sc["out"] = torch.empty_like(q)
+        sc["ws"] = None
+    dims = _dims(h_q, h_kv, d, r, _dtype_code(q), softmax_scale)
+    _check(lib.lra_naive_expand_pages(
+        ctypes.byref(dims), n_req, _ptr(ctx_req_start), n_ctx, _ptr(req_agent), _ptr(k_pool),
+        _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _ptr(block_table), max_blocks,
+        _ptr(ctx_len), _ptr(b_k), _ptr(b_v), n_agents, _ptr(sc["k"]), _ptr(sc["v"]), out_blocks,
+        _stream(q, stream)))
+    if sc["ws"] is None:
+        n_ws = decode_workspace_size(n_q_heads=h_q, n_kv_heads=h_kv, head_dim=d, rank=r,
+                                     dtype=_dtype_code(q), n_req=n_req, n_ctx=n_req,
+                                     max_req_per_ctx=1, max_ctx_len=max_ctx_len)
+        sc["ws"] = torch.zeros(max(n_ws, 16), dtype=torch.uint8, device=q.device)
+    return decode(q, sc["crs"], sc["agent0"], sc["k"], sc["v"], sc["lk"], sc["lv"], sc["bt"],
+                  sc["len"], sc["bz"], sc["bz"], max_req_per_ctx=1, max_ctx_len=max_ctx_len,
+                  out=sc["out"], workspace=sc["ws"], softmax_scale=softmax_scale, stream=stream)

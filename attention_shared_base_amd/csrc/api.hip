@@ -322,6 +322,63 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
     return lra::launch_lr_build_bf16(a, (hipStream_t)stream);
 }
 
+lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req, const int32_t* ctx_req_start,
+                                  int32_t n_ctx, const int32_t* req_agent, const void* k_pool,
+                                  const void* v_pool, const void* lk_pool, const void* lv_pool,
+                                  int32_t n_pages, int32_t page_size, const int32_t* block_table,
+                                  int32_t max_blocks, const int32_t* ctx_len, const void* b_k,
+                                  const void* b_v, int32_t n_agents, void* k_out, void* v_out,
+                                  int32_t out_blocks, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "naive expand: bf16 only");
+    if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+    if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
+    if (n_ctx < 1) return fail(LRA_ERR_BAD_SHAPE, "n_ctx %d < 1", n_ctx);
+    if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
+    if (max_blocks < 1) return fail(LRA_ERR_BAD_SHAPE, "max_blocks %d < 1", max_blocks);
+    if (out_blocks < 1 || out_blocks > max_blocks)
+        return fail(LRA_ERR_BAD_SHAPE, "out_blocks %d outside [1, max_blocks=%d]", out_blocks, max_blocks);
+    if (n_agents < 1) return fail(LRA_ERR_BAD_SHAPE, "n_agents %d < 1", n_agents);
+    REQUIRE_PTR(ctx_req_start);
+    REQUIRE_PTR(req_agent);
+    REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool);
+    REQUIRE_PTR(lk_pool);
+    REQUIRE_PTR(lv_pool);
+    REQUIRE_PTR(block_table);
+    REQUIRE_PTR(ctx_len);
+    REQUIRE_PTR(b_k);
+    REQUIRE_PTR(b_v);
+    REQUIRE_PTR(k_out);
+    REQUIRE_PTR(v_out);
+    lra::ExpandArgs a;
+    a.ctx_req_start = ctx_req_start;
+    a.req_agent = req_agent;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.lk_pool = lk_pool;
+    a.lv_pool = lv_pool;
+    a.block_table = block_table;
+    a.ctx_len = ctx_len;
+    a.b_k = b_k;
+    a.b_v = b_v;
+    a.k_out = k_out;
+    a.v_out = v_out;
+    a.n_req = n_req;
+    a.n_ctx = n_ctx;
+    a.n_pages = n_pages;
+    a.max_blocks = max_blocks;
+    a.n_agents = n_agents;
+    a.out_blocks = out_blocks;
+    a.h_kv = dims->n_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.rank = dims->rank;
+    if (n_req == 0) return LRA_OK;
+    return lra::launch_naive_expand_bf16(a, (hipStream_t)stream);
+}
+
 lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos, float* cos_out,
                                 float* sin_out, void* stream) {
     g_err[0] = 0;

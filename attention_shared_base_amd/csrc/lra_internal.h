@@ -102,4 +102,25 @@ lra_status launch_lr_build_f32(const LRBuildArgs& a, hipStream_t s);
 lra_status launch_rope_table(double theta, int head_dim, int n_pos, float* c, float* s,
                              hipStream_t st);
 
+// ----------------------------------------------------------------- naive baseline
+// Materialised adapter terms (measurement baseline only; see naive_expand.hip).
+struct ExpandArgs {
+    const int32_t* ctx_req_start;
+    const int32_t* req_agent;
+    const void* k_pool;
+    const void* v_pool;
+    const void* lk_pool;
+    const void* lv_pool;
+    const int32_t* block_table;
+    const int32_t* ctx_len;
+    const void* b_k;
+    const void* b_v;
+    void* k_out;
+    void* v_out;
+    int32_t n_req, n_ctx, n_pages, max_blocks, n_agents, out_blocks;
+    int32_t h_kv, head_dim, rank;
+};
+
+lra_status launch_naive_expand_bf16(const ExpandArgs& a, hipStream_t s);
+
 }  // namespace lra

@@ -257,6 +257,45 @@ def extra_decode_rope(steps, warmup, base_ms):
     }
 
 
+def extra_naive_decode(steps, warmup, base_ms):
+    """Baseline of the Flash-LoRA comparison on the primary decode workload: every
+    request's K, V materialised at head dimension (expansion kernel), then plain decode
+    attention over the per-request caches.  Reported next to the method's time."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    n_sets = 2
+    cases = [w.config2(layer=i) for i in range(n_sets)]
+    sets = [DecodeSet(c) for c in cases]
+    c0 = cases[0]
+    mrpc = int(np.bincount(c0.req_ctx).max())
+    max_len = int(c0.ctx_len.max())
+    scratch = {}
+
+    def call(i):
+        s = sets[i]
+        lra.naive_decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
+                         max_req_per_ctx=mrpc, max_ctx_len=max_len, scratch=scratch)
+
+    ms = _time_calls(call, n_sets, steps, warmup)
+    n_tok = int(c0.ctx_len[c0.req_ctx].sum())
+    # bytes the baseline moves: base K, V read and the expanded K, V written per request,
+    # the expanded K, V read again by the attention (per KV head, bf16)
+    kv_req = n_tok * 8 * 128 * 2 * 2
+    nbytes = 3 * kv_req
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "baseline without Flash-LoRA-Attention: primary decode workload with each "
+                    "request's K = K_base + L_k B_k, V = V_base + L_v B_v written to HBM, then "
+                    "plain decode attention over the per-request caches",
+        "value": c0.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+        "method_speedup": ms / base_ms,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "algorithmic_bytes": nbytes,
+    }
+
+
 def extra_prefill_rope(steps, warmup, n_sets=2):
     """512 new tokens over a 16384-token shared context, 4 agents, RoPE 5e5 on the adapter key."""
     import torch
@@ -413,7 +452,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="decode_rope,prefill_rope,paged_decode,lr_build,prelr_step",
+    ap.add_argument("--extra", default="decode_rope,naive_decode,prefill_rope,paged_decode,lr_build,"
+                                       "prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -444,6 +484,7 @@ def main():
     extra = {}
     if not args.no_extra:
         legs = {"decode_rope": lambda: extra_decode_rope(args.steps, args.warmup, ms),
+                "naive_decode": lambda: extra_naive_decode(max(5, args.steps // 10), 3, ms),
                 "prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
                 "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
                 "lr_build": lambda: extra_lr_build(args.steps, 10),

@@ -210,6 +210,34 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
 lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos,
                                 float* cos_out, float* sin_out, void* stream);
 
+/*
+ * Measurement baseline, not part of the method: the naive reconstruction that
+ * Flash-LoRA-Attention avoids (LRAgent §3 "Flash-LoRA-Attention" and App. B:
+ * expanding the low-rank terms to head dimension before attention).  For every
+ * request i (context c, agent a = req_agent[i]) and every block b of c
+ * (b < min(ceil(ctx_len[c] / page_size), out_blocks)) it writes page
+ * i * out_blocks + b of k_out / v_out:
+ *     K = K_base + L_k B_k^(a),  V = V_base + L_v B_v^(a)   (every KV head)
+ * in the layouts of k_pool / v_pool, bf16 rounded to nearest even.  Decode
+ * attention over those pages (lra_attn_decode with one context per request,
+ * block table i * out_blocks + b and B = 0) is then plain attention over
+ * per-request materialised caches.  Arguments as in lra_attn_decode;
+ *   k_out, v_out   [n_req * out_blocks, H_kv, ...] device, caller-owned
+ *   out_blocks     blocks reserved per request, 1 <= out_blocks <= max_blocks
+ * bf16 only.  Blocks past a context's length are not written.
+ */
+lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req,
+                                  const int32_t* ctx_req_start, int32_t n_ctx,
+                                  const int32_t* req_agent,
+                                  const void* k_pool, const void* v_pool,
+                                  const void* lk_pool, const void* lv_pool,
+                                  int32_t n_pages, int32_t page_size,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* ctx_len,
+                                  const void* b_k, const void* b_v, int32_t n_agents,
+                                  void* k_out, void* v_out, int32_t out_blocks,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -171,3 +171,31 @@ def test_workspace_size_queries():
     assert ws_small == 0  # a single chunk per unit needs no partials
     assert lib.lra_attn_decode_workspace_size(ctypes.byref(dims(dt=0)), 16, 4, 4, 8192) == 0
     assert lib.lra_attn_decode_workspace_size(ctypes.byref(dims(d=96)), 16, 4, 4, 8192) == 0
+
+
+def call_expand(dm, **over):
+    lib = lra.load()
+    a = dict(n_req=4, crs=A, n_ctx=2, agent=A, k=A, v=A, lk=A, lv=A, n_pages=64, page=16, bt=A,
+             max_blocks=32, clen=A, bk=A, bv=A, n_agents=2, ko=A, vo=A, out_blocks=32)
+    a.update(over)
+    st = lib.lra_naive_expand_pages(ctypes.byref(dm), a["n_req"], a["crs"], a["n_ctx"], a["agent"],
+                                    a["k"], a["v"], a["lk"], a["lv"], a["n_pages"], a["page"],
+                                    a["bt"], a["max_blocks"], a["clen"], a["bk"], a["bv"],
+                                    a["n_agents"], a["ko"], a["vo"], a["out_blocks"], None)
+    return st, lib.lra_last_error().decode()
+
+
+@pytest.mark.parametrize("dm,over,want", [
+    (dims(dt=0), {}, 3),                     # the baseline is bf16 only
+    (dims(r=4), {}, 3),
+    (dims(), {"page": 8}, 3),
+    (dims(), {"out_blocks": 0}, 2),
+    (dims(), {"out_blocks": 33}, 2),
+    (dims(), {"n_ctx": 0}, 2),
+    (dims(), {"ko": None}, 1),
+    (dims(), {"vo": ctypes.c_void_p(0x100002)}, 4),
+])
+def test_naive_expand_validation(dm, over, want):
+    st, msg = call_expand(dm, **over)
+    assert st == want, msg
+    assert msg
