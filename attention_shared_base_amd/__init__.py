@@ -16,6 +16,7 @@ import os
 __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
+    "prefill_paged", "cache_append",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +27,8 @@ LRA_F32, LRA_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "lra_abi_version", "lra_status_str", "lra_last_error", "lra_attn_decode_workspace_size",
     "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build", "lra_rope_table_build",
-    "lra_naive_expand_pages",
+    "lra_naive_expand_pages", "lra_attn_prefill_paged_workspace_size", "lra_attn_prefill_paged",
+    "lra_cache_append",
 )
 
 
@@ -76,6 +78,15 @@ def load():
     lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, P, P, ctypes.c_int64, P]
     lib.lra_rope_table_build.restype = I32
     lib.lra_rope_table_build.argtypes = [ctypes.c_double, I32, I32, P, P, P]
+    lib.lra_attn_prefill_paged_workspace_size.restype = ctypes.c_size_t
+    lib.lra_attn_prefill_paged_workspace_size.argtypes = [ctypes.POINTER(Dims), I32]
+    lib.lra_attn_prefill_paged.restype = I32
+    lib.lra_attn_prefill_paged.argtypes = [
+        ctypes.POINTER(Dims), P, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, P, I32, P, P,
+        P, P, ctypes.c_size_t, P]
+    lib.lra_cache_append.restype = I32
+    lib.lra_cache_append.argtypes = [ctypes.POINTER(Dims), I32, P, P, P, P, P, P, P, P, P, I32,
+                                     I32, P]
     lib.lra_naive_expand_pages.restype = I32
     lib.lra_naive_expand_pages.argtypes = [
         ctypes.POINTER(Dims), I32, P, I32, P, P, P, P, P, I32, I32, P, I32, P, P, P, I32, P, P,
@@ -314,3 +325,64 @@ def naive_decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, 
     return decode(q, sc["crs"], sc["agent0"], sc["k"], sc["v"], sc["lk"], sc["lv"], sc["bt"],
                   sc["len"], sc["bz"], sc["bz"], max_req_per_ctx=1, max_ctx_len=max_ctx_len,
                   out=sc["out"], workspace=sc["ws"], softmax_scale=softmax_scale, stream=stream)
+
+
+def prefill_paged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len, b_k,
+                  b_v, *, rope_cos=None, rope_sin=None, out=None, workspace=None,
+                  softmax_scale=0.0, stream=None):
+    """Chunked prefill over one context in the paged pools (``lra_attn_prefill_paged``):
+    q [n_req, q_len, H_q, d]; pools as in ``decode``; block_table_row [max_blocks] int32;
+    ``workspace`` (uint8) is allocated when not given."""
+    import torch
+    lib = load()
+    n_req, q_len, h_q, d = q.shape
+    n_pages, h_kv = k_pool.shape[:2]
+    r = lk_pool.shape[2]
+    n_agents = b_k.shape[0]
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
+                    ("lv_pool", lv_pool), ("b_k", b_k), ("b_v", b_v)):
+        _contig(name, t)
+        _need(_dtype_code(t) == dt, f"{name} dtype differs from q")
+    for name, t in (("req_agent", req_agent), ("block_table_row", block_table_row)):
+        _contig(name, t)
+        _need(t.dtype == torch.int32, f"{name} must be int32")
+    if rope_cos is not None:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            _contig(name, t)
+            _need(t.dtype == torch.float32 and t.shape[0] >= kv_len and t.shape[1] == d // 2,
+                  f"{name} must be fp32 [>=kv_len, d/2]")
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale)
+    need = int(lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dims), kv_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _contig("out", out)
+    _check(lib.lra_attn_prefill_paged(
+        ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_pool), _ptr(v_pool),
+        _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _ptr(block_table_row),
+        block_table_row.shape[0], kv_len, _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
+        _ptr(rope_sin), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q, stream)))
+    return out
+
+
+def cache_append(slot_mapping, k_new, v_new, lk_new, lv_new, k_pool, v_pool, lk_pool, lv_pool,
+                 *, n_q_heads=None, stream=None):
+    """Write new tokens' K/V rows [n_tok, H_kv, d] and LR rows [n_tok, r] into the paged
+    pools at ``slot_mapping`` [n_tok] int64 (``lra_cache_append``)."""
+    import torch
+    lib = load()
+    n_tok, h_kv, d = k_new.shape
+    r = lk_new.shape[1]
+    n_pages = k_pool.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("lk_new", lk_new), ("lv_new", lv_new),
+                    ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
+                    ("lv_pool", lv_pool), ("slot_mapping", slot_mapping)):
+        _contig(name, t)
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (n_tok,), "slot_mapping [n_tok] int64")
+    _need(tuple(v_new.shape) == (n_tok, h_kv, d) and tuple(lv_new.shape) == (n_tok, r), "new row shapes")
+    dims = _dims(n_q_heads or h_kv, h_kv, d, r, _dtype_code(k_new), 0.0)
+    _check(lib.lra_cache_append(ctypes.byref(dims), n_tok, _ptr(slot_mapping), _ptr(k_new),
+                                _ptr(v_new), _ptr(lk_new), _ptr(lv_new), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _stream(k_new, stream)))

@@ -20,7 +20,7 @@ LIB_NAME = "liblra_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.hip", "decode_bf16.hip", "prefill_bf16.hip", "attn_f32.hip", "lr_build.hip",
-           "naive_expand.hip"]
+           "naive_expand.hip", "paged.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

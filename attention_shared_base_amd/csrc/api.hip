@@ -119,6 +119,11 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     return true;
 }
 
+size_t prefill_paged_workspace(int h_kv, int d, int r, int kv_len) {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    return 2 * al((size_t)h_kv * kv_len * d * 2) + 2 * al((size_t)kv_len * r * 2);
+}
+
 }  // namespace lra
 
 extern "C" {
@@ -288,6 +293,117 @@ lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, 
     if (n_req == 0) return LRA_OK;
     if (dims->dtype == LRA_F32) return lra::launch_prefill_f32(a, (hipStream_t)stream);
     return lra::launch_prefill_bf16(a, (hipStream_t)stream);
+}
+
+size_t lra_attn_prefill_paged_workspace_size(const lra_dims* dims, int32_t kv_len) {
+    if (check_dims(dims) != LRA_OK || dims->dtype != LRA_BF16 || kv_len < 0) return 0;
+    return lra::prefill_paged_workspace(dims->n_kv_heads, dims->head_dim, dims->rank, kv_len);
+}
+
+lra_status lra_attn_prefill_paged(const lra_dims* dims, const void* q, int32_t n_req, int32_t q_len,
+                                  const int32_t* req_agent, const void* k_pool, const void* v_pool,
+                                  const void* lk_pool, const void* lv_pool, int32_t n_pages,
+                                  int32_t page_size, const int32_t* block_table, int32_t max_blocks,
+                                  int32_t kv_len, const void* b_k, const void* b_v, int32_t n_agents,
+                                  const float* rope_cos, const float* rope_sin, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "paged prefill: bf16 only");
+    if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+    if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
+    if (q_len < 1) return fail(LRA_ERR_BAD_SHAPE, "q_len %d < 1", q_len);
+    if (kv_len < q_len) return fail(LRA_ERR_BAD_SHAPE, "kv_len %d < q_len %d", kv_len, q_len);
+    if (max_blocks < 1 || (long long)max_blocks * page_size < kv_len)
+        return fail(LRA_ERR_BAD_SHAPE, "max_blocks %d cannot hold kv_len %d", max_blocks, kv_len);
+    REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool);
+    REQUIRE_PTR(lk_pool);
+    REQUIRE_PTR(lv_pool);
+    REQUIRE_PTR(block_table);
+    REQUIRE_PTR(workspace);
+    const size_t need = lra::prefill_paged_workspace(dims->n_kv_heads, dims->head_dim, dims->rank, kv_len);
+    if (workspace_bytes < need)
+        return fail(LRA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, need);
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    char* w = (char*)workspace;
+    const size_t kvb = al((size_t)dims->n_kv_heads * kv_len * dims->head_dim * 2);
+    const size_t lb = al((size_t)kv_len * dims->rank * 2);
+    lra::PagedArgs g{};
+    g.block_table = block_table;
+    g.k_pool = (void*)k_pool;
+    g.v_pool = (void*)v_pool;
+    g.lk_pool = (void*)lk_pool;
+    g.lv_pool = (void*)lv_pool;
+    g.k_out = w;
+    g.v_out = w + kvb;
+    g.lk_out = w + 2 * kvb;
+    g.lv_out = w + 2 * kvb + lb;
+    g.n_pages = n_pages;
+    g.h_kv = dims->n_kv_heads;
+    g.kv_len = kv_len;
+    g.head_dim = dims->head_dim;
+    g.rank = dims->rank;
+    // the staged rows feed the contiguous prefill: validate its arguments first
+    // (a failing call launches nothing)
+    if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
+    if (n_agents < 1) return fail(LRA_ERR_BAD_SHAPE, "n_agents %d < 1", n_agents);
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return fail(LRA_ERR_NULL_PTR, "rope_cos and rope_sin must both be given or both NULL");
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(req_agent);
+    REQUIRE_PTR(b_k);
+    REQUIRE_PTR(b_v);
+    REQUIRE_PTR(out);
+    if (rope_cos) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+    }
+    if (n_req == 0) return LRA_OK;
+    st = lra::launch_cache_gather_bf16(g, (hipStream_t)stream);
+    if (st != LRA_OK) return st;
+    return lra_attn_prefill(dims, q, n_req, q_len, req_agent, g.k_out, g.v_out, kv_len, g.lk_out,
+                            g.lv_out, b_k, b_v, n_agents, rope_cos, rope_sin, out, stream);
+}
+
+lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* slot_mapping,
+                            const void* k_new, const void* v_new, const void* lk_new,
+                            const void* lv_new, void* k_pool, void* v_pool, void* lk_pool,
+                            void* lv_pool, int32_t n_pages, int32_t page_size, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "cache append: bf16 only");
+    if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+    if (n_tok < 0) return fail(LRA_ERR_BAD_SHAPE, "n_tok %d < 0", n_tok);
+    if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
+    REQUIRE_PTR(slot_mapping);
+    REQUIRE_PTR(k_new);
+    REQUIRE_PTR(v_new);
+    REQUIRE_PTR(lk_new);
+    REQUIRE_PTR(lv_new);
+    REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool);
+    REQUIRE_PTR(lk_pool);
+    REQUIRE_PTR(lv_pool);
+    if (n_tok == 0) return LRA_OK;
+    lra::PagedArgs a{};
+    a.slots = slot_mapping;
+    a.k_rows = k_new;
+    a.v_rows = v_new;
+    a.lk_rows = lk_new;
+    a.lv_rows = lv_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.lk_pool = lk_pool;
+    a.lv_pool = lv_pool;
+    a.n_tok = n_tok;
+    a.n_pages = n_pages;
+    a.h_kv = dims->n_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.rank = dims->rank;
+    return lra::launch_cache_append_bf16(a, (hipStream_t)stream);
 }
 
 lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,

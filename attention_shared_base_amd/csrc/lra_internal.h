@@ -123,4 +123,29 @@ struct ExpandArgs {
 
 lra_status launch_naive_expand_bf16(const ExpandArgs& a, hipStream_t s);
 
+// ----------------------------------------------------------------- paged cache
+struct PagedArgs {
+    const int64_t* slots;        // append
+    const int32_t* block_table;  // gather: one context's row
+    const void* k_rows;          // append sources
+    const void* v_rows;
+    const void* lk_rows;
+    const void* lv_rows;
+    void* k_pool;
+    void* v_pool;
+    void* lk_pool;
+    void* lv_pool;
+    void* k_out;  // gather destinations
+    void* v_out;
+    void* lk_out;
+    void* lv_out;
+    int32_t n_tok, n_pages, h_kv, kv_len, head_dim, rank;
+};
+
+lra_status launch_cache_append_bf16(const PagedArgs& a, hipStream_t s);
+lra_status launch_cache_gather_bf16(const PagedArgs& a, hipStream_t s);
+
+// bytes of the contiguous K/V/L staging of a paged prefill (each part 256-byte aligned)
+size_t prefill_paged_workspace(int h_kv, int d, int r, int kv_len);
+
 }  // namespace lra

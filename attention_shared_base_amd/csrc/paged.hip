@@ -1,0 +1,166 @@
+// Paged cache maintenance around the attention kernels (LRAgent §3: agents
+// compute only the newly appended context; App. B: the accumulated context is
+// L = L_p + L_c).
+//
+// * Append: the base K/V rows and the shared LR rows of new tokens (a prefill
+//   chunk or one decode token per request) are written into the page pools at
+//   the slots a slot mapping names (slot = page * 16 + offset; negative = skip).
+//   Page layouts are the decode kernel's: K [H_kv][d/8][16][8], V [H_kv][d][16],
+//   L_k [16][r], L_v [r][16].
+// * Gather: one context's pages back to the contiguous per-head rows the
+//   chunked-prefill kernel streams ([H_kv, kv_len, d], [kv_len, r]).  Prefill is
+//   bound by the matrix cores (hundreds of flops per byte of K/V), so staging
+//   its keys and values once costs a few percent of the attention itself and
+//   leaves the prefill kernel's LDS tile layout untouched.
+#include "lra_common.h"
+#include "lra_internal.h"
+
+namespace {
+
+constexpr int PAGE = 16;
+
+struct PagedK {
+    const int64_t* slots;       // append: [n_tok]
+    const int32_t* block_table; // gather: one context's row
+    const bf16* k_rows;         // append source / gather destination (contiguous)
+    const bf16* v_rows;
+    const bf16* lk_rows;
+    const bf16* lv_rows;
+    bf16* k_pool;
+    bf16* v_pool;
+    bf16* lk_pool;
+    bf16* lv_pool;
+    bf16* k_out;  // gather outputs
+    bf16* v_out;
+    bf16* lk_out;
+    bf16* lv_out;
+    int32_t n_tok, n_pages, h_kv, kv_len, max_blocks;
+};
+
+// Append: workgroup = one token, 256 threads.  Rows k_rows/v_rows are
+// [n_tok, H_kv, d] (the layout a K/V projection produces), lk_rows/lv_rows
+// [n_tok, r].
+template <int D, int R>
+__global__ __launch_bounds__(256) void lra_cache_append_kernel(PagedK a) {
+    const int tok = blockIdx.x;
+    const int64_t slot = a.slots[tok];
+    if (slot < 0 || slot >= (int64_t)a.n_pages * PAGE) return;
+    const int64_t pid = slot / PAGE;
+    const int t = (int)(slot % PAGE);
+    const size_t kv_page = (size_t)a.h_kv * D * PAGE;
+    // K: 16-byte chunks (head, dim group); V: single elements (dim-major page)
+    for (int e = threadIdx.x; e < a.h_kv * (D / 8); e += blockDim.x) {
+        const int h = e / (D / 8), dg = e % (D / 8);
+        const bf16x8 v = *(const bf16x8*)(a.k_rows + ((size_t)tok * a.h_kv + h) * D + 8 * dg);
+        *(bf16x8*)(a.k_pool + pid * kv_page + (size_t)h * D * PAGE + ((size_t)dg * PAGE + t) * 8) = v;
+    }
+    for (int e = threadIdx.x; e < a.h_kv * D; e += blockDim.x) {
+        const int h = e / D, c = e % D;
+        a.v_pool[pid * kv_page + (size_t)h * D * PAGE + (size_t)c * PAGE + t] =
+            a.v_rows[((size_t)tok * a.h_kv + h) * D + c];
+    }
+    for (int e = threadIdx.x; e < R; e += blockDim.x) {
+        a.lk_pool[(pid * PAGE + t) * R + e] = a.lk_rows[(size_t)tok * R + e];
+        a.lv_pool[(pid * R + e) * PAGE + t] = a.lv_rows[(size_t)tok * R + e];
+    }
+}
+
+// Gather: workgroup = (block b of the context, KV head h), 256 threads.  The
+// dim-major V page is turned into rows through LDS.
+template <int D, int R>
+__global__ __launch_bounds__(256) void lra_cache_gather_kernel(PagedK a) {
+    __shared__ bf16 s_v[D][PAGE + 2];
+    const int b = blockIdx.x / a.h_kv;
+    const int h = blockIdx.x % a.h_kv;
+    const int key0 = b * PAGE;
+    const int n = min(PAGE, a.kv_len - key0);
+    const int pid = min(max(a.block_table[b], 0), a.n_pages - 1);
+    const size_t kv_page = (size_t)a.h_kv * D * PAGE;
+    const bf16* kp = a.k_pool + (size_t)pid * kv_page + (size_t)h * D * PAGE;
+    const bf16* vp = a.v_pool + (size_t)pid * kv_page + (size_t)h * D * PAGE;
+    for (int e = threadIdx.x; e < (D / 8) * PAGE; e += blockDim.x) {
+        const int dg = e / PAGE, t = e % PAGE;
+        if (t < n)
+            *(bf16x8*)(a.k_out + ((size_t)h * a.kv_len + key0 + t) * D + 8 * dg) = *(const bf16x8*)(kp + e * 8);
+    }
+    for (int e = threadIdx.x; e < D * PAGE; e += blockDim.x) s_v[e / PAGE][e % PAGE] = vp[e];
+    __syncthreads();
+    for (int e = threadIdx.x; e < PAGE * D; e += blockDim.x) {
+        const int t = e / D, c = e % D;
+        if (t < n) a.v_out[((size_t)h * a.kv_len + key0 + t) * D + c] = s_v[c][t];
+    }
+    if (h == 0) {
+        for (int e = threadIdx.x; e < PAGE * R; e += blockDim.x) {
+            const int t = e / R, rk = e % R;
+            if (t < n) {
+                a.lk_out[(size_t)(key0 + t) * R + rk] = a.lk_pool[((size_t)pid * PAGE + t) * R + rk];
+                a.lv_out[(size_t)(key0 + t) * R + rk] = a.lv_pool[((size_t)pid * R + rk) * PAGE + t];
+            }
+        }
+    }
+}
+
+template <int D, int R>
+lra_status launch_append_t(const lra::PagedArgs& p, hipStream_t s) {
+    PagedK k{};
+    k.slots = p.slots;
+    k.k_rows = (const bf16*)p.k_rows;
+    k.v_rows = (const bf16*)p.v_rows;
+    k.lk_rows = (const bf16*)p.lk_rows;
+    k.lv_rows = (const bf16*)p.lv_rows;
+    k.k_pool = (bf16*)p.k_pool;
+    k.v_pool = (bf16*)p.v_pool;
+    k.lk_pool = (bf16*)p.lk_pool;
+    k.lv_pool = (bf16*)p.lv_pool;
+    k.n_tok = p.n_tok;
+    k.n_pages = p.n_pages;
+    k.h_kv = p.h_kv;
+    hipLaunchKernelGGL((lra_cache_append_kernel<D, R>), dim3(p.n_tok), dim3(256), 0, s, k);
+    return lra::check_launch("lra_cache_append_kernel");
+}
+
+template <int D, int R>
+lra_status launch_gather_t(const lra::PagedArgs& p, hipStream_t s) {
+    PagedK k{};
+    k.block_table = p.block_table;
+    k.k_pool = (bf16*)p.k_pool;
+    k.v_pool = (bf16*)p.v_pool;
+    k.lk_pool = (bf16*)p.lk_pool;
+    k.lv_pool = (bf16*)p.lv_pool;
+    k.k_out = (bf16*)p.k_out;
+    k.v_out = (bf16*)p.v_out;
+    k.lk_out = (bf16*)p.lk_out;
+    k.lv_out = (bf16*)p.lv_out;
+    k.n_pages = p.n_pages;
+    k.h_kv = p.h_kv;
+    k.kv_len = p.kv_len;
+    const long long grid = (long long)((p.kv_len + PAGE - 1) / PAGE) * p.h_kv;
+    if (grid > 0x7fffffffLL) {
+        lra::set_error("paged gather: grid of %lld workgroups too large", grid);
+        return LRA_ERR_BAD_SHAPE;
+    }
+    hipLaunchKernelGGL((lra_cache_gather_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, s, k);
+    return lra::check_launch("lra_cache_gather_kernel");
+}
+
+}  // namespace
+
+namespace lra {
+
+#define LRA_DISPATCH(FN)                                                         \
+    if (p.head_dim == 128 && p.rank == 16) return FN<128, 16>(p, s);             \
+    if (p.head_dim == 128 && p.rank == 32) return FN<128, 32>(p, s);             \
+    if (p.head_dim == 128 && p.rank == 8) return FN<128, 8>(p, s);               \
+    if (p.head_dim == 64 && p.rank == 16) return FN<64, 16>(p, s);               \
+    if (p.head_dim == 64 && p.rank == 32) return FN<64, 32>(p, s);               \
+    if (p.head_dim == 64 && p.rank == 8) return FN<64, 8>(p, s);                 \
+    set_error("paged cache: unsupported head_dim %d / rank %d", p.head_dim, p.rank); \
+    return LRA_ERR_UNSUPPORTED;
+
+lra_status launch_cache_append_bf16(const PagedArgs& p, hipStream_t s) { LRA_DISPATCH(launch_append_t) }
+
+lra_status launch_cache_gather_bf16(const PagedArgs& p, hipStream_t s) { LRA_DISPATCH(launch_gather_t) }
+
+#undef LRA_DISPATCH
+
+}  // namespace lra

@@ -331,6 +331,48 @@ def extra_prefill_rope(steps, warmup, n_sets=2):
             "algorithmic_flops": fl}
 
 
+def extra_prefill_paged(steps, warmup, base_ms):
+    """The prefill leg's workload with the context in shuffled 16-token pages
+    (lra_attn_prefill_paged: staging of the context's rows, then the prefill)."""
+    import torch
+    import attention_shared_base_amd as lra
+    n_req, q_len, kv_len, h_q, h_kv, d, r = 4, 512, 16896, 32, 8, 128, 16
+    n_pages = kv_len // 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    sets = []
+    for _ in range(2):
+        sets.append(dict(
+            q=_randn_bf16((n_req, q_len, h_q, d), 1.0, g),
+            k=_randn_bf16((n_pages, h_kv, d // 8, 16, 8), 1.0, g),
+            v=_randn_bf16((n_pages, h_kv, d, 16), 1.0, g),
+            lk=_randn_bf16((n_pages, 16, r), 1.0, g), lv=_randn_bf16((n_pages, r, 16), 1.0, g),
+            bk=_randn_bf16((4, r, h_kv * d), 0.05, g), bv=_randn_bf16((4, r, h_kv * d), 0.05, g),
+            bt=torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32)))
+    agent = _dev(np.arange(4, dtype=np.int32))
+    cos, sin = lra.rope_table(500000.0, d, kv_len)
+    ws = torch.empty(2 * h_kv * kv_len * d * 2 + 2 * kv_len * r * 2 + 4096, dtype=torch.uint8,
+                     device="cuda")
+    for s in sets:
+        s["out"] = torch.empty_like(s["q"])
+
+    def call(i):
+        s = sets[i]
+        lra.prefill_paged(s["q"], agent, s["k"], s["v"], s["lk"], s["lv"], s["bt"], kv_len,
+                          s["bk"], s["bv"], rope_cos=cos, rope_sin=sin, out=s["out"], workspace=ws)
+
+    ms = _time_calls(call, 2, steps, warmup)
+    fl = prefill_flops(n_req, q_len, kv_len, h_q, h_kv, d, r, rope=True)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": "paged chunked prefill: the prefill leg's workload (512 new tokens over "
+                        "16384, 4 agents, RoPE) with the context in shuffled 16-token pages",
+            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms,
+            "time_vs_contiguous": ms / base_ms if base_ms else None,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None},
+            "algorithmic_flops": fl}
+
+
 def extra_lr_build(steps, warmup, n_sets=8):
     import torch
     import attention_shared_base_amd as lra
@@ -452,8 +494,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="decode_rope,naive_decode,prefill_rope,paged_decode,lr_build,"
-                                       "prelr_step",
+    ap.add_argument("--extra", default="decode_rope,naive_decode,prefill_rope,prefill_paged,"
+                                       "paged_decode,lr_build,prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -486,6 +528,9 @@ def main():
         legs = {"decode_rope": lambda: extra_decode_rope(args.steps, args.warmup, ms),
                 "naive_decode": lambda: extra_naive_decode(max(5, args.steps // 10), 3, ms),
                 "prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
+                "prefill_paged": lambda: extra_prefill_paged(
+                    max(5, args.steps // 10), 3,
+                    extra.get("prefill_rope", {}).get("ms_per_call")),
                 "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
                 "lr_build": lambda: extra_lr_build(args.steps, 10),
                 "prelr_step": lambda: extra_prelr_step(1, 1)}

@@ -186,6 +186,52 @@ lra_status lra_attn_prefill(const lra_dims* dims,
                             void* out, void* stream);
 
 /*
+ * Chunked prefill over one context held in the paged pools of lra_attn_decode
+ * (LRAgent §3: agents process only the newly appended context; App. B: the
+ * accumulated context L = L_p + L_c).  Same computation as lra_attn_prefill
+ * with k_base/v_base/l_k/l_v taken from the pages: logical token t is in page
+ * block_table[t / page_size], slot t % page_size (the q_len new tokens are the
+ * last q_len of the kv_len tokens, already appended with lra_cache_append).
+ * The context's keys, values and LR rows are first staged contiguously in the
+ * workspace (the prefill streams them from there), then attended as in
+ * lra_attn_prefill.
+ *   block_table  [max_blocks] int32, this context's row   device
+ *   workspace    >= lra_attn_prefill_paged_workspace_size(dims, kv_len) bytes,
+ *                device, caller-owned; no state is kept between calls
+ * Other arguments and layouts as in lra_attn_decode / lra_attn_prefill.
+ * bf16 only.
+ */
+size_t lra_attn_prefill_paged_workspace_size(const lra_dims* dims, int32_t kv_len);
+lra_status lra_attn_prefill_paged(const lra_dims* dims,
+                                  const void* q, int32_t n_req, int32_t q_len,
+                                  const int32_t* req_agent,
+                                  const void* k_pool, const void* v_pool,
+                                  const void* lk_pool, const void* lv_pool,
+                                  int32_t n_pages, int32_t page_size,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  int32_t kv_len,
+                                  const void* b_k, const void* b_v, int32_t n_agents,
+                                  const float* rope_cos, const float* rope_sin,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+/*
+ * Append new tokens to the paged pools (the decode-time and prefill-time write
+ * of the base K/V rows and the shared LR rows; LRAgent §3 BaseLRShared: one LR
+ * row per token serves every agent).  Token i goes to slot slot_mapping[i] =
+ * page * page_size + offset; a negative slot skips the token.
+ *   slot_mapping   [n_tok] int64                    device
+ *   k_new, v_new   [n_tok, H_kv, d] (K already rotated if the model uses RoPE)
+ *   lk_new, lv_new [n_tok, r]  (e.g. rows written by lra_lr_cache_build)
+ *   k_pool ...     the pools of lra_attn_decode, written in place
+ * Slots at or past n_pages * page_size are skipped.  Two tokens with the same
+ * slot leave either one.  bf16 only.
+ */
+lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* slot_mapping,
+                            const void* k_new, const void* v_new,
+                            const void* lk_new, const void* lv_new,
+                            void* k_pool, void* v_pool, void* lk_pool, void* lv_pool,
+                            int32_t n_pages, int32_t page_size, void* stream);
+/*
  * Shared low-rank cache rows for new tokens (PReCache PreLRShared; LRAgent §3
  * BaseLRShared with shared A):  L_k[row_offset + i] = x[i] A_k,
  * L_v[row_offset + i] = x[i] A_v  for i < n_tok, i.e. L = X A.

@@ -199,3 +199,41 @@ def test_naive_expand_validation(dm, over, want):
     st, msg = call_expand(dm, **over)
     assert st == want, msg
     assert msg
+
+
+def test_paged_prefill_and_append_validation():
+    lib = lra.load()
+    dm = dims()
+    # workspace size grows with kv_len and is 0 for an invalid dims
+    assert lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dm), 1000) > \
+        lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dm), 10) > 0
+    assert lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dims(dt=0)), 10) == 0
+
+    def pp(**o):
+        a = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, lk=A, lv=A, n_pages=64, page=16, bt=A,
+                 max_blocks=16, kv_len=256, bk=A, bv=A, n_agents=2, cos=None, sin=None, out=A,
+                 ws=A, ws_bytes=1 << 30)
+        a.update(o)
+        return lib.lra_attn_prefill_paged(ctypes.byref(o.pop("dm", dm)), a["q"], a["n_req"], a["q_len"],
+                                          a["agent"], a["k"], a["v"], a["lk"], a["lv"], a["n_pages"],
+                                          a["page"], a["bt"], a["max_blocks"], a["kv_len"], a["bk"],
+                                          a["bv"], a["n_agents"], a["cos"], a["sin"], a["out"],
+                                          a["ws"], a["ws_bytes"], None)
+    assert pp(max_blocks=15) == 2            # 15 blocks cannot hold 256 tokens
+    assert pp(ws_bytes=1) == 5
+    assert pp(ws=None) == 1
+    assert pp(kv_len=8) == 2                  # kv_len < q_len
+    assert pp(page=32) == 3
+    assert pp(cos=A) == 1
+
+    def ap(**o):
+        a = dict(n=4, slots=A, k=A, v=A, lk=A, lv=A, kp=A, vp=A, lkp=A, lvp=A, n_pages=8, page=16)
+        a.update(o)
+        return lib.lra_cache_append(ctypes.byref(o.pop("dm", dm)), a["n"], a["slots"], a["k"], a["v"],
+                                    a["lk"], a["lv"], a["kp"], a["vp"], a["lkp"], a["lvp"],
+                                    a["n_pages"], a["page"], None)
+    assert ap(slots=None) == 1
+    assert ap(n=-1) == 2
+    assert ap(page=8) == 3
+    assert ap(dm=dims(dt=0)) == 3
+    assert ap(kp=ctypes.c_void_p(0x100004)) == 4
