@@ -41,7 +41,8 @@ class LraError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("lr_agent_stride", ctypes.c_int64)]
 
 
 _lib = None
@@ -75,7 +76,8 @@ def load():
     lib.lra_attn_prefill.argtypes = [
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, P, P]
     lib.lra_lr_cache_build.restype = I32
-    lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, P, P, ctypes.c_int64, P]
+    lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, I32, P, P, ctypes.c_int64,
+                                       ctypes.c_int64, P]
     lib.lra_rope_table_build.restype = I32
     lib.lra_rope_table_build.argtypes = [ctypes.c_double, I32, I32, P, P, P]
     lib.lra_attn_prefill_paged_workspace_size.restype = ctypes.c_size_t
@@ -136,13 +138,13 @@ def _contig(name, t):
     return t
 
 
-def _dims(h_q, h_kv, d, r, dtype, scale):
-    return Dims(h_q, h_kv, d, r, dtype, float(scale))
+def _dims(h_q, h_kv, d, r, dtype, scale, lr_stride=0):
+    return Dims(h_q, h_kv, d, r, dtype, float(scale), int(lr_stride))
 
 
 def decode_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, dtype, n_req, n_ctx,
-                          max_req_per_ctx, max_ctx_len):
-    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, dtype, 0.0)
+                          max_req_per_ctx, max_ctx_len, lr_agent_stride=0):
+    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, dtype, 0.0, lr_agent_stride)
     return int(load().lra_attn_decode_workspace_size(ctypes.byref(dims), n_req, n_ctx,
                                                       max_req_per_ctx, max_ctx_len))
 
@@ -153,7 +155,9 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
     """Paged decode (``lra_attn_decode``).  Layouts as in include/lra_attn.h:
 
     q [n_req, H_q, d]; k_pool [n_pages, H_kv, d/8, 16, 8]; v_pool [n_pages, H_kv, d, 16];
-    lk_pool [n_pages, 16, r]; lv_pool [n_pages, r, 16]; block_table [n_ctx, max_blocks];
+    lk_pool [n_pages, 16, r]; lv_pool [n_pages, r, 16] (one LR cache for every agent) or
+    [n_agents, n_pages, 16, r] / [n_agents, n_pages, r, 16] (one per agent);
+    block_table [n_ctx, max_blocks];
     ctx_len [n_ctx]; ctx_req_start [n_ctx+1]; req_agent [n_req]; b_k, b_v [n_agents, r, H_kv*d];
     optional RoPE tables rope_cos, rope_sin [>= max(max_ctx_len, 1), d/2] fp32 rotate the
     adapter key term.  ``workspace`` (uint8, zero-filled before first use) is allocated
@@ -164,9 +168,11 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
     n_req, h_q, d = q.shape
     n_pages, h_kv, d8, page, eight = k_pool.shape
     _need(d8 * 8 == d and eight == 8, "k_pool must be [n_pages, H_kv, d/8, page, 8]")
-    r = lk_pool.shape[2]
+    r = lk_pool.shape[-1]
     n_ctx, max_blocks = block_table.shape
     n_agents = b_k.shape[0]
+    per_agent = lk_pool.dim() == 4
+    lr_stride = n_pages * page * r if per_agent else 0
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
                     ("lv_pool", lv_pool), ("b_k", b_k), ("b_v", b_v)):
@@ -177,8 +183,9 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
         _contig(name, t)
         _need(t.dtype == torch.int32, f"{name} must be int32")
     _need(tuple(v_pool.shape) == (n_pages, h_kv, d, page), "v_pool must be [n_pages, H_kv, d, page]")
-    _need(tuple(lk_pool.shape) == (n_pages, page, r), "lk_pool must be [n_pages, page, r]")
-    _need(tuple(lv_pool.shape) == (n_pages, r, page), "lv_pool must be [n_pages, r, page]")
+    lead = (n_agents,) if per_agent else ()
+    _need(tuple(lk_pool.shape) == lead + (n_pages, page, r), "lk_pool must be [(n_agents,) n_pages, page, r]")
+    _need(tuple(lv_pool.shape) == lead + (n_pages, r, page), "lv_pool must be [(n_agents,) n_pages, r, page]")
     _need(tuple(b_k.shape) == (n_agents, r, h_kv * d) and b_v.shape == b_k.shape,
           "b_k/b_v must be [n_agents, r, H_kv*d]")
     _need(ctx_req_start.shape == (n_ctx + 1,) and ctx_len.shape == (n_ctx,)
@@ -192,7 +199,7 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
     if out is None:
         out = torch.empty_like(q)
     _contig("out", out)
-    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale)
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale, lr_stride)
     ws_bytes = int(lib.lra_attn_decode_workspace_size(ctypes.byref(dims), n_req, n_ctx,
                                                       max_req_per_ctx, max_ctx_len))
     if workspace is None and ws_bytes > 0:
@@ -209,14 +216,17 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
 def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, rope_sin=None,
             out=None, softmax_scale=0.0, stream=None):
     """Chunked prefill (``lra_attn_prefill``): q [n_req, q_len, H_q, d] over
-    k_base/v_base [H_kv, kv_len, d], l_k/l_v [kv_len, r]; optional RoPE tables
-    [kv_len, d/2] fp32 rotate the adapter key term."""
+    k_base/v_base [H_kv, kv_len, d], l_k/l_v [kv_len, r] (shared) or [n_agents, kv_len, r]
+    (one LR cache per agent); optional RoPE tables [kv_len, d/2] fp32 rotate the adapter
+    key term."""
     import torch
     lib = load()
     n_req, q_len, h_q, d = q.shape
     h_kv, kv_len, _ = k_base.shape
-    r = l_k.shape[1]
+    r = l_k.shape[-1]
     n_agents = b_k.shape[0]
+    per_agent = l_k.dim() == 3
+    lead = (n_agents,) if per_agent else ()
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k_base", k_base), ("v_base", v_base), ("l_k", l_k), ("l_v", l_v),
                     ("b_k", b_k), ("b_v", b_v)):
@@ -225,7 +235,8 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, 
     _contig("req_agent", req_agent)
     _need(req_agent.dtype == torch.int32 and req_agent.shape == (n_req,), "req_agent [n_req] int32")
     _need(tuple(v_base.shape) == (h_kv, kv_len, d), "v_base shape")
-    _need(tuple(l_k.shape) == (kv_len, r) and tuple(l_v.shape) == (kv_len, r), "l_k/l_v [kv_len, r]")
+    _need(tuple(l_k.shape) == lead + (kv_len, r) and tuple(l_v.shape) == lead + (kv_len, r),
+          "l_k/l_v [(n_agents,) kv_len, r]")
     _need(tuple(b_k.shape) == (n_agents, r, h_kv * d) and b_v.shape == b_k.shape, "b_k/b_v shape")
     if rope_cos is not None:
         for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
@@ -235,7 +246,7 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, 
     if out is None:
         out = torch.empty_like(q)
     _contig("out", out)
-    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale)
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale, kv_len * r if per_agent else 0)
     _check(lib.lra_attn_prefill(
         ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_base), _ptr(v_base),
         kv_len, _ptr(l_k), _ptr(l_v), _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
@@ -246,22 +257,28 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, 
 def lr_cache_build(x, a_k, a_v, l_k, l_v, *, row_offset=0, stream=None):
     """LR-cache rows ``L[row_offset + i] = x[i] A`` (``lra_lr_cache_build``).
 
-    x [n_tok, d_model]; a_k, a_v [r, d_model] (LoRA A weight layout, out x in);
-    l_k, l_v [>= row_offset + n_tok, r], written in place.
+    x [n_tok, d_model]; a_k, a_v [r, d_model] (LoRA A weight layout, out x in) and
+    l_k, l_v [>= row_offset + n_tok, r], written in place; or, one A per agent,
+    a_k, a_v [n_agents, r, d_model] and l_k, l_v [n_agents, rows, r] (X [A_1 .. A_n]).
     """
     lib = load()
     n_tok, d_model = x.shape
-    r = a_k.shape[0]
+    r = a_k.shape[-2]
+    n_lr = a_k.shape[0] if a_k.dim() == 3 else 1
     dt = _dtype_code(x)
     for name, t in (("x", x), ("a_k", a_k), ("a_v", a_v), ("l_k", l_k), ("l_v", l_v)):
         _contig(name, t)
         _need(_dtype_code(t) == dt, f"{name} dtype differs from x")
-    _need(tuple(a_k.shape) == (r, d_model) and tuple(a_v.shape) == (r, d_model), "a_k/a_v [r, d_model]")
-    _need(l_k.shape[1] == r and l_v.shape[1] == r, "l_k/l_v [*, r]")
-    _need(l_k.shape[0] >= row_offset + n_tok and l_v.shape[0] >= row_offset + n_tok,
-          "l_k/l_v too short for row_offset + n_tok")
-    _check(lib.lra_lr_cache_build(dt, _ptr(x), n_tok, d_model, _ptr(a_k), _ptr(a_v), r,
-                                  _ptr(l_k), _ptr(l_v), int(row_offset), _stream(x, stream)))
+    lead = (n_lr,) if a_k.dim() == 3 else ()
+    _need(tuple(a_k.shape) == lead + (r, d_model) and tuple(a_v.shape) == lead + (r, d_model),
+          "a_k/a_v [(n_lr,) r, d_model]")
+    _need(l_k.dim() == len(lead) + 2 and l_k.shape[-1] == r and l_v.shape == l_k.shape
+          and tuple(l_k.shape[:len(lead)]) == lead, "l_k/l_v [(n_lr,) rows, r]")
+    rows = l_k.shape[-2]
+    _need(rows >= row_offset + n_tok, "l_k/l_v too short for row_offset + n_tok")
+    _check(lib.lra_lr_cache_build(dt, _ptr(x), n_tok, d_model, _ptr(a_k), _ptr(a_v), r, n_lr,
+                                  _ptr(l_k), _ptr(l_v), int(row_offset), rows * r if n_lr > 1 else 0,
+                                  _stream(x, stream)))
     return l_k, l_v
 
 

@@ -42,6 +42,8 @@ lra_status check_dims(const lra_dims* d) {
         return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 8, 16, 32)", d->rank);
     if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
         return fail(LRA_ERR_BAD_SHAPE, "softmax_scale is not finite");
+    if (d->lr_agent_stride < 0)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < 0", (long long)d->lr_agent_stride);
     return LRA_OK;
 }
 
@@ -80,7 +82,8 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     const int g = d.n_q_heads / d.n_kv_heads;
     if (g < 1 || g > 16 || n_ctx < 1 || max_req_per_ctx < 1 || max_ctx_len < 0 || n_req < 0) return false;
     p->g = g;
-    p->rpg = 16 / g;
+    // per-agent LR caches: one LR page stream per request slot, at most 4 per group
+    p->rpg = d.lr_agent_stride != 0 ? (16 / g < 4 ? 16 / g : 4) : 16 / g;
     p->n_rg = (max_req_per_ctx + p->rpg - 1) / p->rpg;
     const long long units = (long long)n_ctx * p->n_rg * d.n_kv_heads;
     if (units > (1 << 26)) return false;
@@ -213,6 +216,9 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
     a.rope_sin = rope_sin;
     a.out = out;
     a.workspace = workspace;
+    a.lr_stride = dims->lr_agent_stride;
+    if (rope_cos && dims->lr_agent_stride != 0 && dims->dtype == LRA_BF16)
+        return fail(LRA_ERR_UNSUPPORTED, "decode: RoPE with per-agent LR caches is not supported");
     a.n_req = n_req;
     a.n_ctx = n_ctx;
     a.n_pages = n_pages;
@@ -281,6 +287,7 @@ lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, 
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
     a.out = out;
+    a.lr_stride = dims->lr_agent_stride;
     a.n_req = n_req;
     a.q_len = q_len;
     a.kv_len = kv_len;
@@ -311,6 +318,8 @@ lra_status lra_attn_prefill_paged(const lra_dims* dims, const void* q, int32_t n
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
     if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "paged prefill: bf16 only");
+    if (dims->lr_agent_stride != 0)
+        return fail(LRA_ERR_UNSUPPORTED, "paged prefill: shared LR cache only (lr_agent_stride 0)");
     if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
     if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
     if (q_len < 1) return fail(LRA_ERR_BAD_SHAPE, "q_len %d < 1", q_len);
@@ -375,6 +384,8 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
     if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "cache append: bf16 only");
+    if (dims->lr_agent_stride != 0)
+        return fail(LRA_ERR_UNSUPPORTED, "cache append: shared LR cache only (lr_agent_stride 0)");
     if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
     if (n_tok < 0) return fail(LRA_ERR_BAD_SHAPE, "n_tok %d < 0", n_tok);
     if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
@@ -407,8 +418,9 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
 }
 
 lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,
-                              const void* a_k, const void* a_v, int32_t rank, void* l_k, void* l_v,
-                              int64_t row_offset, void* stream) {
+                              const void* a_k, const void* a_v, int32_t rank, int32_t n_lr,
+                              void* l_k, void* l_v, int64_t row_offset, int64_t lr_agent_stride,
+                              void* stream) {
     g_err[0] = 0;
     if (dtype != LRA_F32 && dtype != LRA_BF16)
         return fail(LRA_ERR_UNSUPPORTED, "dtype %d (expected LRA_F32=0 or LRA_BF16=1)", dtype);
@@ -418,6 +430,10 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
     if (d_model <= 0) return fail(LRA_ERR_BAD_SHAPE, "d_model %d <= 0", d_model);
     if (d_model % 32 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %d is not a multiple of 32", d_model);
     if (row_offset < 0) return fail(LRA_ERR_BAD_SHAPE, "row_offset %lld < 0", (long long)row_offset);
+    if (n_lr < 1) return fail(LRA_ERR_BAD_SHAPE, "n_lr %d < 1", n_lr);
+    if (n_lr > 1 && lr_agent_stride < (row_offset + n_tok) * (long long)rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld smaller than one cache's rows (%lld)",
+                    (long long)lr_agent_stride, (long long)(row_offset + n_tok) * rank);
     REQUIRE_PTR(x);
     REQUIRE_PTR(a_k);
     REQUIRE_PTR(a_v);
@@ -432,7 +448,9 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
     a.n_tok = n_tok;
     a.d_model = d_model;
     a.rank = rank;
+    a.n_lr = n_lr;
     a.row_offset = row_offset;
+    a.lr_stride = n_lr > 1 ? lr_agent_stride : 0;
     if (n_tok == 0) return LRA_OK;
     if (dtype == LRA_F32) return lra::launch_lr_build_f32(a, (hipStream_t)stream);
     return lra::launch_lr_build_bf16(a, (hipStream_t)stream);
@@ -449,6 +467,8 @@ lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req, const int
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
     if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "naive expand: bf16 only");
+    if (dims->lr_agent_stride != 0)
+        return fail(LRA_ERR_UNSUPPORTED, "naive expand: shared LR cache only (lr_agent_stride 0)");
     if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
     if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
     if (n_ctx < 1) return fail(LRA_ERR_BAD_SHAPE, "n_ctx %d < 1", n_ctx);

@@ -33,12 +33,14 @@ struct F32K {
     int32_t q_len, kv_len;  // prefill
     int32_t h_q, h_kv, d, r;
     float scale;
+    int64_t lr_stride;  // per-agent LR caches: elements between agents' caches (0: shared)
 };
 
 struct Paged {
     const F32K* a;
     const int32_t* bt;
     int h;
+    size_t lr_off;  // this request's LR cache
     __device__ int pid(int j) const {
         int p = bt[j / PAGE];
         return min(max(p, 0), a->n_pages - 1);
@@ -51,17 +53,22 @@ struct Paged {
         const int d = a->d;
         return a->v[(((size_t)pid(j) * a->h_kv + h) * d + c) * PAGE + j % PAGE];
     }
-    __device__ float LK(int j, int t) const { return a->lk[((size_t)pid(j) * PAGE + j % PAGE) * a->r + t]; }
-    __device__ float LV(int j, int t) const { return a->lv[((size_t)pid(j) * a->r + t) * PAGE + j % PAGE]; }
+    __device__ float LK(int j, int t) const {
+        return a->lk[lr_off + ((size_t)pid(j) * PAGE + j % PAGE) * a->r + t];
+    }
+    __device__ float LV(int j, int t) const {
+        return a->lv[lr_off + ((size_t)pid(j) * a->r + t) * PAGE + j % PAGE];
+    }
 };
 
 struct Contig {
     const F32K* a;
     int h;
+    size_t lr_off;  // this request's LR cache
     __device__ float K(int j, int c) const { return a->k[((size_t)h * a->kv_len + j) * a->d + c]; }
     __device__ float V(int j, int c) const { return a->v[((size_t)h * a->kv_len + j) * a->d + c]; }
-    __device__ float LK(int j, int t) const { return a->lk[(size_t)j * a->r + t]; }
-    __device__ float LV(int j, int t) const { return a->lv[(size_t)j * a->r + t]; }
+    __device__ float LK(int j, int t) const { return a->lk[lr_off + (size_t)j * a->r + t]; }
+    __device__ float LV(int j, int t) const { return a->lv[lr_off + (size_t)j * a->r + t]; }
 };
 
 // One query row: q (length d) at absolute position `pos`, sees keys 0..pos.
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(64) void lra_decode_f32_kernel(F32K a) {
         return;
     }
     int agent = min(max(a.req_agent[req], 0), a.n_agents - 1);
-    Paged acc{&a, a.block_table + (size_t)ctx * a.max_blocks, h};
+    Paged acc{&a, a.block_table + (size_t)ctx * a.max_blocks, h, (size_t)agent * a.lr_stride};
     row_attend(a, acc, a.q + ((size_t)req * a.h_q + hq) * a.d, agent, h, len - 1, orow,
                a.rope_cos != nullptr);
 }
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(64) void lra_prefill_f32_kernel(F32K a) {
     const int g = a.h_q / a.h_kv;
     const int h = hq / g;
     const int agent = min(max(a.req_agent[req], 0), a.n_agents - 1);
-    Contig acc{&a, h};
+    Contig acc{&a, h, (size_t)agent * a.lr_stride};
     const size_t off = (((size_t)req * a.q_len + i) * a.h_q + hq) * a.d;
     row_attend(a, acc, a.q + off, agent, h, a.kv_len - a.q_len + i, a.out + off, a.rope_cos != nullptr);
 }
@@ -212,6 +219,7 @@ F32K common(const lra::DecodeArgs& d) {
     k.d = d.head_dim;
     k.r = d.rank;
     k.scale = d.scale;
+    k.lr_stride = d.lr_stride;
     return k;
 }
 
@@ -248,6 +256,7 @@ lra_status launch_prefill_f32(const PrefillArgs& p, hipStream_t s) {
     k.d = p.head_dim;
     k.r = p.rank;
     k.scale = p.scale;
+    k.lr_stride = p.lr_stride;
     const long long blocks = (long long)p.n_req * p.q_len * p.h_q;
     if (blocks == 0) return LRA_OK;
     if (blocks > 0x7fffffffLL) {

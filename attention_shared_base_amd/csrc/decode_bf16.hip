@@ -77,6 +77,7 @@ struct DecodeK {
     const float* rope_cos;  // RoPE: [rope_rows, D/2] tables of the keys' positions
     const float* rope_sin;
     int32_t rope_rows;
+    int64_t lr_stride;  // per-agent LR caches: elements between agents' pools (0: one shared cache)
 };
 
 // Persistent mode keeps the per-context item prefix sums in LDS.
@@ -106,16 +107,23 @@ template <int D, int R, int SP>
 __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
                                                int n, int cl, float (*o_out)[SP], float* L_out);
 
-template <int D, int R>
+// NQ: LR caches read per step (1 shared; 4 = one per request slot of the group)
+template <int D, int R, int NQ = 1>
 struct Step {
     static constexpr int NJ = D / 32;          // score MFMAs (dims) per page
     static constexpr int NDT = D / 16;         // value tiles (dims)
     static constexpr int NRT = (R + 15) / 16;  // value tiles (ranks)
     bf16x8 k[2][NJ];
-    bf16x8 lk[2];
+    bf16x8 lk[NQ][2];
     bf16x4 v[2][NDT];
-    bf16x4 lv[2][NRT];
+    bf16x4 lv[NQ][2][NRT];
 };
+
+// Modes of the decode kernel: the rank-r score term on the shared LR cache; the
+// adapter key rebuilt and rotated (RoPE); one LR cache per agent (the agent's
+// L_k, L_v rows for its own requests' rows, at most PA_REQ requests per group).
+constexpr int MODE_SHARED = 0, MODE_ROPE = 1, MODE_PER_AGENT = 2;
+constexpr int PA_REQ = 4;
 
 // RoPE: cos, sin of one step's keys (page t, token n16), dims 16*ht + 4*q4 .. +3
 template <int D>
@@ -125,13 +133,16 @@ struct StepRope {
 
 // WAVES wavefronts per workgroup; SPW = 32-token steps per wavefront; a
 // workgroup covers WAVES * SPW * 32 tokens.  DEPTH = step buffers per
-// wavefront (DEPTH - 1 steps of loads in flight).  ROPE: rotate the adapter
-// key term (rebuilt per request) instead of the rank-r score term.
-template <int D, int R, int SPW, int DEPTH, int WAVES, bool ROPE>
+// wavefront (DEPTH - 1 steps of loads in flight).  MODE: see MODE_SHARED ..
+template <int D, int R, int SPW, int DEPTH, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) {
-    constexpr int NJ = Step<D, R>::NJ;
-    constexpr int NDT = Step<D, R>::NDT;
-    constexpr int NRT = Step<D, R>::NRT;
+    constexpr bool ROPE = MODE == MODE_ROPE;
+    constexpr bool PA = MODE == MODE_PER_AGENT;
+    constexpr int NQ = PA ? PA_REQ : 1;
+    using StepT = Step<D, R, NQ>;
+    constexpr int NJ = StepT::NJ;
+    constexpr int NDT = StepT::NDT;
+    constexpr int NRT = StepT::NRT;
     constexpr int DR = D + R;
     constexpr int SP = DR + 1;  // LDS row pitch (odd: no bank aliasing across rows)
     constexpr int CHUNK = WAVES * SPW * KEYS_PER_STEP;
@@ -259,34 +270,50 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     const bf16* kbase = a.k_pool + (size_t)h * D * PAGE;
     const bf16* vbase = a.v_pool + (size_t)h * D * PAGE;
 
+    // agent ids of the group's first four requests: requested before the step
+    // loads, so that waiting for them does not wait for those
+    int agent0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) agent0[u] = a.req_agent[req0 + min(u, nreq - 1)];
+    // per-agent LR caches: the step loads address the agents' pools
+    int agent_of[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) agent_of[u] = PA ? min(max(agent0[u], 0), a.n_agents - 1) : 0;
+
     // Loads of one step: no data-dependent branches; dead slots are masked later.
-    auto load = [&](Step<D, R>& T, const int (&pids)[2]) {
+    auto load = [&](StepT& T, const int (&pids)[2]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const bf16* kp = kbase + (size_t)pids[t] * kv_page;
             const bf16* vp = vbase + (size_t)pids[t] * kv_page;
-            const bf16* lkp = a.lk_pool + (size_t)pids[t] * PAGE * R;
-            const bf16* lvp = a.lv_pool + (size_t)pids[t] * PAGE * R;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 T.k[t][j] = ldg_stream((const bf16x8*)(kp + ((4 * j + q4) * PAGE + n16) * 8));
-            if constexpr (R == 32) {
-                T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)),
-                               ldg((const bf16x4*)(lkp + n16 * R + 16 + 4 * q4)));
-            } else if constexpr (R == 16) {
-                T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)), zero4());
-            } else {
-                T.lk[t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * (q4 & 1))), zero4());
-                if (q4 >= 2) T.lk[t] = zero8();
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) {
+                // per-agent LR caches: request slot u reads its agent's pages
+                // (slots past the group repeat its last request; never used)
+                const size_t lr_off = PA ? (size_t)agent_of[u] * a.lr_stride : 0;
+                const bf16* lkp = a.lk_pool + lr_off + (size_t)pids[t] * PAGE * R;
+                const bf16* lvp = a.lv_pool + lr_off + (size_t)pids[t] * PAGE * R;
+                if constexpr (R == 32) {
+                    T.lk[u][t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)),
+                                      ldg((const bf16x4*)(lkp + n16 * R + 16 + 4 * q4)));
+                } else if constexpr (R == 16) {
+                    T.lk[u][t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)), zero4());
+                } else {
+                    T.lk[u][t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * (q4 & 1))), zero4());
+                    if (q4 >= 2) T.lk[u][t] = zero8();
+                }
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt) {
+                    const int rank = min(16 * rt + n16, R - 1);
+                    T.lv[u][t][rt] = ldg((const bf16x4*)(lvp + rank * PAGE + 4 * q4));
+                }
             }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 T.v[t][dt] = ldg_stream((const bf16x4*)(vp + (16 * dt + n16) * PAGE + 4 * q4));
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                const int rank = min(16 * rt + n16, R - 1);
-                T.lv[t][rt] = ldg((const bf16x4*)(lvp + rank * PAGE + 4 * q4));
-            }
         }
     };
     // RoPE tables of step i's keys: the key's position in its context is its
@@ -314,14 +341,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         }
     };
 
-    // agent ids of the group's first four requests: requested before the step
-    // loads, so that waiting for them does not wait for those
-    int agent0[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) agent0[u] = a.req_agent[req0 + min(u, nreq - 1)];
 
     // ---- the first DEPTH-1 steps' loads go out before the prologue's dependent chain
-    Step<D, R> buf[DEPTH];
+    StepT buf[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH - 1; ++i)
         if (i < NPRE) load(buf[i], pid[i]);
@@ -458,14 +480,19 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     const float sl2 = a.scale_log2;
 
     const int my_req = n16 / g;  // request (within the group) of this lane's row
-    auto compute = [&](Step<D, R>& T, int key0) {
+    auto compute = [&](StepT& T, int key0) {
         f32x4 s[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             s[t] = zf4();
 #pragma unroll
             for (int j = 0; j < NJ; ++j) s[t] = mfma16x16x32(T.k[t][j], qf[j], s[t]);
-            if constexpr (!ROPE) s[t] = mfma16x16x32(T.lk[t], qb, s[t]);
+            if constexpr (MODE == MODE_SHARED) s[t] = mfma16x16x32(T.lk[0][t], qb, s[t]);
+            if constexpr (PA) {
+                // each request slot's LR rows meet only that request's rows
+#pragma unroll
+                for (int u = 0; u < NQ; ++u) s[t] = mfma16x16x32(T.lk[u][t], my_req == u ? qb : zero8(), s[t]);
+            }
         }
         if constexpr (ROPE) {
             // adapter key term of each request: dK^T = B_k^(h)T L_k^T (lane =
@@ -486,7 +513,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                             bop = cat4(*(const bf16x4*)(bkp + tile * 64 * BKW), zero4());
                             if (R == 8 && q4 >= 2) bop = zero8();
                         }
-                        dk[tile] = mfma16x16x32(bop, T.lk[t], zf4());
+                        dk[tile] = mfma16x16x32(bop, T.lk[0][t], zf4());
                     }
 #pragma unroll
                     for (int ht = 0; ht < NDT / 2; ++ht) {
@@ -556,13 +583,21 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) T.v[t][dt] = and_mask(T.v[t][dt], keep[t][0], keep[t][1]);
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) T.lv[t][rt] = and_mask(T.lv[t][rt], keep[t][0], keep[t][1]);
+            for (int u = 0; u < NQ; ++u)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    T.lv[u][t][rt] = and_mask(T.lv[u][t][rt], keep[t][0], keep[t][1]);
         }
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            bf16x8 lvop = cat4(T.lv[0][rt], T.lv[1][rt]);
-            if (16 * rt + n16 >= R) lvop = zero8();
-            acc_lr[rt] = mfma16x16x32(lvop, pb, acc_lr[rt]);
+        for (int u = 0; u < NQ; ++u) {
+            // per-agent LR caches: request slot u's L_v rows against its rows' P only
+            const bf16x8 pu = (!PA || my_req == u) ? pb : zero8();
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                bf16x8 lvop = cat4(T.lv[u][0][rt], T.lv[u][1][rt]);
+                if (16 * rt + n16 >= R) lvop = zero8();
+                acc_lr[rt] = mfma16x16x32(lvop, pu, acc_lr[rt]);
+            }
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma16x16x32(cat4(T.v[0][dt], T.v[1][dt]), pb, acc[dt]);
@@ -586,7 +621,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         // runtime loop over step pairs (bounded registers and code size).  Loads
         // stay unconditional: past the last step they repeat it (never used).
         static_assert(DEPTH == 2 && SPW % 2 == 0, "RoPE stream: two step buffers, even step count");
-        auto rstep = [&](int i, Step<D, R>& cur, Step<D, R>& nxt) {
+        auto rstep = [&](int i, StepT& cur, StepT& nxt) {
             const int in = min(i + 1, SPW - 1);
             const int pn[2] = {page_now(in, 0), page_now(in, 1)};
             load(nxt, pn);
@@ -874,7 +909,7 @@ __device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)
     *(typename BvCols<D, R>::vec*)(a.out + ((size_t)req * a.h_q + h * g + n % g) * D + c0) = res;
 }
 
-template <int D, int R, int SPW, bool ROPE>
+template <int D, int R, int SPW, int MODE>
 lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
     constexpr int DEPTH = 2;  // one step of loads in flight per wavefront
     constexpr int W = 4;      // wavefronts per workgroup
@@ -909,6 +944,7 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.rope_cos = a.rope_cos;
     k.rope_sin = a.rope_sin;
     k.rope_rows = a.max_ctx_len;
+    k.lr_stride = a.lr_stride;
     int grid = p.grid;
     if (p.persistent) {
         // one workgroup per CU of the current device
@@ -920,19 +956,19 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
         }
         grid = min(n_cu, p.grid);
     }
-    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W, ROPE>), dim3(grid), dim3(64 * W), 0, s, k);
+    hipLaunchKernelGGL((lra_decode_bf16_kernel<D, R, SPW, DEPTH, W, MODE>), dim3(grid), dim3(64 * W), 0, s, k);
     return lra::check_launch("lra_decode_bf16_kernel");
 }
 
-template <int D, int R, bool ROPE>
+template <int D, int R, int MODE>
 lra_status launch_dr(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStream_t s) {
     // chunk = 4 wavefronts x SPW steps x 32 tokens
     switch (p.chunk) {
-        case 256: return launch_t<D, R, 2, ROPE>(a, p, s);
-        case 512: return launch_t<D, R, 4, ROPE>(a, p, s);
-        case 1024: return launch_t<D, R, 8, ROPE>(a, p, s);
-        case 2048: return launch_t<D, R, 16, ROPE>(a, p, s);
-        case 4096: return launch_t<D, R, 32, ROPE>(a, p, s);
+        case 256: return launch_t<D, R, 2, MODE>(a, p, s);
+        case 512: return launch_t<D, R, 4, MODE>(a, p, s);
+        case 1024: return launch_t<D, R, 8, MODE>(a, p, s);
+        case 2048: return launch_t<D, R, 16, MODE>(a, p, s);
+        case 4096: return launch_t<D, R, 32, MODE>(a, p, s);
         default: break;
     }
     lra::set_error("decode: unsupported chunk %d", p.chunk);
@@ -945,9 +981,16 @@ namespace lra {
 
 lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
     const int d = a.head_dim, r = a.rank;
-    const bool rope = a.rope_cos != nullptr;
-#define LRA_CASE(D_, R_) \
-    if (d == D_ && r == R_) return rope ? launch_dr<D_, R_, true>(a, p, s) : launch_dr<D_, R_, false>(a, p, s);
+    const int mode = a.rope_cos != nullptr ? MODE_ROPE : a.lr_stride != 0 ? MODE_PER_AGENT : MODE_SHARED;
+    if (a.rope_cos != nullptr && a.lr_stride != 0) {
+        set_error("decode: RoPE on the adapter key with per-agent LR caches is not supported");
+        return LRA_ERR_UNSUPPORTED;
+    }
+#define LRA_CASE(D_, R_)                                                                   \
+    if (d == D_ && r == R_)                                                                \
+        return mode == MODE_ROPE ? launch_dr<D_, R_, MODE_ROPE>(a, p, s)                   \
+               : mode == MODE_PER_AGENT ? launch_dr<D_, R_, MODE_PER_AGENT>(a, p, s)       \
+                                        : launch_dr<D_, R_, MODE_SHARED>(a, p, s);
     LRA_CASE(128, 16)
     LRA_CASE(128, 32)
     LRA_CASE(128, 8)

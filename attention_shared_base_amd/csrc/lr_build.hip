@@ -6,6 +6,11 @@
 // one product serves every agent.  Here both the key and the value
 // down-projections are applied in one pass over X:  [L_k | L_v] = X [A_k | A_v].
 //
+// With one A per agent (PReCache PreLRShared with per-agent adapters, LRAgent
+// §3 BaseShared) the same launch builds every agent's cache, X [A_1 .. A_n]:
+// workgroups of neighbouring indices take the same 16 tokens for successive
+// agents, so X is read from HBM about once and reused from the caches.
+//
 // The product is tall and skinny (d_model x 2r with 2r <= 64) and bound by
 // reading X once from HBM.  A workgroup owns 16 tokens; its 8 wavefronts take
 // interleaved 32-wide slices of d_model (so together they stream each X row
@@ -29,7 +34,8 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
                                                                 bf16* __restrict__ l_k,
                                                                 bf16* __restrict__ l_v,
                                                                 int n_tok, int d_model,
-                                                                long long row_offset) {
+                                                                long long row_offset, int n_lr,
+                                                                long long lr_stride) {
     constexpr int NT = 2 * R / 16;  // 16-column output tiles (R = 8, 16, 32)
     constexpr int NC = NT * 16;
     constexpr int BATCH = R == 32 ? 8 : 16;  // k-slices per wavefront in flight
@@ -38,7 +44,12 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int tok0 = blockIdx.x * TOK;
+    const int ag = blockIdx.x % n_lr;  // whose A / LR cache
+    const int tok0 = (blockIdx.x / n_lr) * TOK;
+    a_k += (size_t)ag * R * d_model;
+    a_v += (size_t)ag * R * d_model;
+    l_k += (size_t)ag * lr_stride;
+    l_v += (size_t)ag * lr_stride;
 
     // rows past n_tok read a valid row; their results are never stored
     const bf16* xp = x + (size_t)min(tok0 + l16, n_tok - 1) * d_model + 8 * kq;
@@ -58,7 +69,7 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
     // all of A_k and A_v; each starts at its own slice offset so that they do
     // not all request the same A lines (one L2 channel) at once.
     const int n_steps = d_model / 32;
-    const int rot = (int)((blockIdx.x * 16u) % (unsigned)n_steps) & ~1;
+    const int rot = (int)(((blockIdx.x / n_lr) * 16u) % (unsigned)n_steps) & ~1;
     for (int s0 = 2 * wave; s0 < n_steps; s0 += BATCH * WAVES) {
         bf16x8 xa[BATCH], wb[BATCH][NT];
 #pragma unroll
@@ -101,9 +112,15 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
 __global__ void lra_lr_build_f32_kernel(const float* __restrict__ x, const float* __restrict__ a_k,
                                         const float* __restrict__ a_v, float* __restrict__ l_k,
                                         float* __restrict__ l_v, int n_tok, int d_model, int r,
-                                        long long row_offset) {
-    const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (long long)n_tok * 2 * r) return;
+                                        long long row_offset, int n_lr, long long lr_stride) {
+    long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (long long)n_tok * 2 * r * n_lr) return;
+    const int ag = (int)(e / ((long long)n_tok * 2 * r));
+    e %= (long long)n_tok * 2 * r;
+    a_k += (size_t)ag * r * d_model;
+    a_v += (size_t)ag * r * d_model;
+    l_k += (size_t)ag * lr_stride;
+    l_v += (size_t)ag * lr_stride;
     const int t = (int)(e / (2 * r)), c = (int)(e % (2 * r));
     const float* w = c < r ? a_k + (size_t)c * d_model : a_v + (size_t)(c - r) * d_model;
     const float* xr = x + (size_t)t * d_model;
@@ -130,27 +147,38 @@ namespace lra {
 
 lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
     if (a.n_tok == 0) return LRA_OK;
-    const dim3 grid((a.n_tok + TOK - 1) / TOK), block(64 * WAVES);
+    const long long nb = (long long)(a.n_tok + TOK - 1) / TOK * a.n_lr;
+    if (nb > 0x7fffffffLL) {
+        set_error("lr build: grid of %lld workgroups too large", nb);
+        return LRA_ERR_BAD_SHAPE;
+    }
+    const dim3 grid((unsigned)nb), block(64 * WAVES);
+    const long long ro = (long long)a.row_offset, ls = (long long)a.lr_stride;
     const bf16* x = (const bf16*)a.x;
     const bf16* ak = (const bf16*)a.a_k;
     const bf16* av = (const bf16*)a.a_v;
     bf16* lk = (bf16*)a.l_k;
     bf16* lv = (bf16*)a.l_v;
     switch (a.rank) {
-        case 8: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<8>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, (long long)a.row_offset); break;
-        case 16: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<16>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, (long long)a.row_offset); break;
-        case 32: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<32>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, (long long)a.row_offset); break;
+        case 8: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<8>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
+        case 16: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<16>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
+        case 32: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<32>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
         default: set_error("lr build: unsupported rank %d", a.rank); return LRA_ERR_UNSUPPORTED;
     }
     return check_launch("lra_lr_build_bf16_kernel");
 }
 
 lra_status launch_lr_build_f32(const LRBuildArgs& a, hipStream_t s) {
-    const long long n = (long long)a.n_tok * 2 * a.rank;
+    const long long n = (long long)a.n_tok * 2 * a.rank * a.n_lr;
     if (n == 0) return LRA_OK;
+    if ((n + 255) / 256 > 0x7fffffffLL) {
+        set_error("lr build f32: %lld outputs too many", n);
+        return LRA_ERR_BAD_SHAPE;
+    }
     hipLaunchKernelGGL(lra_lr_build_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        (const float*)a.x, (const float*)a.a_k, (const float*)a.a_v, (float*)a.l_k,
-                       (float*)a.l_v, a.n_tok, a.d_model, a.rank, (long long)a.row_offset);
+                       (float*)a.l_v, a.n_tok, a.d_model, a.rank, (long long)a.row_offset, a.n_lr,
+                       (long long)a.lr_stride);
     return check_launch("lra_lr_build_f32_kernel");
 }
 

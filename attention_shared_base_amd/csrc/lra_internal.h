@@ -55,6 +55,7 @@ struct DecodeArgs {
     int32_t n_req, n_ctx, n_pages, max_blocks, max_ctx_len, n_agents;
     int32_t h_q, h_kv, head_dim, rank;
     float scale;
+    int64_t lr_stride;  // elements between agents' LR pools (0: one shared LR cache)
 };
 
 lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
@@ -75,6 +76,7 @@ struct PrefillArgs {
     int32_t n_req, q_len, kv_len, n_agents;
     int32_t h_q, h_kv, head_dim, rank;
     float scale;
+    int64_t lr_stride;  // elements between agents' LR caches (0: one shared LR cache)
 };
 
 lra_status launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
@@ -88,12 +90,12 @@ lra_status launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 // ----------------------------------------------------------------- LR build
 struct LRBuildArgs {
     const void* x;
-    const void* a_k;
+    const void* a_k;  // [n_lr, rank, d_model]
     const void* a_v;
-    void* l_k;
+    void* l_k;        // agent a's rows at a * lr_stride
     void* l_v;
-    int32_t n_tok, d_model, rank;
-    int64_t row_offset;
+    int32_t n_tok, d_model, rank, n_lr;
+    int64_t row_offset, lr_stride;
 };
 
 lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s);

@@ -68,6 +68,7 @@ struct PrefillK {
     bf16* out;
     int32_t n_req, q_len, kv_len, n_agents, h_q, h_kv, g, n_qblk;
     float scale_log2;
+    int64_t lr_stride;  // per-agent LR caches: elements between agents' caches (0: shared)
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -169,6 +170,9 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     const int q_len = a.q_len, kv_len = a.kv_len;
     int agent = a.req_agent[req];
     agent = min(max(agent, 0), a.n_agents - 1);
+    // the LR cache this request reads: the shared one, or its agent's
+    const bf16* lk_ag = a.l_k + (size_t)agent * a.lr_stride;
+    const bf16* lv_ag = a.l_v + (size_t)agent * a.lr_stride;
 
     // this lane's row: token tok (chunk-local), query head h*g + (n32 % g)
     const int tok = tok_wg + wave * TW + n32 / g;
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) dma_1k(rk, smem_lds + OFF_K + b * TK + (wave + WAVES * u) * KBS, voff_row[u]);
         if (wave < RCH)
-            dma_1k(make_rsrc(a.l_k + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LK + b * TLK + wave * 1024,
+            dma_1k(make_rsrc(lk_ag + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LK + b * TLK + wave * 1024,
                    voff_l + 16 * wave);
         if constexpr (ROPE) {
             const auto rc = make_rsrc(a.rope_cos + (size_t)key0 * (D / 2), rem * RB);
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         for (int u = 0; u < NU; ++u) dma_1k(rv, smem_lds + OFF_V + b * TV + (wave + WAVES * u) * VBS, voff_row[u]);
         const int c = wave - 4;
         if (c >= 0 && c < RCH)
-            dma_1k(make_rsrc(a.l_v + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LV + b * TLV + c * VBS,
+            dma_1k(make_rsrc(lv_ag + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LV + b * TLV + c * VBS,
                    voff_l + 16 * c);
     };
 
@@ -620,6 +624,7 @@ lra_status launch_t(const lra::PrefillArgs& p, hipStream_t s) {
     const int tw = 32 / k.g;
     k.n_qblk = (p.q_len + WAVES * tw - 1) / (WAVES * tw);
     k.scale_log2 = p.scale * LRA_LOG2E;
+    k.lr_stride = p.lr_stride;
     // tiles are addressed through 32-bit buffer ranges of kv_len rows of 2*D bytes
     if ((long long)p.kv_len * 2 * D > 0x7fffffffLL) {
         lra::set_error("prefill: kv_len %d too long for 32-bit tile addressing", p.kv_len);

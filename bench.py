@@ -167,7 +167,7 @@ class DecodeSet:
         self.out = None
 
 
-def primary_decode(steps, warmup, n_sets, rope_theta=None):
+def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False):
     import torch
     import attention_shared_base_amd as lra
     import workloads as w
@@ -178,10 +178,17 @@ def primary_decode(steps, warmup, n_sets, rope_theta=None):
     max_len = int(c0.ctx_len.max())
     ws = torch.zeros(lra.decode_workspace_size(
         n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=c0.n_req,
-        n_ctx=c0.n_ctx, max_req_per_ctx=mrpc, max_ctx_len=max_len), dtype=torch.uint8,
-        device="cuda")
+        n_ctx=c0.n_ctx, max_req_per_ctx=mrpc, max_ctx_len=max_len,
+        lr_agent_stride=1 if per_agent else 0), dtype=torch.uint8, device="cuda")
     for s in sets:
         s.out = torch.empty_like(s.q)
+        if per_agent:
+            # one LR cache per agent (BaseShared): the agents' pools, own draws
+            g = torch.Generator(device="cuda")
+            g.manual_seed(11)
+            n_ag = s.b_k.shape[0]
+            s.lk = _randn_bf16((n_ag,) + tuple(s.lk.shape), 1.0, g)
+            s.lv = _randn_bf16((n_ag,) + tuple(s.lv.shape), 1.0, g)
     cos = sin = None
     if rope_theta is not None:
         cos, sin = lra.rope_table(rope_theta, 128, max_len)
@@ -196,6 +203,9 @@ def primary_decode(steps, warmup, n_sets, rope_theta=None):
     nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, 16)
     if rope_theta is not None:
         nbytes += 2 * max_len * 64 * 4  # the cos / sin rows, read once
+    if per_agent:  # every agent of a context reads its own L_k, L_v rows
+        n_ag_ctx = len(np.unique(c0.req_agent[c0.req_ctx == 0]))
+        nbytes += int(c0.ctx_len.sum()) * 2 * 16 * 2 * (n_ag_ctx - 1)
     return cases[0], ms, nbytes
 
 
@@ -251,6 +261,22 @@ def extra_decode_rope(steps, warmup, base_ms):
                     "contexts, Hq32 Hkv8 d128 r16, theta 5e5, bf16",
         "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
         "time_vs_no_rope": ms / base_ms,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "algorithmic_bytes": nbytes,
+    }
+
+
+def extra_decode_per_agent(steps, warmup, base_ms):
+    """The primary decode workload with one LR cache per agent (BaseShared / PreLRShared with
+    per-agent A): each request reads its agent's L_k, L_v pages beside the shared base pages."""
+    case, ms, nbytes = primary_decode(steps, warmup, 4, per_agent=True)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "decode with one LR cache per agent: 16 requests over 4 shared 8192-token "
+                    "contexts (4 agents each), Hq32 Hkv8 d128 r16, bf16",
+        "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+        "time_vs_shared_lr": ms / base_ms,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
         "algorithmic_bytes": nbytes,
@@ -494,8 +520,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="decode_rope,naive_decode,prefill_rope,prefill_paged,"
-                                       "paged_decode,lr_build,prelr_step",
+    ap.add_argument("--extra", default="decode_rope,decode_per_agent,naive_decode,prefill_rope,"
+                                       "prefill_paged,paged_decode,lr_build,prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -526,6 +552,7 @@ def main():
     extra = {}
     if not args.no_extra:
         legs = {"decode_rope": lambda: extra_decode_rope(args.steps, args.warmup, ms),
+                "decode_per_agent": lambda: extra_decode_per_agent(args.steps, args.warmup, ms),
                 "naive_decode": lambda: extra_naive_decode(max(5, args.steps // 10), 3, ms),
                 "prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
                 "prefill_paged": lambda: extra_prefill_paged(

@@ -71,6 +71,14 @@ typedef struct lra_dims {
     int32_t rank;        /* r: 8, 16 or 32 */
     int32_t dtype;       /* LRA_F32 or LRA_BF16, for every tensor of the call */
     float softmax_scale; /* <= 0 selects 1/sqrt(head_dim) */
+    /* 0: one LR cache shared by every agent (BaseLRShared, shared A).  > 0: one
+     * LR cache per agent (BaseShared, or PreLRShared with per-agent A; LRAgent
+     * §3, PReCache): agent a's L_k / L_v start lr_agent_stride elements after
+     * agent a-1's, in l_k / l_v of lra_attn_prefill and lk_pool / lv_pool of
+     * lra_attn_decode (which then packs at most 4 requests per row group and
+     * does not combine it with RoPE).  The paged prefill, the cache append and
+     * the naive baseline take 0 only. */
+    int64_t lr_agent_stride;
 } lra_dims;
 
 /* ABI version of the loaded library (LRA_ABI_VERSION it was built with). */
@@ -232,20 +240,27 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
                             void* k_pool, void* v_pool, void* lk_pool, void* lv_pool,
                             int32_t n_pages, int32_t page_size, void* stream);
 /*
- * Shared low-rank cache rows for new tokens (PReCache PreLRShared; LRAgent §3
+ * Low-rank cache rows for new tokens (PReCache PreLRShared; LRAgent §3
  * BaseLRShared with shared A):  L_k[row_offset + i] = x[i] A_k,
- * L_v[row_offset + i] = x[i] A_v  for i < n_tok, i.e. L = X A.
+ * L_v[row_offset + i] = x[i] A_v  for i < n_tok, i.e. L = X A.  With n_lr > 1
+ * (one A per agent: BaseShared, or PreLRShared with per-agent adapters) one
+ * call builds every agent's cache, X [A_1 .. A_n]: agent a's rows go to
+ * l_k + a * lr_agent_stride (the layout lra_dims.lr_agent_stride describes).
  *
  *   x          [n_tok, d_model]   device
- *   a_k, a_v   [rank, d_model]    device: the down-projections stored as
+ *   a_k, a_v   [n_lr, rank, d_model] device: the down-projections stored as
  *              out x in (row t is column t of A), the usual layout of a LoRA
  *              "A" weight
- *   l_k, l_v   [>= row_offset + n_tok, rank], rows written in place  device
+ *   n_lr       number of LR caches (1: shared A)
+ *   l_k, l_v   n_lr blocks lr_agent_stride elements apart (ignored for
+ *              n_lr = 1), each [>= row_offset + n_tok, rank]; rows written in
+ *              place  device
  *   Requires d_model % 32 == 0.  bf16 results are rounded to nearest even.
  */
 lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,
-                              const void* a_k, const void* a_v, int32_t rank,
-                              void* l_k, void* l_v, int64_t row_offset, void* stream);
+                              const void* a_k, const void* a_v, int32_t rank, int32_t n_lr,
+                              void* l_k, void* l_v, int64_t row_offset,
+                              int64_t lr_agent_stride, void* stream);
 
 /*
  * RoPE tables for prefill and decode: cos/sin of pos * theta^(-2i/d), pos in

@@ -256,7 +256,11 @@ def decode_paged(q, req_ctx, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
     ``q`` ``[n_req, H_q, d]``; request ``i`` reads context ``req_ctx[i]`` (its
     base and LR pages) with agent ``req_agent[i]``'s ``B_k``/``B_v``
     (``b_k``, ``b_v``: ``[n_agents, r, H_kv*d]``).  The newest token is part of
-    the context, so the query sees all ``ctx_len[c]`` keys.  ``rope`` is
+    the context, so the query sees all ``ctx_len[c]`` keys.  ``lk_pool`` /
+    ``lv_pool`` are one LR pool shared by every agent (BaseLRShared, LRAgent §3)
+    or, with a leading agent axis, one LR pool per agent (BaseShared: each agent
+    keeps its own A and so its own LR cache); request ``i`` then reads agent
+    ``req_agent[i]``'s pool through the same block table.  ``rope`` is
     ``(cos, sin)`` ``[>= max ctx_len, d/2]``: the adapter key term of the key at
     token index ``j`` of a context is rotated by row ``j`` (App. D.1, as in
     prefill).  ``requests`` optionally restricts which requests are evaluated
@@ -269,8 +273,10 @@ def decode_paged(q, req_ctx, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
     for i in idx:
         c, a = int(req_ctx[i]), int(req_agent[i])
         n = int(ctx_len[c])
-        kb, lk = gather_pages(k_pool, lk_pool, block_table[c], n)
-        vb, lv = gather_pages(v_pool, lv_pool, block_table[c], n)
+        lkp = lk_pool[a] if np.ndim(lk_pool) == 4 else lk_pool
+        lvp = lv_pool[a] if np.ndim(lv_pool) == 4 else lv_pool
+        kb, lk = gather_pages(k_pool, lkp, block_table[c], n)
+        vb, lv = gather_pages(v_pool, lvp, block_table[c], n)
         out[i] = attention_materialised(q[i][None], kb, vb, lk, lv, _f64(b_k[a]), _f64(b_v[a]),
                                         q_pos=[n - 1], rope=rope, scale=scale)[0]
     return out
@@ -282,9 +288,11 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope=None, scal
 
     ``q`` ``[n_req, q_len, H_q, d]``; the new tokens are the last ``q_len`` of
     the ``kv_len`` cached tokens (their base and LR rows are already in the
-    caches), attended causally.  ``rows`` optionally selects the chunk-local
-    query indices to evaluate (same for every request); the result then has
-    ``len(rows)`` rows per request.
+    caches), attended causally.  ``l_k`` / ``l_v`` are ``[kv_len, r]`` (shared)
+    or ``[n_agents, kv_len, r]`` (one LR cache per agent, LRAgent §3
+    BaseShared).  ``rows`` optionally selects the chunk-local query indices to
+    evaluate (same for every request); the result then has ``len(rows)`` rows
+    per request.
     """
     q = _f64(q)
     n_req, q_len, h_q, d = q.shape
@@ -294,7 +302,9 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope=None, scal
     out = np.empty((n_req, len(rows), h_q, d))
     for i in range(n_req):
         a = int(req_agent[i])
-        out[i] = attention_materialised(q[i, rows], k_base, v_base, l_k, l_v,
+        lk = l_k[a] if np.ndim(l_k) == 3 else l_k
+        lv = l_v[a] if np.ndim(l_v) == 3 else l_v
+        out[i] = attention_materialised(q[i, rows], k_base, v_base, lk, lv,
                                         _f64(b_k[a]), _f64(b_v[a]),
                                         q_pos=kv_len - q_len + rows, rope=rope,
                                         scale=scale, row_chunk=row_chunk)

@@ -82,13 +82,15 @@ class DecodeDev:
             self._rope[theta] = lra.rope_table(theta, self.case.d, max(self.max_ctx_len, 1))
         return self._rope[theta]
 
-    def run(self, out=None, workspace=None, b_k=None, b_v=None, q=None, rope_theta=None):
+    def run(self, out=None, workspace=None, b_k=None, b_v=None, q=None, rope_theta=None, lk=None,
+            lv=None):
         import attention_shared_base_amd as lra
         cos = sin = None
         if rope_theta is not None:
             cos, sin = self.rope(rope_theta)
         return lra.decode(self.q if q is None else q, self.crs, self.agent, self.k, self.v,
-                          self.lk, self.lv, self.bt, self.clen,
+                          self.lk if lk is None else lk, self.lv if lv is None else lv,
+                          self.bt, self.clen,
                           self.b_k if b_k is None else b_k, self.b_v if b_v is None else b_v,
                           max_req_per_ctx=self.max_req_per_ctx, max_ctx_len=self.max_ctx_len,
                           rope_cos=cos, rope_sin=sin, out=out, workspace=workspace)

@@ -88,6 +88,8 @@ def call_decode(dm, **over):
     (dims(), {"ws_bytes": 1}, 5),
     (dims(), {"ws": None}, 1),
     (dims(), {"cos": A}, 1),                 # rope tables go in pairs
+    (lra.Dims(32, 8, 128, 16, 1, 0.0, -1), {}, 2),   # negative LR stride
+    (lra.Dims(32, 8, 128, 16, 1, 0.0, 4096), {"cos": A, "sin": A}, 3),  # per-agent LR + RoPE
     (dims(), {"cos": A, "sin": ctypes.c_void_p(0x100004)}, 4),
 ])
 def test_decode_validation(dm, over, want):
@@ -136,10 +138,11 @@ def test_lr_build_validation():
     lib = lra.load()
 
     def call(**o):
-        a = dict(dt=1, x=A, n_tok=16, d_model=4096, ak=A, av=A, r=16, lk=A, lv=A, off=0)
+        a = dict(dt=1, x=A, n_tok=16, d_model=4096, ak=A, av=A, r=16, n_lr=1, lk=A, lv=A, off=0,
+                 ls=0)
         a.update(o)
         return lib.lra_lr_cache_build(a["dt"], a["x"], a["n_tok"], a["d_model"], a["ak"], a["av"],
-                                      a["r"], a["lk"], a["lv"], a["off"], None)
+                                      a["r"], a["n_lr"], a["lk"], a["lv"], a["off"], a["ls"], None)
 
     assert call(r=12) == 3
     assert call(dt=5) == 3
@@ -150,6 +153,9 @@ def test_lr_build_validation():
     assert call(x=None) == 1
     assert call(av=ctypes.c_void_p(0x100002)) == 4
     assert call(n_tok=0) == 0
+    assert call(n_lr=0) == 2
+    assert call(n_lr=4, ls=16 * 16 - 1) == 2      # agents' caches would overlap
+    assert call(n_lr=4, ls=16 * 16, n_tok=0) == 0
 
 
 def test_rope_table_validation():

@@ -375,3 +375,36 @@ def test_decode_rope_matches_brute_force():
     # the rotation matters here: without it the result moves
     plain = ref.decode_paged(q, req_ctx, req_agent, kp, vp, lkp, lvp, table, lens, b_k, b_v)
     assert np.max(np.abs(plain - got)) > 1e-3
+
+
+def test_per_agent_lr_caches_match_brute_force():
+    """BaseShared (LRAgent §3): each agent has its own A, hence its own LR cache.  Decode and
+    prefill with per-agent LR pools equal the brute force run with each request's own L;
+    with one cache repeated for every agent they equal the shared-cache result."""
+    from workloads import paginate
+    rng = np.random.default_rng(71)
+    h_q, h_kv, d, r, L, n_ag = 4, 2, 8, 2, 29, 3
+    c = rand_case(72, n_rows=1, h_q=h_q, h_kv=h_kv, d=d, r=r, kv_len=L)
+    lk = rng.standard_normal((n_ag, L, r))
+    lv = rng.standard_normal((n_ag, L, r))
+    b_k = 0.5 * rng.standard_normal((n_ag, r, h_kv * d))
+    b_v = 0.5 * rng.standard_normal((n_ag, r, h_kv * d))
+    q = rng.standard_normal((3, h_q, d))
+    agents = [2, 0, 1]
+    ids = rng.permutation(2)
+    kp, _ = paginate(c["k_base"], lk[0], ids, 2, 16)
+    vp, _ = paginate(c["v_base"], lv[0], ids, 2, 16)
+    lkp = np.stack([paginate(c["k_base"], lk[a], ids, 2, 16)[1] for a in range(n_ag)])
+    lvp = np.stack([paginate(c["v_base"], lv[a], ids, 2, 16)[1] for a in range(n_ag)])
+    dec = ref.decode_paged(q, [0, 0, 0], agents, kp, vp, lkp, lvp, ids[None], [L], b_k, b_v)
+    pre = ref.prefill(q[:, None], agents, c["k_base"], c["v_base"], lk, lv, b_k, b_v)
+    for i, a in enumerate(agents):
+        want = np.array(brute_attention(q[i][None].tolist(), c["k_base"].tolist(),
+                                        c["v_base"].tolist(), lk[a].tolist(), lv[a].tolist(),
+                                        b_k[a].tolist(), b_v[a].tolist(), q_pos=[L - 1]))[0]
+        assert np.max(np.abs(dec[i] - want)) < 1e-12
+        assert np.max(np.abs(pre[i, 0] - want)) < 1e-12
+    same = ref.decode_paged(q, [0, 0, 0], agents, kp, vp, np.stack([lkp[1]] * n_ag),
+                            np.stack([lvp[1]] * n_ag), ids[None], [L], b_k, b_v)
+    shared = ref.decode_paged(q, [0, 0, 0], agents, kp, vp, lkp[1], lvp[1], ids[None], [L], b_k, b_v)
+    assert np.array_equal(same, shared)
