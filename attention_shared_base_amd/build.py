@@ -19,8 +19,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "liblra_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.hip", "decode_bf16.hip", "prefill_bf16.hip", "attn_f32.hip", "lr_build.hip",
-           "naive_expand.hip", "paged.hip"]
+SOURCES = ["api.hip", "decode_bf16.hip", "decode_rope_bf16.hip", "prefill_bf16.hip", "attn_f32.hip",
+           "lr_build.hip", "naive_expand.hip", "paged.hip"]
+# per-source extra flags: the RoPE decode keeps MFMA results in VGPRs (its rotation
+# reads them on the VALU)
+EXTRA_FLAGS = {"decode_rope_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -56,7 +59,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *CFLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+        cmds.append([hipcc, *CFLAGS, *EXTRA_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
                      os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:

@@ -124,7 +124,8 @@ def _time_calls(fn, n_sets, steps, warmup):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16__decode_4ctx_x_8192_r16__hbm_traffic.txt")
-TRAFFIC_SOURCES = ("attention_shared_base_amd/csrc/decode_bf16.hip", "attention_shared_base_amd/csrc/api.hip")
+TRAFFIC_SOURCES = ("attention_shared_base_amd/csrc/decode_kernel.h", "attention_shared_base_amd/csrc/decode_bf16.hip",
+                   "attention_shared_base_amd/csrc/api.hip")
 
 
 def measured_traffic():
