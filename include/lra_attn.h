@@ -108,6 +108,10 @@ const char* lra_last_error(void);
  *   v_pool         [n_pages, H_kv, d, page_size]           device (dim-major)
  *   lk_pool        [n_pages, page_size, r]                 device
  *   lv_pool        [n_pages, r, page_size]                 device (rank-major)
+ *                  With dims->lr_agent_stride > 0 these are n_agents pools
+ *                  lr_agent_stride elements apart (stride >= n_pages *
+ *                  page_size * r), agent a's at a * lr_agent_stride; request
+ *                  i reads req_agent[i]'s pool through the same block table.
  *   block_table    [n_ctx, max_blocks] int32               device
  *                  logical token t of context c is in page
  *                  block_table[c][t / page_size], slot t % page_size; the base
@@ -173,7 +177,9 @@ lra_status lra_attn_decode(const lra_dims* dims,
  *   req_agent  [n_req] int32 in [0, n_agents)  device
  *   k_base     [H_kv, kv_len, d]               device
  *   v_base     [H_kv, kv_len, d]               device
- *   l_k, l_v   [kv_len, r]                     device
+ *   l_k, l_v   [kv_len, r]                     device; with
+ *              dims->lr_agent_stride > 0, one [kv_len, r] cache per agent,
+ *              agent a's at a * lr_agent_stride elements
  *   b_k, b_v   [n_agents, r, H_kv * d]         device
  *   rope_cos,
  *   rope_sin   NULL (no rotation of the adapter key term) or both
