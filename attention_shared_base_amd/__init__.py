@@ -16,7 +16,7 @@ import os
 __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
-    "prefill_paged", "cache_append",
+    "prefill_paged", "prefill_paged_workspace_size", "cache_append",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -342,6 +342,12 @@ def naive_decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, 
     return decode(q, sc["crs"], sc["agent0"], sc["k"], sc["v"], sc["lk"], sc["lv"], sc["bt"],
                   sc["len"], sc["bz"], sc["bz"], max_req_per_ctx=1, max_ctx_len=max_ctx_len,
                   out=sc["out"], workspace=sc["ws"], softmax_scale=softmax_scale, stream=stream)
+
+
+def prefill_paged_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, kv_len):
+    """Bytes of workspace ``prefill_paged`` needs for a context of ``kv_len`` tokens (bf16)."""
+    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, LRA_BF16, 0.0)
+    return int(load().lra_attn_prefill_paged_workspace_size(ctypes.byref(dims), kv_len))
 
 
 def prefill_paged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len, b_k,

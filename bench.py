@@ -378,8 +378,9 @@ def extra_prefill_paged(steps, warmup, base_ms):
             bt=torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32)))
     agent = _dev(np.arange(4, dtype=np.int32))
     cos, sin = lra.rope_table(500000.0, d, kv_len)
-    ws = torch.empty(2 * h_kv * kv_len * d * 2 + 2 * kv_len * r * 2 + 4096, dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(lra.prefill_paged_workspace_size(n_q_heads=h_q, n_kv_heads=h_kv, head_dim=d,
+                                                      rank=r, kv_len=kv_len),
+                     dtype=torch.uint8, device="cuda")
     for s in sets:
         s["out"] = torch.empty_like(s["q"])
 
