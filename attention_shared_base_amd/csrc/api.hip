@@ -114,7 +114,8 @@ bool decode_plan(const lra_dims& d, int n_req, int n_ctx, int max_req_per_ctx, i
     // per-context prefix sums in LDS.
     const int per = env_int("LRA_DECODE_PERSISTENT", -1);
     p->persistent = p->n_split > 1 && n_ctx <= 1024 && (per == 1 || (per != 0 && wgs > 4 * 256));
-    const int dr2 = d.head_dim + d.rank + 2;
+    // partial row: [O_base | O_lr], then (m, l) padded to 16 bytes
+    const int dr2 = d.head_dim + d.rank + 4;
     // per-unit merge counters, then the queue head and the workgroups-done count
     p->ws_counter_bytes = ((size_t)(p->n_units + 2) * sizeof(int32_t) + 255) / 256 * 256;
     p->ws_part_bytes = p->n_split > 1 ? (size_t)p->n_units * p->n_split * 16 * dr2 * sizeof(float) : 0;

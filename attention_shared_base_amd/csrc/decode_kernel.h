@@ -106,9 +106,19 @@ __device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)
                                               int n, int cl, int nrows, int req0, int h,
                                               const BvCols<D, R>& bv);
 
+// cache-policy bit sc1 of buffer loads/stores (agent-coherent, as the
+// agent-scope atomic loads/stores the compiler emits); s_waitcnt immediate for
+// vmcnt(0) with the other counters left unconstrained
+constexpr int CPOL_SC1 = 16;
+constexpr int WAITCNT_VMCNT0 = 0x0f70;
+// 16-byte groups per partial row ([O_base | O_lr], then (m, l)) handled by each
+// of the 16 threads of a row
+template <int DR>
+constexpr int MERGE_NG = (DR / 4 + 1 + 15) / 16;
+
 template <int D, int R, int SP>
-__device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
-                                               int n, int cl, float (*o_out)[SP], float* L_out);
+__device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int own, int n_active, int nrows,
+                                               int n, int cl, float (*o)[SP], float* M_row, float* L_row);
 
 // NQ: LR caches read per step (1 shared; 4 = one per request slot of the group)
 template <int D, int R, int NQ = 1>
@@ -166,6 +176,10 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     __shared__ float sm_M[ROWS];
     __shared__ float sm_L[ROWS];
     __shared__ int sm_last;
+    // agent ids of the row group's requests.  Every thread writes every entry
+    // (the same uniform values), so each thread reads back its own writes and
+    // no barrier is needed between the prologue and the epilogue's reads.
+    __shared__ int sm_agent[ROWS];
     __shared__ int sm_pref[MAX_CTX_PERSISTENT + 1];
     __shared__ int sm_item;
 
@@ -398,6 +412,8 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
             for (int u = 0; u < 4; ++u) agent[u] = s0 == 0 ? agent0[u] : a.req_agent[req0 + min(s0 + u, nreq - 1)];
             asm volatile("" ::"s"(agent[0]), "s"(agent[1]), "s"(agent[2]), "s"(agent[3]));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sm_agent[s0 + u] = agent[u];  // s0 + u < 16: s0 < nreq <= 16
             bf16x8 raw[4][PPT];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -439,6 +455,8 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
         for (int u = 0; u < 4; ++u) agent[u] = s0 == 0 ? agent0[u] : a.req_agent[req0 + min(s0 + u, nreq - 1)];
         asm volatile("" ::"s"(agent[0]), "s"(agent[1]), "s"(agent[2]), "s"(agent[3]));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sm_agent[s0 + u] = agent[u];  // s0 + u < 16: s0 < nreq <= 16
         bf16x8 bk[4][NRT][NJ];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -688,43 +706,59 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         }
     }
 
-    // B_v^(h) columns of this thread's output row, fetched now: they are needed
-    // only by the workgroup that finalizes, but their latency then overlaps the
-    // partial stores and the counter round trip instead of following them.
+    // B_v^(h) columns of this thread's output row (agent ids from LDS, so one
+    // memory round trip).  Only the workgroup that finalizes the unit needs
+    // them: the merging one requests them together with the partials.
     BvCols<D, R> bvc;
-    if (n < nrows) {
-        int agent = a.req_agent[req0 + n / g];
-        agent = min(max(agent, 0), a.n_agents - 1);
-        const bf16* bv = a.b_v + (size_t)agent * R * a.h_kv * D + (size_t)h * D + cl * (D / 16);
+    auto load_bv = [&]() {
+        if (n < nrows) {
+            const int agent = min(max(sm_agent[n / g], 0), a.n_agents - 1);
+            const bf16* bv = a.b_v + (size_t)agent * R * a.h_kv * D + (size_t)h * D + cl * (D / 16);
 #pragma unroll
-        for (int t = 0; t < R; ++t)
-            bvc.r[t] = ldg((const typename BvCols<D, R>::vec*)(bv + (size_t)t * a.h_kv * D));
-    }
+            for (int t = 0; t < R; ++t)
+                bvc.r[t] = ldg((const typename BvCols<D, R>::vec*)(bv + (size_t)t * a.h_kv * D));
+        }
+    };
 
     if (n_active > 1) {
         // ---- partial row -> workspace; the last workgroup of the unit merges.
         //
-        // Cross-workgroup protocol without an L2 write-back: partials are
-        // written and read as agent-scope relaxed atomics (coherent across the
-        // XCDs' L2s), the workgroup-scope release waits until every store of
-        // this wavefront has completed at that coherence level, the barrier
-        // extends that to the whole workgroup, and only then is the counter
-        // bumped.  The workgroup that sees the count reach n_active - 1 reads
-        // every partial back with agent-scope loads.  (An agent-scope release
-        // fence instead would write back the whole L2 once per workgroup,
-        // which serialises across the GPU.)
+        // Cross-workgroup protocol without an L2 write-back.  Partial rows are
+        // written with stores that carry the agent-coherence bit (sc1, what
+        // agent-scope atomic stores use), and every wavefront waits until its
+        // stores have completed (vmcnt(0): the store acknowledgements) before
+        // the barrier; only then is the unit's counter bumped.  The workgroup
+        // that sees the count reach n_active - 1 reads the other partials with
+        // sc1 loads (agent-coherent, as agent-scope atomic loads).  A
+        // workgroup-scope release would not wait for the acknowledgements, and
+        // an agent-scope release would write back the whole L2 once per
+        // workgroup, which serialises across the GPU.
+        constexpr int PW = DR + 4;
+        // buffer descriptors must be wave-uniform (scalar registers): a
+        // per-lane base makes the compiler loop over the distinct values
+        // ("waterfall"), so the row goes into the per-lane offset
+        const int unit_s = __builtin_amdgcn_readfirstlane(unit);
+        const int split_s = __builtin_amdgcn_readfirstlane(split);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            a.ws_part + ((size_t)unit_s * a.n_split + split_s) * ROWS * PW, (short)0, ROWS * PW * 4, 0x00020000);
         __syncthreads();
-        constexpr int PW = DR + 2;
-        float* part = a.ws_part + ((size_t)unit * a.n_split + split) * ROWS * PW;
         if (n < nrows) {
-            for (int c = cl; c < DR; c += 16)
-                __hip_atomic_store(part + n * PW + c, sm_o[0][n][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (cl == 0) {
-                __hip_atomic_store(part + n * PW + DR, sm_M[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(part + n * PW + DR + 1, sm_L[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < MERGE_NG<DR>; ++k) {
+                const int gi = cl + 16 * k;  // 16-byte group of the row: columns 4 gi .. 4 gi + 3, then (m, l)
+                if (gi <= DR / 4) {
+                    f32x4 v;
+                    if (gi < DR / 4) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = sm_o[0][n][4 * gi + e];
+                    } else {
+                        v = f32x4{sm_M[n], sm_L[n], 0.f, 0.f};
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (n * PW + 4 * gi) * 4, 0, CPOL_SC1);
+                }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VMCNT0);
         __syncthreads();
         if (tid == 0) {
             const int prev = __hip_atomic_fetch_add(a.ws_count + unit, 1, __ATOMIC_RELAXED,
@@ -733,8 +767,11 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         }
         __syncthreads();
         if (!sm_last) return;
-        merge_partials<D, R, SP>(a, unit, n_active, nrows, n, cl, sm_o[0], sm_L);
+        load_bv();
+        merge_partials<D, R, SP>(a, unit_s, split_s, n_active, nrows, n, cl, sm_o[0], sm_M, sm_L);
         if (tid == 0) __hip_atomic_store(a.ws_count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        load_bv();
     }
     __syncthreads();
     finalize_rows<D, R, SP>(a, sm_o[0], sm_L, n, cl, nrows, req0, h, bvc);
@@ -823,61 +860,90 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 }
 
 // Log-sum-exp merge of the chunk partials of one work unit into o[row][0..DR)
-// and L[row].  Runs in the last workgroup to finish.  Thread (row n, phase cl)
-// owns columns cl, cl + 16, ...; the partials of up to GB chunks (their maxima,
-// sums and columns) are requested together, so a merge of <= GB chunks waits
-// for one memory round trip.
+// and L[row].  Runs in the last workgroup to finish, whose own partial (chunk
+// `own`) is still in o / M_row / L_row and is taken from there; the others are
+// read from the workspace.  Chunks are combined in chunk order whichever
+// workgroup merges, so repeated calls give identical bits.  Thread (row n,
+// phase cl) owns the 16-byte column groups cl, cl + 16, ... of the row and
+// reads every partial's (m, l); the partials of up to GB chunks are requested
+// together, so a merge of <= GB chunks waits for one memory round trip.
 template <int D, int R, int SP>
-__device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int n_active, int nrows,
-                                               int n, int cl, float (*o_out)[SP], float* L_out) {
+__device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int own, int n_active, int nrows,
+                                               int n, int cl, float (*o)[SP], float* M_row, float* L_row) {
     constexpr int DR = D + R;
-    constexpr int PW = DR + 2;
-    constexpr int NC = (DR + 15) / 16;  // columns per thread
-    constexpr int GB = 8;               // chunks per batch
+    constexpr int PW = DR + 4;
+    constexpr int NG = MERGE_NG<DR>;
+    constexpr int GB = 8;  // chunks per batch
+    // `unit` and `own` are wave-uniform (scalar): the descriptor stays in
+    // scalar registers and the row is part of the per-lane offset
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_part + (size_t)unit * a.n_split * ROWS * PW, (short)0,
+        (uint32_t)((size_t)a.n_split * ROWS * PW * 4), 0x00020000);
     if (n >= nrows) return;
-    const float* base = a.ws_part + (size_t)unit * a.n_split * ROWS * PW + n * PW;
-    const size_t sstride = (size_t)ROWS * PW;
-    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    float M = -INFINITY, L = 0.f;
-    float o[NC];
+    const uint32_t sstride = ROWS * PW * 4;  // bytes between chunks
+    const uint32_t row_off = (uint32_t)n * PW * 4;
+    // the own partial, in the layout of a loaded one
+    const f32x4 own_ml = f32x4{M_row[n], L_row[n], 0.f, 0.f};
+    f32x4 own_o[NG];
 #pragma unroll
-    for (int k = 0; k < NC; ++k) o[k] = 0.f;
+    for (int k = 0; k < NG; ++k) {
+        const int gi = min(cl + 16 * k, DR / 4 - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) own_o[k][e] = o[n][4 * gi + e];
+    }
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int g0 = 0; g0 < n_active; g0 += GB) {
-        float mv[GB], lv[GB], ov[GB][NC];
+        f32x4 ml[GB], ov[GB][NG];
 #pragma unroll
         for (int u = 0; u < GB; ++u) {
-            const bool ok = g0 + u < n_active;
-            const float* p = base + (size_t)(ok ? g0 + u : g0) * sstride;
-            mv[u] = ok ? ld(p + DR) : -INFINITY;
-            lv[u] = ok ? ld(p + DR + 1) : 0.f;
+            // chunks past n_active re-read the own slot (weight 0); the own
+            // chunk's loaded values are replaced by the LDS ones
+            const int c = g0 + u < n_active ? g0 + u : own;
+            ml[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, c * sstride + row_off + 16 * (DR / 4), 0, CPOL_SC1));
 #pragma unroll
-            for (int k = 0; k < NC; ++k) {
-                const int c = cl + 16 * k;
-                ov[u][k] = (ok && c < DR) ? ld(p + c) : 0.f;
+            for (int k = 0; k < NG; ++k)
+                ov[u][k] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, c * sstride + row_off + 16 * min(cl + 16 * k, DR / 4 - 1), 0, CPOL_SC1));
+        }
+#pragma unroll
+        for (int u = 0; u < GB; ++u) {
+            if (g0 + u == own) {
+                ml[u] = own_ml;
+#pragma unroll
+                for (int k = 0; k < NG; ++k) ov[u][k] = own_o[k];
             }
         }
+        float mv[GB];
+#pragma unroll
+        for (int u = 0; u < GB; ++u) mv[u] = g0 + u < n_active ? ml[u][0] : -INFINITY;
         float M_new = M;
 #pragma unroll
         for (int u = 0; u < GB; ++u) M_new = fmaxf(M_new, mv[u]);
         const float resc = M == -INFINITY ? 0.f : fast_exp2(M - M_new);
         L *= resc;
 #pragma unroll
-        for (int k = 0; k < NC; ++k) o[k] *= resc;
+        for (int k = 0; k < NG; ++k) acc[k] *= resc;
 #pragma unroll
         for (int u = 0; u < GB; ++u) {
             const float w = mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - M_new);
-            L += w * lv[u];
+            L += w * ml[u][1];
 #pragma unroll
-            for (int k = 0; k < NC; ++k) o[k] += w * ov[u][k];
+            for (int k = 0; k < NG; ++k) acc[k] += w * ov[u][k];
         }
         M = M_new;
     }
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-        const int c = cl + 16 * k;
-        if (c < DR) o_out[n][c] = o[k];
+    for (int k = 0; k < NG; ++k) {
+        const int gi = cl + 16 * k;
+        if (gi < DR / 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[n][4 * gi + e] = acc[k][e];
+        }
     }
-    if (cl == 0) L_out[n] = L;
+    if (cl == 0) L_row[n] = L;
 }
 
 // O = (O_base + O_lr B_v^(h)) / l for the rows of one work unit: the single
