@@ -694,12 +694,18 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
             wt[w] = (M == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
             L += wt[w] * sm_l[w][n];
         }
-        for (int c = cl; c < DR; c += 16) {
-            float o = 0.f;
+        // unrolled: the LDS reads of every column go out before the first wait
+        float o[(DR + 15) / 16];
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) o += wt[w] * sm_o[w][n][c];
-            sm_o[0][n][c] = o;  // each (n, c) is read and written by this thread only
+        for (int k = 0; k < (DR + 15) / 16; ++k) {
+            const int c = min(cl + 16 * k, DR - 1);
+            o[k] = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) o[k] += wt[w] * sm_o[w][n][c];
         }
+#pragma unroll
+        for (int k = 0; k < (DR + 15) / 16; ++k)  // each (n, c) is read and written by this thread only
+            if (cl + 16 * k < DR) sm_o[0][n][cl + 16 * k] = o[k];
         if (cl == 0) {
             sm_M[n] = M;
             sm_L[n] = L;
