@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
-    "lr_cache_build", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
+    "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
     "prefill_paged", "prefill_paged_workspace_size", "cache_append",
 ]
 
@@ -26,7 +26,8 @@ LRA_F32, LRA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "lra_abi_version", "lra_status_str", "lra_last_error", "lra_attn_decode_workspace_size",
-    "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build", "lra_rope_table_build",
+    "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build",
+    "lra_lr_cache_build_workspace_size", "lra_rope_table_build",
     "lra_naive_expand_pages", "lra_attn_prefill_paged_workspace_size", "lra_attn_prefill_paged",
     "lra_cache_append",
 )
@@ -77,7 +78,9 @@ def load():
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, P, P]
     lib.lra_lr_cache_build.restype = I32
     lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, I32, P, P, ctypes.c_int64,
-                                       ctypes.c_int64, P]
+                                       ctypes.c_int64, P, ctypes.c_size_t, P]
+    lib.lra_lr_cache_build_workspace_size.restype = ctypes.c_size_t
+    lib.lra_lr_cache_build_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.lra_rope_table_build.restype = I32
     lib.lra_rope_table_build.argtypes = [ctypes.c_double, I32, I32, P, P, P]
     lib.lra_attn_prefill_paged_workspace_size.restype = ctypes.c_size_t
@@ -254,12 +257,19 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, 
     return out
 
 
-def lr_cache_build(x, a_k, a_v, l_k, l_v, *, row_offset=0, stream=None):
+def lr_cache_build_workspace_size(*, dtype, n_tok, d_model, rank, n_lr=1):
+    """Workspace bytes of ``lra_lr_cache_build`` for these sizes (0: none used)."""
+    return int(load().lra_lr_cache_build_workspace_size(dtype, n_tok, d_model, rank, n_lr))
+
+
+def lr_cache_build(x, a_k, a_v, l_k, l_v, *, row_offset=0, workspace=None, split=True, stream=None):
     """LR-cache rows ``L[row_offset + i] = x[i] A`` (``lra_lr_cache_build``).
 
     x [n_tok, d_model]; a_k, a_v [r, d_model] (LoRA A weight layout, out x in) and
     l_k, l_v [>= row_offset + n_tok, r], written in place; or, one A per agent,
     a_k, a_v [n_agents, r, d_model] and l_k, l_v [n_agents, rows, r] (X [A_1 .. A_n]).
+    ``workspace`` (uint8, zero-filled before first use) is allocated when the split
+    build needs one and none is given; ``split=False`` passes none (single-pass kernel).
     """
     lib = load()
     n_tok, d_model = x.shape
@@ -276,9 +286,17 @@ def lr_cache_build(x, a_k, a_v, l_k, l_v, *, row_offset=0, stream=None):
           and tuple(l_k.shape[:len(lead)]) == lead, "l_k/l_v [(n_lr,) rows, r]")
     rows = l_k.shape[-2]
     _need(rows >= row_offset + n_tok, "l_k/l_v too short for row_offset + n_tok")
+    if not split:
+        workspace = None
+    elif workspace is None:
+        import torch
+        n_ws = int(lib.lra_lr_cache_build_workspace_size(dt, n_tok, d_model, r, n_lr))
+        if n_ws > 0:
+            workspace = torch.zeros(n_ws, dtype=torch.uint8, device=x.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.lra_lr_cache_build(dt, _ptr(x), n_tok, d_model, _ptr(a_k), _ptr(a_v), r, n_lr,
                                   _ptr(l_k), _ptr(l_v), int(row_offset), rows * r if n_lr > 1 else 0,
-                                  _stream(x, stream)))
+                                  _ptr(workspace), wsz, _stream(x, stream)))
     return l_k, l_v
 
 

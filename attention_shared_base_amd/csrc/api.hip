@@ -418,10 +418,17 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
     return lra::launch_cache_append_bf16(a, (hipStream_t)stream);
 }
 
+size_t lra_lr_cache_build_workspace_size(int32_t dtype, int32_t n_tok, int32_t d_model, int32_t rank,
+                                        int32_t n_lr) {
+    if (dtype != LRA_BF16 || n_tok <= 0 || d_model <= 0 || d_model % 32 != 0 || n_lr < 1) return 0;
+    if (rank != 8 && rank != 16 && rank != 32) return 0;
+    return lra::lr_build_plan(n_tok, d_model, rank, n_lr).ws_bytes;
+}
+
 lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,
                               const void* a_k, const void* a_v, int32_t rank, int32_t n_lr,
                               void* l_k, void* l_v, int64_t row_offset, int64_t lr_agent_stride,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (dtype != LRA_F32 && dtype != LRA_BF16)
         return fail(LRA_ERR_UNSUPPORTED, "dtype %d (expected LRA_F32=0 or LRA_BF16=1)", dtype);
@@ -452,7 +459,17 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
     a.n_lr = n_lr;
     a.row_offset = row_offset;
     a.lr_stride = n_lr > 1 ? lr_agent_stride : 0;
+    a.workspace = nullptr;
     if (n_tok == 0) return LRA_OK;
+    if (workspace != nullptr && dtype == LRA_BF16) {
+        const size_t need = lra::lr_build_plan(n_tok, d_model, rank, n_lr).ws_bytes;
+        if (need > 0) {
+            if (!aligned16(workspace)) return fail(LRA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+            if (workspace_bytes < need)
+                return fail(LRA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, need);
+            a.workspace = workspace;
+        }
+    }
     if (dtype == LRA_F32) return lra::launch_lr_build_f32(a, (hipStream_t)stream);
     return lra::launch_lr_build_bf16(a, (hipStream_t)stream);
 }

@@ -12,7 +12,20 @@
 // agents, so X is read from HBM about once and reused from the caches.
 //
 // The product is tall and skinny (d_model x 2r with 2r <= 64) and bound by
-// reading X once from HBM.  A workgroup owns 16 tokens; its 8 wavefronts take
+// reading X once from HBM.  Every workgroup also reads the A columns of its
+// d_model range, and a CU streams only ~30-40 GB/s of loads (measured: one
+// workgroup alone takes as long as 256 together), so the A bytes per token
+// set the pace when every CU works on few tokens.
+//
+// Split kernel (with a workspace): a workgroup owns 64 tokens and one of KS
+// ranges of d_model (KS chosen so the grid fills the GPU); each of its 8
+// wavefronts takes pairs of 32-wide slices of the range for all four 16-token
+// tiles, so an A fragment is loaded once per wavefront and used four times.
+// The eight partial tiles are summed in LDS; with KS > 1 the fp32 partial goes
+// to the workspace and the last workgroup of the 64 tokens (a counter per
+// token block) adds the KS partials in range order and rounds once to bf16.
+//
+// Single-pass kernel (no workspace): a workgroup owns 16 tokens; its 8 wavefronts take
 // interleaved 32-wide slices of d_model (so together they stream each X row
 // contiguously) and each accumulates the full 16 x 2r tile with
 // v_mfma_f32_16x16x32_bf16; the eight partial tiles are summed in LDS and
@@ -109,6 +122,165 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
     }
 }
 
+// cache-policy bit sc1 (agent-coherent, as agent-scope atomic accesses) and
+// the s_waitcnt immediate for vmcnt(0)
+constexpr int LR_CPOL_SC1 = 16;
+constexpr int LR_WAITCNT_VMCNT0 = 0x0f70;
+constexpr int STOK = 64;  // tokens per workgroup of the split kernel
+
+struct LRSplitK {
+    const bf16* x;
+    const bf16* a_k;
+    const bf16* a_v;
+    bf16* l_k;
+    bf16* l_v;
+    float* ws_part;   // [units][ks][STOK][2R]
+    int32_t* ws_count;  // [units]
+    long long row_offset, lr_stride;
+    int32_t n_tok, d_model, n_lr, ks, slices_per_split;
+};
+
+template <int R>
+__global__ __launch_bounds__(512) void lra_lr_build_split_kernel(LRSplitK p) {
+    constexpr int NT = 2 * R / 16;  // 16-column output tiles
+    constexpr int NC = NT * 16;     // = 2R
+    constexpr int MT = STOK / 16;   // 16-token tiles
+    constexpr int PB = 2;           // slice pairs per wavefront per batch
+    __shared__ float sm[WAVES][STOK][NC + 1];
+    __shared__ int sm_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, kq = lane >> 4;
+    // neighbouring workgroups: the same tokens and range for successive agents
+    // (X reused from the caches), then the ranges of one token block
+    const int ag = blockIdx.x % p.n_lr;
+    const int rest = blockIdx.x / p.n_lr;
+    const int ks = rest % p.ks;
+    const int tb = rest / p.ks;
+    const int tok0 = tb * STOK;
+    const int unit = tb * p.n_lr + ag;
+    const bf16* a_k = p.a_k + (size_t)ag * R * p.d_model;
+    const bf16* a_v = p.a_v + (size_t)ag * R * p.d_model;
+
+    const bf16* xp[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)  // rows past n_tok read a valid row; never stored
+        xp[m] = p.x + (size_t)min(tok0 + 16 * m + l16, p.n_tok - 1) * p.d_model + 8 * kq;
+    const bf16* wp[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + l16;
+        wp[nt] = (col < R ? a_k + (size_t)col * p.d_model : a_v + (size_t)(col - R) * p.d_model) + 8 * kq;
+    }
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[m][nt] = zf4();
+
+    // slices [s_beg, s_end) of this range; a wavefront takes two adjacent
+    // slices at a time (its two loads per token row cover a 128-byte line)
+    const int n_steps = p.d_model / 32;
+    const int s_beg = ks * p.slices_per_split;
+    const int s_end = min(s_beg + p.slices_per_split, n_steps);
+    for (int s0 = s_beg + 2 * wave; s0 < s_end; s0 += 2 * WAVES * PB) {
+        bf16x8 xa[MT][2 * PB], wb[2 * PB][NT];
+#pragma unroll
+        for (int u = 0; u < 2 * PB; ++u) {
+            const int k = min(s0 + (u >> 1) * 2 * WAVES + (u & 1), n_steps - 1) * 32;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) xa[m][u] = ldg((const bf16x8*)(xp[m] + k));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) wb[u][nt] = ldg((const bf16x8*)(wp[nt] + k));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the batch's loads all in flight before the first wait
+#pragma unroll
+        for (int u = 0; u < 2 * PB; ++u) {
+            // slices past the range contribute zero (branch-free)
+            const bool ok = s0 + (u >> 1) * 2 * WAVES + (u & 1) < s_end;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const bf16x8 xv = ok ? xa[m][u] : zero8();
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[m][nt] = mfma16x16x32(xv, wb[u][nt], acc[m][nt]);
+            }
+        }
+    }
+    // C lane layout: tokens 16 m + 4 kq + v, column nt * 16 + l16
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sm[wave][16 * m + 4 * kq + v][nt * 16 + l16] = acc[m][nt][v];
+    __syncthreads();
+    // thread e: elements e, e + 512, ... of the [STOK][2R] tile
+    constexpr int EPT = STOK * NC / 512;
+    float sum[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = tid + 512 * j, t = e / NC, c = e % NC;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += sm[w][t][c];
+        sum[j] = s;
+    }
+    if (p.ks > 1) {
+        // partial -> workspace with agent-coherent stores; every wavefront waits
+        // for its store acknowledgements before the barrier, and only then is
+        // the counter bumped; the last of the KS workgroups reads the others
+        // with agent-coherent loads and adds all in range order
+        float* part = p.ws_part + (size_t)unit * p.ks * STOK * NC;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            __hip_atomic_store(part + (size_t)ks * STOK * NC + tid + 512 * j, sum[j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(LR_WAITCNT_VMCNT0);
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(p.ws_count + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == p.ks - 1;
+        }
+        __syncthreads();
+        if (!sm_last) return;
+        float tot[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) tot[j] = 0.f;
+        for (int r0 = 0; r0 < p.ks; r0 += 4) {
+            float v[4][EPT];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < EPT; ++j)
+                    v[u][j] = (r0 + u < p.ks && r0 + u != ks)
+                                  ? __hip_atomic_load(part + (size_t)(r0 + u) * STOK * NC + tid + 512 * j,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : sum[j];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < EPT; ++j)
+                    if (r0 + u < p.ks) tot[j] += v[u][j];
+        }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) sum[j] = tot[j];
+        if (tid == 0) __hip_atomic_store(p.ws_count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bf16* l_k = p.l_k + (size_t)ag * p.lr_stride;
+    bf16* l_v = p.l_v + (size_t)ag * p.lr_stride;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = tid + 512 * j, t = e / NC, c = e % NC;
+        if (tok0 + t < p.n_tok) {
+            const size_t row = (size_t)(p.row_offset + tok0 + t);
+            if (c < R) l_k[row * R + c] = (bf16)sum[j];
+            else l_v[row * R + (c - R)] = (bf16)sum[j];
+        }
+    }
+}
+
 __global__ void lra_lr_build_f32_kernel(const float* __restrict__ x, const float* __restrict__ a_k,
                                         const float* __restrict__ a_v, float* __restrict__ l_k,
                                         float* __restrict__ l_v, int n_tok, int d_model, int r,
@@ -145,20 +317,71 @@ __global__ void lra_rope_table_kernel(double theta, int head_dim, int n_pos, flo
 
 namespace lra {
 
+LRPlan lr_build_plan(int n_tok, int d_model, int rank, int n_lr) {
+    LRPlan pl{};
+    const long long units = (long long)(n_tok + STOK - 1) / STOK * n_lr;
+    const int n_steps = d_model / 32;
+    // ranges of d_model: enough workgroups for every CU from one agent's token
+    // blocks, each range still >= 16 slices (two per wavefront).  The split
+    // does not depend on n_lr, so a build of n caches in one call gives the
+    // bits of n single-cache builds.
+    const long long blocks = (long long)(n_tok + STOK - 1) / STOK;
+    int ks = 1;
+    while (ks < 8 && blocks * ks < 256 && n_steps / (2 * ks) >= 16) ks *= 2;
+    pl.ks = ks;
+    pl.slices_per_split = ((n_steps + ks - 1) / ks + 1) / 2 * 2;
+    pl.units = units;
+    pl.ws_counter_bytes = ((size_t)units * sizeof(int32_t) + 255) / 256 * 256;
+    pl.ws_bytes = ks > 1 ? pl.ws_counter_bytes + (size_t)units * ks * STOK * 2 * rank * sizeof(float) : 0;
+    return pl;
+}
+
 lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
     if (a.n_tok == 0) return LRA_OK;
+    const bf16* x = (const bf16*)a.x;
+    const bf16* ak = (const bf16*)a.a_k;
+    const bf16* av = (const bf16*)a.a_v;
+    bf16* lk = (bf16*)a.l_k;
+    bf16* lv = (bf16*)a.l_v;
+    const long long ro = (long long)a.row_offset, ls = (long long)a.lr_stride;
+    const LRPlan pl = lr_build_plan(a.n_tok, a.d_model, a.rank, a.n_lr);
+    if (pl.ks == 1 || a.workspace != nullptr) {
+        const long long nb = pl.units * pl.ks;
+        if (nb > 0x7fffffffLL) {
+            set_error("lr build: grid of %lld workgroups too large", nb);
+            return LRA_ERR_BAD_SHAPE;
+        }
+        LRSplitK k{};
+        k.x = x;
+        k.a_k = ak;
+        k.a_v = av;
+        k.l_k = lk;
+        k.l_v = lv;
+        k.ws_count = (int32_t*)a.workspace;
+        k.ws_part = a.workspace ? (float*)((char*)a.workspace + pl.ws_counter_bytes) : nullptr;
+        k.row_offset = ro;
+        k.lr_stride = ls;
+        k.n_tok = a.n_tok;
+        k.d_model = a.d_model;
+        k.n_lr = a.n_lr;
+        k.ks = pl.ks;
+        k.slices_per_split = pl.slices_per_split;
+        const dim3 grid((unsigned)nb), block(64 * WAVES);
+        switch (a.rank) {
+            case 8: hipLaunchKernelGGL(lra_lr_build_split_kernel<8>, grid, block, 0, s, k); break;
+            case 16: hipLaunchKernelGGL(lra_lr_build_split_kernel<16>, grid, block, 0, s, k); break;
+            case 32: hipLaunchKernelGGL(lra_lr_build_split_kernel<32>, grid, block, 0, s, k); break;
+            default: set_error("lr build: unsupported rank %d", a.rank); return LRA_ERR_UNSUPPORTED;
+        }
+        return check_launch("lra_lr_build_split_kernel");
+    }
+    // no workspace: 16-token workgroups over the whole of d_model
     const long long nb = (long long)(a.n_tok + TOK - 1) / TOK * a.n_lr;
     if (nb > 0x7fffffffLL) {
         set_error("lr build: grid of %lld workgroups too large", nb);
         return LRA_ERR_BAD_SHAPE;
     }
     const dim3 grid((unsigned)nb), block(64 * WAVES);
-    const long long ro = (long long)a.row_offset, ls = (long long)a.lr_stride;
-    const bf16* x = (const bf16*)a.x;
-    const bf16* ak = (const bf16*)a.a_k;
-    const bf16* av = (const bf16*)a.a_v;
-    bf16* lk = (bf16*)a.l_k;
-    bf16* lv = (bf16*)a.l_v;
     switch (a.rank) {
         case 8: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<8>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
         case 16: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<16>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;

@@ -96,7 +96,16 @@ struct LRBuildArgs {
     void* l_v;
     int32_t n_tok, d_model, rank, n_lr;
     int64_t row_offset, lr_stride;
+    void* workspace;  // NULL: single-pass kernel; else >= lr_build_plan().ws_bytes, zeroed before first use
 };
+
+// d_model split of the bf16 LR build: ks ranges per 64-token block and agent
+struct LRPlan {
+    int ks, slices_per_split;
+    long long units;
+    size_t ws_counter_bytes, ws_bytes;
+};
+LRPlan lr_build_plan(int n_tok, int d_model, int rank, int n_lr);
 
 lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s);
 lra_status launch_lr_build_f32(const LRBuildArgs& a, hipStream_t s);

@@ -412,10 +412,13 @@ def extra_lr_build(steps, warmup, n_sets=8):
                  lk=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda"),
                  lv=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda"))
             for _ in range(n_sets)]
+    # one zero-filled workspace for every call (the calls leave it ready)
+    n_ws = lra.lr_cache_build_workspace_size(dtype=1, n_tok=n_tok, d_model=d_model, rank=r)
+    ws = torch.zeros(max(n_ws, 16), dtype=torch.uint8, device="cuda")
 
     def call(i):
         s = sets[i]
-        lra.lr_cache_build(s["x"], s["ak"], s["av"], s["lk"], s["lv"])
+        lra.lr_cache_build(s["x"], s["ak"], s["av"], s["lk"], s["lv"], workspace=ws)
 
     ms = _time_calls(call, n_sets, steps, warmup)
     nbytes = lr_build_bytes(n_tok, d_model, r)
@@ -456,10 +459,13 @@ def extra_prelr_step(steps, warmup, n_layers=32):
             bv=_randn_bf16((n_ag, r, h_kv * d), 0.05, gen)))
     agent = torch.arange(n_ag, dtype=torch.int32, device="cuda")
     out = torch.empty((n_ag, n_new, h_q, d), dtype=torch.bfloat16, device="cuda")
+    n_ws = lra.lr_cache_build_workspace_size(dtype=1, n_tok=n_new, d_model=d_model, rank=r)
+    ws = torch.zeros(max(n_ws, 16), dtype=torch.uint8, device="cuda")
 
     def call(_):
         for L in layers:
-            lra.lr_cache_build(L["x"], L["ak"], L["av"], L["lk"], L["lv"], row_offset=n_old)
+            lra.lr_cache_build(L["x"], L["ak"], L["av"], L["lk"], L["lv"], row_offset=n_old,
+                               workspace=ws)
             lra.prefill(L["q"], agent, L["k"], L["v"], L["lk"], L["lv"], L["bk"], L["bv"], out=out)
 
     ms = _time_calls(call, 1, steps, warmup)

@@ -62,7 +62,7 @@ typedef int32_t lra_status;
 #define LRA_F32 0
 #define LRA_BF16 1
 
-#define LRA_ABI_VERSION 2
+#define LRA_ABI_VERSION 3
 
 typedef struct lra_dims {
     int32_t n_q_heads;   /* H_q */
@@ -261,12 +261,29 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
  *   l_k, l_v   n_lr blocks lr_agent_stride elements apart (ignored for
  *              n_lr = 1), each [>= row_offset + n_tok, rank]; rows written in
  *              place  device
- *   Requires d_model % 32 == 0.  bf16 results are rounded to nearest even.
+ *   workspace  optional (may be NULL), device, caller-owned, 16-byte aligned,
+ *              >= lra_lr_cache_build_workspace_size(...) bytes, zero-filled
+ *              before its first use (each call leaves it ready for the next:
+ *              its counters return to zero).  With it,
+ *              bf16 builds split d_model over several workgroups per token
+ *              block and add their fp32 partials in a fixed order (faster when
+ *              n_tok * n_lr is small); without it one workgroup covers each
+ *              token's whole d_model.  Either way the result is deterministic.
+ *              Concurrent calls must not share a workspace.
+ *   Requires d_model % 32 == 0.  bf16 results are rounded to nearest even
+ *   once, after fp32 accumulation.
+ *   Errors: LRA_ERR_WORKSPACE_TOO_SMALL, LRA_ERR_MISALIGNED for a workspace
+ *   that is given but too small or misaligned.
  */
 lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32_t d_model,
                               const void* a_k, const void* a_v, int32_t rank, int32_t n_lr,
                               void* l_k, void* l_v, int64_t row_offset,
-                              int64_t lr_agent_stride, void* stream);
+                              int64_t lr_agent_stride, void* workspace, size_t workspace_bytes,
+                              void* stream);
+/* Workspace bytes lra_lr_cache_build uses for these sizes (0: none needed;
+ * also 0 for fp32 and for arguments lra_lr_cache_build rejects). */
+size_t lra_lr_cache_build_workspace_size(int32_t dtype, int32_t n_tok, int32_t d_model, int32_t rank,
+                                         int32_t n_lr);
 
 /*
  * RoPE tables for prefill and decode: cos/sin of pos * theta^(-2i/d), pos in

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = lra.load()
-    assert lra.abi_version() == 2
+    assert lra.abi_version() == 3
     for s in range(7):
         assert lib.lra_status_str(s).decode().startswith("LRA_")
     assert b"unknown" in lib.lra_status_str(99)
@@ -139,10 +139,11 @@ def test_lr_build_validation():
 
     def call(**o):
         a = dict(dt=1, x=A, n_tok=16, d_model=4096, ak=A, av=A, r=16, n_lr=1, lk=A, lv=A, off=0,
-                 ls=0)
+                 ls=0, ws=None, wsz=0)
         a.update(o)
         return lib.lra_lr_cache_build(a["dt"], a["x"], a["n_tok"], a["d_model"], a["ak"], a["av"],
-                                      a["r"], a["n_lr"], a["lk"], a["lv"], a["off"], a["ls"], None)
+                                      a["r"], a["n_lr"], a["lk"], a["lv"], a["off"], a["ls"],
+                                      a["ws"], a["wsz"], None)
 
     assert call(r=12) == 3
     assert call(dt=5) == 3
@@ -156,6 +157,11 @@ def test_lr_build_validation():
     assert call(n_lr=0) == 2
     assert call(n_lr=4, ls=16 * 16 - 1) == 2      # agents' caches would overlap
     assert call(n_lr=4, ls=16 * 16, n_tok=0) == 0
+    # a workspace that is given must be large enough and aligned (16 tokens: split in 8)
+    need = lra.lr_cache_build_workspace_size(dtype=1, n_tok=16, d_model=4096, rank=16)
+    assert need > 0
+    assert call(ws=A, wsz=need - 1) == 5
+    assert call(ws=ctypes.c_void_p(0x100008), wsz=need) == 4
 
 
 def test_rope_table_validation():
@@ -243,3 +249,24 @@ def test_paged_prefill_and_append_validation():
     assert ap(page=8) == 3
     assert ap(dm=dims(dt=0)) == 3
     assert ap(kp=ctypes.c_void_p(0x100004)) == 4
+
+
+def test_lr_build_workspace_size():
+    """Split plan: ranges of d_model until one agent's token blocks cover 256 CUs, each
+    range >= 16 slices;
+    partials of 64 tokens x 2r fp32 per range, counters padded to 256 bytes."""
+    ws = lambda **o: lra.lr_cache_build_workspace_size(**{**dict(dtype=1, d_model=4096, rank=16), **o})
+    # 4096 tokens: 64 blocks x 4 ranges = 256 workgroups
+    assert ws(n_tok=4096) == 256 + 64 * 4 * 64 * 32 * 4
+    # 16384 tokens fill the GPU without a split: no workspace
+    assert ws(n_tok=16384) == 0
+    # 8 agents x 1024 tokens: the split of one agent's 16 blocks (8 ranges), 128 units
+    assert ws(n_tok=1024, n_lr=8) == 512 + 128 * 8 * 64 * 32 * 4
+    # at most 8 ranges, and d_model 1024 (32 slices) allows only 2
+    assert ws(n_tok=64) == 256 + 1 * 8 * 64 * 32 * 4
+    assert ws(n_tok=64, d_model=1024) == 256 + 1 * 2 * 64 * 32 * 4
+    assert ws(n_tok=4096, rank=32) == 256 + 64 * 4 * 64 * 64 * 4
+    # fp32 and rejected arguments need none
+    assert ws(n_tok=4096, dtype=0) == 0
+    assert ws(n_tok=4096, rank=12) == 0
+    assert ws(n_tok=0) == 0

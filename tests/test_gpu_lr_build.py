@@ -48,3 +48,48 @@ def test_rope_tables_match_oracle():
     rc, rs = oracle.rope_tables(16896, 128, 500000.0)
     assert np.max(np.abs(host(cos) - rc)) < 1e-6
     assert np.max(np.abs(host(sin) - rs)) < 1e-6
+
+
+@pytest.mark.parametrize("n_tok,d_model,r,n_lr", [
+    (4096, 4096, 16, 1),    # 64 token blocks x 4 ranges of d_model
+    (1000, 4096, 32, 1),    # ragged last block, 8 ranges
+    (77, 1024, 8, 3),       # three agents, 2 ranges
+    (20000, 2048, 16, 1),   # no split (enough blocks): the 64-token kernel alone
+])
+def test_lr_build_split_matches_oracle_and_single_pass(n_tok, d_model, r, n_lr):
+    """The d_model-split build (workspace given) against the oracle within one bf16 rounding,
+    against the single-pass build (no workspace) within two roundings, repeatable bit for
+    bit, and leaving the workspace zeroed."""
+    import torch
+    import attention_shared_base_amd as lra
+    rng = np.random.default_rng(43)
+    x = w.f32_to_bf16_bits(rng.standard_normal((n_tok, d_model)).astype(np.float32))
+    shp = (n_lr, r, d_model) if n_lr > 1 else (r, d_model)
+    a_k = w.f32_to_bf16_bits((rng.standard_normal(shp) / 64).astype(np.float32))
+    a_v = w.f32_to_bf16_bits((rng.standard_normal(shp) / 64).astype(np.float32))
+    off = 5
+    rows = off + n_tok + 3
+    lshape = (n_lr, rows, r) if n_lr > 1 else (rows, r)
+    n_ws = lra.lr_cache_build_workspace_size(dtype=1, n_tok=n_tok, d_model=d_model, rank=r, n_lr=n_lr)
+    ws = torch.zeros(max(n_ws, 16), dtype=torch.uint8, device="cuda")
+    outs = []
+    for split in (True, True, False):
+        lk = torch.full(lshape, 7.0, dtype=torch.bfloat16, device="cuda")
+        lv = torch.full(lshape, 7.0, dtype=torch.bfloat16, device="cuda")
+        lra.lr_cache_build(dev(x), dev(a_k), dev(a_v), lk, lv, row_offset=off,
+                           workspace=ws if split else None, split=split)
+        outs.append((host(lk).reshape(n_lr, rows, r), host(lv).reshape(n_lr, rows, r)))
+    units = -(-n_tok // 64) * n_lr
+    assert int(ws[:4 * units].view(torch.int32).abs().sum()) == 0  # counters back at zero
+    (sk, sv), (sk2, sv2), (pk, pv) = outs
+    assert np.array_equal(sk, sk2) and np.array_equal(sv, sv2)
+    ak3 = a_k.reshape(n_lr, r, d_model)
+    av3 = a_v.reshape(n_lr, r, d_model)
+    for a in range(n_lr):
+        ek, ev = oracle.lr_cache_build(w.widen(x), w.widen(ak3[a]).T, w.widen(av3[a]).T)
+        for got, single, e in ((sk[a], pk[a], ek), (sv[a], pv[a], ev)):
+            assert np.all(got[:off] == 7.0) and np.all(got[off + n_tok:] == 7.0)
+            g = got[off:off + n_tok]
+            # fp32 accumulation in another order, one bf16 rounding
+            assert np.all(np.abs(g - e) <= 2.0 ** -8 * np.abs(e) + 1e-3)
+            assert np.all(np.abs(g - single[off:off + n_tok]) <= 2.0 ** -7 * np.abs(e) + 2e-3)
