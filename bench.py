@@ -123,6 +123,23 @@ def _time_calls(fn, n_sets, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def _call_stats(fn, n_sets, n_calls):
+    """Per-call times (us) of n_calls back-to-back calls, one HIP event pair per call on the
+    launch stream: median, p10, p90 (after the timed region, so it does not perturb it)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_calls)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i % n_sets)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90)), "calls": n_calls}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16__decode_4ctx_x_8192_r16__hbm_traffic.txt")
 TRAFFIC_SOURCES = ("attention_shared_base_amd/csrc/decode_kernel.h", "attention_shared_base_amd/csrc/decode_bf16.hip",
                    "attention_shared_base_amd/csrc/api.hip")
@@ -168,7 +185,7 @@ class DecodeSet:
         self.out = None
 
 
-def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False):
+def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stats=None):
     import torch
     import attention_shared_base_amd as lra
     import workloads as w
@@ -201,6 +218,8 @@ def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False):
                    out=s.out, workspace=ws)
 
     ms = _time_calls(call, n_sets, steps, warmup)
+    if stats is not None:
+        stats.update(_call_stats(call, n_sets, max(20, min(steps, 200))))
     nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, 16)
     if rope_theta is not None:
         nbytes += 2 * max_len * 64 * 4  # the cos / sin rows, read once
@@ -552,7 +571,8 @@ def main():
     lra.load()
 
     _log("primary: decode, 4 shared contexts x 8192 tokens, 16 requests")
-    case, ms, nbytes = primary_decode(args.steps, args.warmup, args.sets)
+    call_us = {}
+    case, ms, nbytes = primary_decode(args.steps, args.warmup, args.sets, stats=call_us)
     gbs = nbytes / (ms * 1e-3) / 1e9
     value = case.n_req / (ms * 1e-3)
     _log(f"primary: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, {value:.0f} tokens/s")
@@ -611,6 +631,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
+        "call_us": call_us,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
