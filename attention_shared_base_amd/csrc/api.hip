@@ -38,8 +38,8 @@ lra_status check_dims(const lra_dims* d) {
         return fail(LRA_ERR_UNSUPPORTED, "dtype %d (expected LRA_F32=0 or LRA_BF16=1)", d->dtype);
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(LRA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
-    if (d->rank != 8 && d->rank != 16 && d->rank != 32)
-        return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 8, 16, 32)", d->rank);
+    if (d->rank != 4 && d->rank != 8 && d->rank != 16 && d->rank != 32)
+        return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 4, 8, 16, 32)", d->rank);
     if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
         return fail(LRA_ERR_BAD_SHAPE, "softmax_scale is not finite");
     if (d->lr_agent_stride < 0)
@@ -421,7 +421,7 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
 size_t lra_lr_cache_build_workspace_size(int32_t dtype, int32_t n_tok, int32_t d_model, int32_t rank,
                                         int32_t n_lr) {
     if (dtype != LRA_BF16 || n_tok <= 0 || d_model <= 0 || d_model % 32 != 0 || n_lr < 1) return 0;
-    if (rank != 8 && rank != 16 && rank != 32) return 0;
+    if (rank != 4 && rank != 8 && rank != 16 && rank != 32) return 0;
     return lra::lr_build_plan(n_tok, d_model, rank, n_lr).ws_bytes;
 }
 
@@ -432,8 +432,8 @@ lra_status lra_lr_cache_build(int32_t dtype, const void* x, int32_t n_tok, int32
     g_err[0] = 0;
     if (dtype != LRA_F32 && dtype != LRA_BF16)
         return fail(LRA_ERR_UNSUPPORTED, "dtype %d (expected LRA_F32=0 or LRA_BF16=1)", dtype);
-    if (rank != 8 && rank != 16 && rank != 32)
-        return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 8, 16, 32)", rank);
+    if (rank != 4 && rank != 8 && rank != 16 && rank != 32)
+        return fail(LRA_ERR_UNSUPPORTED, "rank %d (supported: 4, 8, 16, 32)", rank);
     if (n_tok < 0) return fail(LRA_ERR_BAD_SHAPE, "n_tok %d < 0", n_tok);
     if (d_model <= 0) return fail(LRA_ERR_BAD_SHAPE, "d_model %d <= 0", d_model);
     if (d_model % 32 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %d is not a multiple of 32", d_model);

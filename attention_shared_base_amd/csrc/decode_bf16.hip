@@ -25,6 +25,8 @@ lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStrea
     LRA_CASE(64, 16)
     LRA_CASE(64, 32)
     LRA_CASE(64, 8)
+    LRA_CASE(128, 4)
+    LRA_CASE(64, 4)
 #undef LRA_CASE
     set_error("decode: unsupported head_dim %d / rank %d", d, r);
     return LRA_ERR_UNSUPPORTED;

@@ -319,8 +319,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                 } else if constexpr (R == 16) {
                     T.lk[u][t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * q4)), zero4());
                 } else {
-                    T.lk[u][t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * (q4 & 1))), zero4());
-                    if (q4 >= 2) T.lk[u][t] = zero8();
+                    // R = 8 / 4: k-groups past R/4 hold zero ranks (loads stay in the row)
+                    T.lk[u][t] = cat4(ldg((const bf16x4*)(lkp + n16 * R + 4 * (q4 % (R / 4)))), zero4());
+                    if (q4 >= R / 4) T.lk[u][t] = zero8();
                 }
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) {
@@ -440,9 +441,13 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                             const int c = c0 + e;
                             char* ent = sm_bk + (((s0 + u) * NDT + (c >> 4)) * 64 + (c & 15) + 16 * grp) * BKW;
                             *(bf16*)(ent + 2 * slot) = raw[u][k][e];
-                            // the zero slots: ranks 16.. (R < 32) and k-groups 2, 3 (R = 8)
+                            // the zero slots: ranks 16.. (R < 32) and the k-groups
+                            // R/4 .. 3 that hold no rank (R < 16; written by rank 0)
                             if (R < 32 && (rank & 3) == 0) *(bf16x4*)(ent + 8) = zero4();
-                            if (R == 8 && (rank & 3) == 0) *(bf16x8*)(ent + 32 * BKW) = zero8();
+                            if (R < 16 && rank == 0) {
+#pragma unroll
+                                for (int gz = R / 4; gz < 4; ++gz) *(bf16x8*)(ent + 16 * gz * BKW) = zero8();
+                            }
                         }
                     }
                 }

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
                                                                 int n_tok, int d_model,
                                                                 long long row_offset, int n_lr,
                                                                 long long lr_stride) {
-    constexpr int NT = 2 * R / 16;  // 16-column output tiles (R = 8, 16, 32)
+    constexpr int NT = (2 * R + 15) / 16;  // 16-column output tiles (R = 4 fills half of one)
     constexpr int NC = NT * 16;
     constexpr int BATCH = R == 32 ? 8 : 16;  // k-slices per wavefront in flight
     __shared__ float sm[WAVES][TOK][NC + 1];
@@ -67,9 +67,11 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
     // rows past n_tok read a valid row; their results are never stored
     const bf16* xp = x + (size_t)min(tok0 + l16, n_tok - 1) * d_model + 8 * kq;
     const bf16* wp[NT];
+    bool col_ok[NT];  // output columns past 2R (R = 4) take zero operands
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int col = nt * 16 + l16;
+        const int col = min(nt * 16 + l16, 2 * R - 1);
+        col_ok[nt] = nt * 16 + l16 < 2 * R;
         wp[nt] = (col < R ? a_k + (size_t)col * d_model : a_v + (size_t)(col - R) * d_model) + 8 * kq;
     }
 
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
             // would drain the loads in flight)
             const bf16x8 xv = s0 + (u >> 1) * 2 * WAVES + (u & 1) < n_steps ? xa[u] : zero8();
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x32(xv, wb[u][nt], acc[nt]);
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x32(xv, col_ok[nt] ? wb[u][nt] : zero8(), acc[nt]);
         }
     }
     // C lane layout: tokens 4*kq + v, column l16 of each tile
@@ -142,8 +144,8 @@ struct LRSplitK {
 
 template <int R>
 __global__ __launch_bounds__(512) void lra_lr_build_split_kernel(LRSplitK p) {
-    constexpr int NT = 2 * R / 16;  // 16-column output tiles
-    constexpr int NC = NT * 16;     // = 2R
+    constexpr int NT = (2 * R + 15) / 16;  // 16-column output tiles (R = 4 fills half of one)
+    constexpr int NC = NT * 16;            // = 2R, or 16 for R = 4
     constexpr int MT = STOK / 16;   // 16-token tiles
     constexpr int PB = 2;           // slice pairs per wavefront per batch
     __shared__ float sm[WAVES][STOK][NC + 1];
@@ -169,9 +171,11 @@ __global__ __launch_bounds__(512) void lra_lr_build_split_kernel(LRSplitK p) {
     for (int m = 0; m < MT; ++m)  // rows past n_tok read a valid row; never stored
         xp[m] = p.x + (size_t)min(tok0 + 16 * m + l16, p.n_tok - 1) * p.d_model + 8 * kq;
     const bf16* wp[NT];
+    bool col_ok[NT];  // output columns past 2R (R = 4) take zero operands
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int col = nt * 16 + l16;
+        const int col = min(nt * 16 + l16, 2 * R - 1);
+        col_ok[nt] = nt * 16 + l16 < 2 * R;
         wp[nt] = (col < R ? a_k + (size_t)col * p.d_model : a_v + (size_t)(col - R) * p.d_model) + 8 * kq;
     }
     f32x4 acc[MT][NT];
@@ -204,7 +208,8 @@ __global__ __launch_bounds__(512) void lra_lr_build_split_kernel(LRSplitK p) {
             for (int m = 0; m < MT; ++m) {
                 const bf16x8 xv = ok ? xa[m][u] : zero8();
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[m][nt] = mfma16x16x32(xv, wb[u][nt], acc[m][nt]);
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[m][nt] = mfma16x16x32(xv, col_ok[nt] ? wb[u][nt] : zero8(), acc[m][nt]);
             }
         }
     }
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(512) void lra_lr_build_split_kernel(LRSplitK p) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         const int e = tid + 512 * j, t = e / NC, c = e % NC;
-        if (tok0 + t < p.n_tok) {
+        if (tok0 + t < p.n_tok && c < 2 * R) {
             const size_t row = (size_t)(p.row_offset + tok0 + t);
             if (c < R) l_k[row * R + c] = (bf16)sum[j];
             else l_v[row * R + (c - R)] = (bf16)sum[j];
@@ -332,7 +337,8 @@ LRPlan lr_build_plan(int n_tok, int d_model, int rank, int n_lr) {
     pl.slices_per_split = ((n_steps + ks - 1) / ks + 1) / 2 * 2;
     pl.units = units;
     pl.ws_counter_bytes = ((size_t)units * sizeof(int32_t) + 255) / 256 * 256;
-    pl.ws_bytes = ks > 1 ? pl.ws_counter_bytes + (size_t)units * ks * STOK * 2 * rank * sizeof(float) : 0;
+    const int nc = 2 * rank < 16 ? 16 : 2 * rank;  // fp32 columns of a partial row
+    pl.ws_bytes = ks > 1 ? pl.ws_counter_bytes + (size_t)units * ks * STOK * nc * sizeof(float) : 0;
     return pl;
 }
 
@@ -368,6 +374,7 @@ lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
         k.slices_per_split = pl.slices_per_split;
         const dim3 grid((unsigned)nb), block(64 * WAVES);
         switch (a.rank) {
+            case 4: hipLaunchKernelGGL(lra_lr_build_split_kernel<4>, grid, block, 0, s, k); break;
             case 8: hipLaunchKernelGGL(lra_lr_build_split_kernel<8>, grid, block, 0, s, k); break;
             case 16: hipLaunchKernelGGL(lra_lr_build_split_kernel<16>, grid, block, 0, s, k); break;
             case 32: hipLaunchKernelGGL(lra_lr_build_split_kernel<32>, grid, block, 0, s, k); break;
@@ -383,6 +390,7 @@ lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
     }
     const dim3 grid((unsigned)nb), block(64 * WAVES);
     switch (a.rank) {
+        case 4: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<4>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
         case 8: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<8>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
         case 16: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<16>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
         case 32: hipLaunchKernelGGL(lra_lr_build_bf16_kernel<32>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;

@@ -166,6 +166,8 @@ lra_status launch_naive_expand_bf16(const ExpandArgs& p, hipStream_t s) {
     LRA_CASE(64, 16)
     LRA_CASE(64, 32)
     LRA_CASE(64, 8)
+    LRA_CASE(128, 4)
+    LRA_CASE(64, 4)
 #undef LRA_CASE
     set_error("naive expand: unsupported head_dim %d / rank %d", p.head_dim, p.rank);
     return LRA_ERR_UNSUPPORTED;

@@ -154,6 +154,8 @@ namespace lra {
     if (p.head_dim == 64 && p.rank == 16) return FN<64, 16>(p, s);               \
     if (p.head_dim == 64 && p.rank == 32) return FN<64, 32>(p, s);               \
     if (p.head_dim == 64 && p.rank == 8) return FN<64, 8>(p, s);                 \
+    if (p.head_dim == 128 && p.rank == 4) return FN<128, 4>(p, s);               \
+    if (p.head_dim == 64 && p.rank == 4) return FN<64, 4>(p, s);                 \
     set_error("paged cache: unsupported head_dim %d / rank %d", p.head_dim, p.rank); \
     return LRA_ERR_UNSUPPORTED;
 

@@ -101,6 +101,21 @@ LRA_DEV void dma_1k(u32x4 r, uint32_t lds, uint32_t voff) {
         : "memory");
 }
 
+// The same with 4 bytes per lane (lane i -> lds + 4 i): the rank-4 L rows, 8
+// bytes each, spread over 16-byte LDS slots.
+LRA_DEV void dma_256(u32x4 r, uint32_t lds, uint32_t voff) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r)
+        : "memory");
+}
+
 // s_waitcnt vmcnt(0): this wavefront's LDS DMA has landed.
 LRA_DEV void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
@@ -125,10 +140,13 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int NKS = D / 16;               // k-steps over head dim
     constexpr int NDT = D / 32;               // 32-wide dim tiles
     constexpr int NKR = RW / 16;              // k-steps over rank
-    constexpr int NLT = (R + 1 + 31) / 32;    // rank tiles of O_lr incl. the ones row
-    constexpr int ONES_T = R / 32;            // tile holding the ones row
-    constexpr int ONES_M = R % 32;            // its row inside the tile
-    constexpr int RCH = R / 8;                // 16-byte rank chunks per L row in HBM
+    // 16-byte rank chunks of an L tile that come from HBM (rank 4: one chunk,
+    // ranks 4-7 zero); the ones row is the first rank of the next chunk
+    constexpr int RCH = R < 8 ? 1 : R / 8;
+    constexpr int ONES_RANK = 8 * RCH;        // = R for R >= 8
+    constexpr int NLT = (ONES_RANK + 1 + 31) / 32;  // rank tiles of O_lr incl. the ones row
+    constexpr int ONES_T = ONES_RANK / 32;    // tile holding the ones row
+    constexpr int ONES_M = ONES_RANK % 32;    // its row inside the tile
     constexpr int NLK = RW / 8;               // L_k chunks held
     constexpr int NLV = 4 * NLT;              // L_v chunks held (ranks, ones row, zeros)
     constexpr int TLK = NLK * 1024;
@@ -143,7 +161,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int VKS = (D == 128) ? RB : 2 * RB;   // V offset of the next 16 keys
     constexpr int V8 = (D == 128) ? 8 * VBS : RB;   // V offset of rows +8
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    static_assert(R % 8 == 0 && R <= 32, "rank 8, 16, 24 or 32");
+    static_assert((R % 8 == 0 && R <= 32) || R == 4, "rank 4, 8, 16, 24 or 32");
     static_assert(NU >= 1 && NI % WAVES == 0, "tile blocks divide over the wavefronts");
     static_assert(RCH <= 4, "L_v DMA uses wavefronts 4..7");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -195,6 +213,10 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     for (int u = 0; u < NU; ++u)
         voff_row[u] = (uint32_t)((wave + WAVES * u) + NI * (lane / CPR)) * RB + (lane % CPR) * 16;
     const uint32_t voff_l = (uint32_t)lane * (2 * R);
+    // rank 4: dword DMA j (of 4) fills keys 16j .. 16j+15; lane -> key 16j + lane/4,
+    // dword lane%4 of its 16-byte slot: the row's two dwords, then two zeros
+    // (an offset past every buffer range reads as zero)
+    const uint32_t voff_l4 = (lane & 3) < 2 ? (uint32_t)(lane >> 2) * 8 + 4 * (lane & 3) : 0x80000000u;
 
     auto dma_k = [&](int T, int b) {
         const int key0 = T * KT;
@@ -202,9 +224,15 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         const auto rk = make_rsrc(kb + (size_t)key0 * D, rem * RB);
 #pragma unroll
         for (int u = 0; u < NU; ++u) dma_1k(rk, smem_lds + OFF_K + b * TK + (wave + WAVES * u) * KBS, voff_row[u]);
-        if (wave < RCH)
+        if constexpr (R < 8) {
+            if (wave < 4)
+                dma_256(make_rsrc(lk_ag + (size_t)(key0 + 16 * wave) * R,
+                                  (uint32_t)max((int)rem - 16 * wave, 0) * (2 * R)),
+                        smem_lds + OFF_LK + b * TLK + wave * 256, voff_l4);
+        } else if (wave < RCH) {
             dma_1k(make_rsrc(lk_ag + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LK + b * TLK + wave * 1024,
                    voff_l + 16 * wave);
+        }
         if constexpr (ROPE) {
             const auto rc = make_rsrc(a.rope_cos + (size_t)key0 * (D / 2), rem * RB);
             const auto rs = make_rsrc(a.rope_sin + (size_t)key0 * (D / 2), rem * RB);
@@ -222,12 +250,18 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) dma_1k(rv, smem_lds + OFF_V + b * TV + (wave + WAVES * u) * VBS, voff_row[u]);
         const int c = wave - 4;
-        if (c >= 0 && c < RCH)
+        if constexpr (R < 8) {
+            if (c >= 0)
+                dma_256(make_rsrc(lv_ag + (size_t)(key0 + 16 * c) * R,
+                                  (uint32_t)max((int)rem - 16 * c, 0) * (2 * R)),
+                        smem_lds + OFF_LV + b * TLV + c * 256, voff_l4);
+        } else if (c >= 0 && c < RCH) {
             dma_1k(make_rsrc(lv_ag + (size_t)key0 * R, rem * (2 * R)), smem_lds + OFF_LV + b * TLV + c * VBS,
                    voff_l + 16 * c);
+        }
     };
 
-    // constant chunks: L_v rank R = ones, further ranks zero; L_k padding zero
+    // constant chunks: L_v rank ONES_RANK = ones, further ranks zero; L_k padding zero
     for (int e = tid; e < 2 * (NLV - RCH) * KT; e += 512) {
         const int b = e / ((NLV - RCH) * KT);
         const int c = RCH + (e / KT) % (NLV - RCH);
@@ -649,6 +683,8 @@ lra_status launch_rope(const lra::PrefillArgs& p, hipStream_t s) {
     LRA_CASE(64, 16)
     LRA_CASE(64, 32)
     LRA_CASE(64, 8)
+    LRA_CASE(128, 4)
+    LRA_CASE(64, 4)
 #undef LRA_CASE
     lra::set_error("prefill: unsupported head_dim %d / rank %d", p.head_dim, p.rank);
     return LRA_ERR_UNSUPPORTED;

@@ -36,7 +36,8 @@
  *   - Element counts and layouts below are in elements of the storage type
  *     (dims->dtype): LRA_BF16 = bfloat16 bits, LRA_F32 = IEEE float.
  *     Accumulation is always fp32.  bf16 outputs are rounded to nearest even.
- *   - Supported: head_dim in {64, 128}, rank in {8, 16, 32},
+ *   - Supported: head_dim in {64, 128}, rank in {4, 8, 16, 32} (4: the rank of
+ *     the query/key/value/output LoRA setting, LRAgent App. D.1),
  *     n_q_heads % n_kv_heads == 0, page_size == 16.  Query heads map to KV
  *     head hq / (n_q_heads / n_kv_heads) (contiguous groups).
  */
@@ -68,7 +69,7 @@ typedef struct lra_dims {
     int32_t n_q_heads;   /* H_q */
     int32_t n_kv_heads;  /* H_kv; H_q % H_kv == 0 */
     int32_t head_dim;    /* d: 64 or 128 */
-    int32_t rank;        /* r: 8, 16 or 32 */
+    int32_t rank;        /* r: 4, 8, 16 or 32 */
     int32_t dtype;       /* LRA_F32 or LRA_BF16, for every tensor of the call */
     float softmax_scale; /* <= 0 selects 1/sqrt(head_dim) */
     /* 0: one LR cache shared by every agent (BaseLRShared, shared A).  > 0: one

@@ -66,7 +66,8 @@ def call_decode(dm, **over):
 
 @pytest.mark.parametrize("dm,over,want", [
     (dims(d=96), {}, 3),
-    (dims(r=4), {}, 3),
+    (dims(r=2), {}, 3),
+    (dims(r=12), {}, 3),
     (dims(dt=2), {}, 3),
     (dims(h_q=30, h_kv=8), {}, 2),
     (dims(h_q=0), {}, 2),
@@ -146,6 +147,7 @@ def test_lr_build_validation():
                                       a["ws"], a["wsz"], None)
 
     assert call(r=12) == 3
+    assert call(r=2) == 3
     assert call(dt=5) == 3
     assert call(d_model=100) == 3
     assert call(d_model=0) == 2
@@ -199,7 +201,8 @@ def call_expand(dm, **over):
 
 @pytest.mark.parametrize("dm,over,want", [
     (dims(dt=0), {}, 3),                     # the baseline is bf16 only
-    (dims(r=4), {}, 3),
+    (dims(r=2), {}, 3),
+    (dims(r=12), {}, 3),
     (dims(), {"page": 8}, 3),
     (dims(), {"out_blocks": 0}, 2),
     (dims(), {"out_blocks": 33}, 2),
@@ -269,4 +272,6 @@ def test_lr_build_workspace_size():
     # fp32 and rejected arguments need none
     assert ws(n_tok=4096, dtype=0) == 0
     assert ws(n_tok=4096, rank=12) == 0
+    # rank 4: partial rows padded to one 16-column tile
+    assert ws(n_tok=4096, rank=4) == 256 + 64 * 4 * 64 * 16 * 4
     assert ws(n_tok=0) == 0

@@ -53,6 +53,9 @@ SMALL = [
     ("g4 d64 r16 multi row-group", 4, 1, 64, 16, [300, 48], 6),
     ("g2 d128 r8", 8, 4, 128, 8, [2, 1500], 5),
     ("g16 d64 r32", 16, 1, 64, 32, [77, 4096], 1),
+    # rank 4: the query/key/value/output LoRA setting (LRAgent App. D.1)
+    ("g4 d128 r4", 32, 8, 128, 4, [1, 17, 300, 1025, 2049], 2),
+    ("g2 d64 r4", 8, 4, 64, 4, [50, 700], 3),
 ]
 
 
@@ -65,10 +68,11 @@ def test_decode_small_shuffled(label, h_q, h_kv, d, r, lens, rpc):
     _check(case)
 
 
-def test_decode_fp32_ragged():
+@pytest.mark.parametrize("r", [32, 4])
+def test_decode_fp32_ragged(r):
     reqs = [(0, 0), (0, 1), (1, 1), (2, 0)]
     case = w.make_decode(19, dtype="f32", ctx_lens=[1, 45, 300], reqs=reqs, n_agents=2, h_q=8,
-                         h_kv=2, d=128, r=32, shuffle=True, b_sigma=0.1, name="fp32 ragged")
+                         h_kv=2, d=128, r=r, shuffle=True, b_sigma=0.1, name=f"fp32 ragged r{r}")
     _check(case)
 
 

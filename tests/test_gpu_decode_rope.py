@@ -54,6 +54,9 @@ SMALL = [
     ("g2 d128 r8", 8, 4, 128, 8, [2, 1500], 5, 0.3),
     ("g16 d64 r32", 16, 1, 64, 32, [77, 4096], 1, 0.3),
     ("g1 d128 r32 sixteen requests", 4, 4, 128, 32, [700], 16, 0.3),
+    # rank 4 with RoPE on the adapter key: the pages' qkvo setting (App. D.1)
+    ("g4 d128 r4 qkvo rank", 32, 8, 128, 4, [33, 700, 1100], 2, 0.3),
+    ("g1 d64 r4", 8, 8, 64, 4, [5, 129], 3, 0.3),
 ]
 
 

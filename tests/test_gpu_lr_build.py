@@ -16,6 +16,8 @@ pytestmark = pytest.mark.gpu
     (4096, 4096, 16, "bf16", 131072),   # one layer of the 4096-new-token PreLRShared step
     (17, 96, 16, "f32", 3),
     (40, 4096, 32, "f32", 0),
+    (64, 512, 4, "bf16", 3),
+    (23, 256, 4, "f32", 1),
 ])
 def test_lr_build(n_tok, d_model, r, dtype, offset):
     import torch
@@ -55,6 +57,7 @@ def test_rope_tables_match_oracle():
     (1000, 4096, 32, 1),    # ragged last block, 8 ranges
     (77, 1024, 8, 3),       # three agents, 2 ranges
     (20000, 2048, 16, 1),   # no split (enough blocks): the 64-token kernel alone
+    (1000, 4096, 4, 2),     # rank 4: half of one 16-column tile
 ])
 def test_lr_build_split_matches_oracle_and_single_pass(n_tok, d_model, r, n_lr):
     """The d_model-split build (workspace given) against the oracle within one bf16 rounding,

@@ -26,6 +26,7 @@ CASES = [
     ("g4 d128 r16", 32, 8, 128, 16, [1, 300, 1500], 2),
     ("g1 d64 r8", 8, 8, 64, 8, [17, 64, 129], 3),
     ("g8 d128 r32", 16, 2, 128, 32, [2049, 33], 2),
+    ("g4 d128 r4", 32, 8, 128, 4, [300, 1100], 2),
 ]
 
 

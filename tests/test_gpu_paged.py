@@ -28,22 +28,23 @@ def _append(case, pools, ids, t0, t1):
     lra.cache_append(slots, k_new, v_new, dev(case.l_k[t0:t1]), dev(case.l_v[t0:t1]), *pools)
 
 
-def test_append_builds_the_page_layout():
+@pytest.mark.parametrize("r", [16, 4])
+def test_append_builds_the_page_layout(r):
     """Appending a whole context token range by range gives exactly the pools the
     layout helper builds (bit-exact), including a partial last page and skipped slots."""
     import torch
     import attention_shared_base_amd as lra
     case = w.make_prefill(61, dtype="bf16", kv_len=1000, q_len=8, req_agents=[0], n_agents=1,
-                          h_q=32, h_kv=8, d=128, r=16, name="append")
+                          h_q=32, h_kv=8, d=128, r=r, name="append")
     n_pages = 70
     ids = np.random.default_rng(3).permutation(n_pages)[:63]
-    pools = _pools_for(1000, 8, 128, 16, n_pages)
+    pools = _pools_for(1000, 8, 128, r, n_pages)
     for t0, t1 in ((0, 300), (300, 999), (999, 1000)):  # prefill chunks, then one decode token
         _append(case, pools, ids, t0, t1)
     # a negative slot is skipped
     neg = torch.full((1,), -1, dtype=torch.int64, device="cuda")
     junk = torch.ones((1, 8, 128), dtype=torch.bfloat16, device="cuda")
-    lra.cache_append(neg, junk, junk, junk[:, 0, :16].contiguous(), junk[:, 0, :16].contiguous(), *pools)
+    lra.cache_append(neg, junk, junk, junk[:, 0, :r].contiguous(), junk[:, 0, :r].contiguous(), *pools)
     kp, lkp = w.paginate(case.k_base, case.l_k, ids, n_pages, 16)
     vp, lvp = w.paginate(case.v_base, case.l_v, ids, n_pages, 16)
     want = w.decode_device_layout(kp, vp, lkp, lvp)

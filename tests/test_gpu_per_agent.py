@@ -41,6 +41,7 @@ CASES = [
     ("g4 d128 r16 four agents per context", 32, 8, 128, 16, [3000, 1, 1025], 4),
     ("g1 d64 r8 six requests (two row groups)", 8, 8, 64, 8, [300, 17], 6),
     ("g8 d128 r32", 16, 2, 128, 32, [2049, 64], 3),
+    ("g4 d128 r4", 32, 8, 128, 4, [1500, 40], 4),
 ]
 
 

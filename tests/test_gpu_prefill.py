@@ -42,6 +42,10 @@ SMALL = [
     ("g8 d128 r8 rope", 16, 2, 128, 8, 1000, 333, True),
     ("g16 d128 r16", 16, 1, 128, 16, 90, 17, False),
     ("g32 d64 r32 rope", 32, 1, 64, 32, 150, 9, True),
+    # rank 4 (query/key/value/output LoRA, App. D.1), with and without RoPE
+    ("g4 d128 r4", 32, 8, 128, 4, 300, 70, False),
+    ("g4 d128 r4 rope", 32, 8, 128, 4, 1000, 333, True),
+    ("g2 d64 r4 rope", 8, 4, 64, 4, 129, 129, True),
 ]
 
 
