@@ -185,17 +185,22 @@ class DecodeSet:
         self.out = None
 
 
-def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stats=None):
+def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stats=None, rank=16):
     import torch
     import attention_shared_base_amd as lra
     import workloads as w
-    cases = [w.config2(layer=i) for i in range(n_sets)]
+    if rank == 16:
+        cases = [w.config2(layer=i) for i in range(n_sets)]
+    else:  # the same shapes and draws at another rank
+        cases = [w.make_decode(2, dtype="bf16", ctx_lens=[8192] * 4, reqs=[(b // 4, b % 4) for b in range(16)],
+                               n_agents=4, h_q=32, h_kv=8, d=128, r=rank, shuffle=False, layer=i)
+                 for i in range(n_sets)]
     sets = [DecodeSet(c) for c in cases]
     c0 = cases[0]
     mrpc = int(np.bincount(c0.req_ctx).max())
     max_len = int(c0.ctx_len.max())
     ws = torch.zeros(lra.decode_workspace_size(
-        n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=c0.n_req,
+        n_q_heads=32, n_kv_heads=8, head_dim=128, rank=rank, dtype=1, n_req=c0.n_req,
         n_ctx=c0.n_ctx, max_req_per_ctx=mrpc, max_ctx_len=max_len,
         lr_agent_stride=1 if per_agent else 0), dtype=torch.uint8, device="cuda")
     for s in sets:
@@ -220,12 +225,12 @@ def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stat
     ms = _time_calls(call, n_sets, steps, warmup)
     if stats is not None:
         stats.update(_call_stats(call, n_sets, max(20, min(steps, 200))))
-    nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, 16)
+    nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, rank)
     if rope_theta is not None:
         nbytes += 2 * max_len * 64 * 4  # the cos / sin rows, read once
     if per_agent:  # every agent of a context reads its own L_k, L_v rows
         n_ag_ctx = len(np.unique(c0.req_agent[c0.req_ctx == 0]))
-        nbytes += int(c0.ctx_len.sum()) * 2 * 16 * 2 * (n_ag_ctx - 1)
+        nbytes += int(c0.ctx_len.sum()) * 2 * rank * 2 * (n_ag_ctx - 1)
     return cases[0], ms, nbytes
 
 
@@ -281,6 +286,24 @@ def extra_decode_rope(steps, warmup, base_ms):
                     "contexts, Hq32 Hkv8 d128 r16, theta 5e5, bf16",
         "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
         "time_vs_no_rope": ms / base_ms,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "algorithmic_bytes": nbytes,
+    }
+
+
+def extra_decode_qkvo_r4(steps, warmup):
+    """The pages' query/key/value/output LoRA setting (LRAgent App. D.1): rank 4 with RoPE on
+    the adapter key, against the plain rank-4 call on the same shapes (the cost of the key
+    rebuild at the pages' rank)."""
+    _, ms_plain, _ = primary_decode(steps, warmup, 4, rank=4)
+    case, ms, nbytes = primary_decode(steps, warmup, 4, rope_theta=500000.0, rank=4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "decode, rank-4 LoRA with RoPE on the adapter key (qkvo setting): 16 requests "
+                    "over 4 shared 8192-token contexts, Hq32 Hkv8 d128 r4, theta 5e5, bf16",
+        "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
+        "ms_per_call_without_rope": ms_plain, "time_vs_no_rope": ms / ms_plain,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
         "algorithmic_bytes": nbytes,
@@ -547,7 +570,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="decode_rope,decode_per_agent,naive_decode,prefill_rope,"
+    ap.add_argument("--extra", default="decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,prefill_rope,"
                                        "prefill_paged,paged_decode,lr_build,prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -581,6 +604,7 @@ def main():
     if not args.no_extra:
         legs = {"decode_rope": lambda: extra_decode_rope(args.steps, args.warmup, ms),
                 "decode_per_agent": lambda: extra_decode_per_agent(args.steps, args.warmup, ms),
+                "decode_qkvo_r4": lambda: extra_decode_qkvo_r4(args.steps, args.warmup),
                 "naive_decode": lambda: extra_naive_decode(max(5, args.steps // 10), 3, ms),
                 "prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
                 "prefill_paged": lambda: extra_prefill_paged(
