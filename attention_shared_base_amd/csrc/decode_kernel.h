@@ -116,9 +116,10 @@ constexpr int WAITCNT_VMCNT0 = 0x0f70;
 template <int DR>
 constexpr int MERGE_NG = (DR / 4 + 1 + 15) / 16;
 
-template <int D, int R, int SP>
+template <int D, int R, int SP, int NG>
 __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int own, int n_active, int nrows,
-                                               int n, int cl, float (*o)[SP], float* M_row, float* L_row);
+                                               int n, int cl, const f32x4 (&own_o)[NG], float own_m,
+                                               float own_l, float (*o)[SP], float* L_row);
 
 // NQ: LR caches read per step (1 shared; 4 = one per request slot of the group)
 template <int D, int R, int NQ = 1>
@@ -173,7 +174,6 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     __shared__ int sm_pid[ROPE ? CHUNK / PAGE : 1];
     __shared__ float sm_m[WAVES][ROWS];
     __shared__ float sm_l[WAVES][ROWS];
-    __shared__ float sm_M[ROWS];
     __shared__ float sm_L[ROWS];
     __shared__ int sm_last;
     // agent ids of the row group's requests.  Every thread writes every entry
@@ -682,40 +682,56 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     }
     __syncthreads();
 
+    // Thread (row n, phase cl) combines the wavefronts' partials for the
+    // 16-byte column groups cl, cl + 16, ... of its row (every column belongs
+    // to one thread) and keeps them in registers: the chunk partial goes to
+    // the workspace straight from there, and the merging workgroup starts from
+    // them.  static_assert: 256 threads = ROWS rows x 16 phases.
+    static_assert(64 * WAVES == ROWS * 16, "one thread per (row, column phase)");
     const int n = tid >> 4;   // row handled by this thread in the epilogues
     const int cl = tid & 15;  // column phase
-    if (tid < ROWS * 16) {
+    constexpr int NG = MERGE_NG<DR>;
+    f32x4 og[NG];
+    float M = -INFINITY, L = 0.f;
+    {
         float mw[WAVES];
-        float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             mw[w] = sm_m[w][n];
             M = fmaxf(M, mw[w]);
         }
         float wt[WAVES];
-        float L = 0.f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             wt[w] = (M == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
             L += wt[w] * sm_l[w][n];
         }
         // unrolled: the LDS reads of every column go out before the first wait
-        float o[(DR + 15) / 16];
 #pragma unroll
-        for (int k = 0; k < (DR + 15) / 16; ++k) {
-            const int c = min(cl + 16 * k, DR - 1);
-            o[k] = 0.f;
+        for (int k = 0; k < NG; ++k) {
+            const int gi = min(cl + 16 * k, DR / 4 - 1);
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) o[k] += wt[w] * sm_o[w][n][c];
-        }
+            for (int e = 0; e < 4; ++e) {
+                float o = 0.f;
 #pragma unroll
-        for (int k = 0; k < (DR + 15) / 16; ++k)  // each (n, c) is read and written by this thread only
-            if (cl + 16 * k < DR) sm_o[0][n][cl + 16 * k] = o[k];
-        if (cl == 0) {
-            sm_M[n] = M;
-            sm_L[n] = L;
+                for (int w = 0; w < WAVES; ++w) o += wt[w] * sm_o[w][n][4 * gi + e];
+                og[k][e] = o;
+            }
         }
     }
+    // the combined partial into LDS (columns 4 gi .. of this thread only), for
+    // the epilogue of a unit of one chunk
+    auto og_to_lds = [&]() {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const int gi = cl + 16 * k;
+            if (gi < DR / 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm_o[0][n][4 * gi + e] = og[k][e];
+            }
+        }
+        if (cl == 0) sm_L[n] = L;
+    };
 
     // B_v^(h) columns of this thread's output row (agent ids from LDS, so one
     // memory round trip).  Only the workgroup that finalizes the unit needs
@@ -752,19 +768,12 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         const int split_s = __builtin_amdgcn_readfirstlane(split);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             a.ws_part + ((size_t)unit_s * a.n_split + split_s) * ROWS * PW, (short)0, ROWS * PW * 4, 0x00020000);
-        __syncthreads();
         if (n < nrows) {
 #pragma unroll
-            for (int k = 0; k < MERGE_NG<DR>; ++k) {
+            for (int k = 0; k < NG; ++k) {
                 const int gi = cl + 16 * k;  // 16-byte group of the row: columns 4 gi .. 4 gi + 3, then (m, l)
                 if (gi <= DR / 4) {
-                    f32x4 v;
-                    if (gi < DR / 4) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = sm_o[0][n][4 * gi + e];
-                    } else {
-                        v = f32x4{sm_M[n], sm_L[n], 0.f, 0.f};
-                    }
+                    const f32x4 v = gi < DR / 4 ? og[k] : f32x4{M, L, 0.f, 0.f};
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (n * PW + 4 * gi) * 4, 0, CPOL_SC1);
                 }
             }
@@ -779,10 +788,11 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         __syncthreads();
         if (!sm_last) return;
         load_bv();
-        merge_partials<D, R, SP>(a, unit_s, split_s, n_active, nrows, n, cl, sm_o[0], sm_M, sm_L);
+        merge_partials<D, R, SP, NG>(a, unit_s, split_s, n_active, nrows, n, cl, og, M, L, sm_o[0], sm_L);
         if (tid == 0) __hip_atomic_store(a.ws_count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
         load_bv();
+        og_to_lds();
     }
     __syncthreads();
     finalize_rows<D, R, SP>(a, sm_o[0], sm_L, n, cl, nrows, req0, h, bvc);
@@ -872,18 +882,19 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 
 // Log-sum-exp merge of the chunk partials of one work unit into o[row][0..DR)
 // and L[row].  Runs in the last workgroup to finish, whose own partial (chunk
-// `own`) is still in o / M_row / L_row and is taken from there; the others are
-// read from the workspace.  Chunks are combined in chunk order whichever
+// `own`) is still in registers (own_o: this thread's column groups, own_m,
+// own_l) and is taken from there; the others are read from the workspace.  Chunks are combined in chunk order whichever
 // workgroup merges, so repeated calls give identical bits.  Thread (row n,
 // phase cl) owns the 16-byte column groups cl, cl + 16, ... of the row and
 // reads every partial's (m, l); the partials of up to GB chunks are requested
 // together, so a merge of <= GB chunks waits for one memory round trip.
-template <int D, int R, int SP>
+template <int D, int R, int SP, int NG>
 __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int own, int n_active, int nrows,
-                                               int n, int cl, float (*o)[SP], float* M_row, float* L_row) {
+                                               int n, int cl, const f32x4 (&own_o)[NG], float own_m,
+                                               float own_l, float (*o)[SP], float* L_row) {
     constexpr int DR = D + R;
     constexpr int PW = DR + 4;
-    constexpr int NG = MERGE_NG<DR>;
+    static_assert(NG == MERGE_NG<DR>, "column groups per thread");
     constexpr int GB = 8;  // chunks per batch
     // `unit` and `own` are wave-uniform (scalar): the descriptor stays in
     // scalar registers and the row is part of the per-lane offset
@@ -894,14 +905,7 @@ __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int o
     const uint32_t sstride = ROWS * PW * 4;  // bytes between chunks
     const uint32_t row_off = (uint32_t)n * PW * 4;
     // the own partial, in the layout of a loaded one
-    const f32x4 own_ml = f32x4{M_row[n], L_row[n], 0.f, 0.f};
-    f32x4 own_o[NG];
-#pragma unroll
-    for (int k = 0; k < NG; ++k) {
-        const int gi = min(cl + 16 * k, DR / 4 - 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) own_o[k][e] = o[n][4 * gi + e];
-    }
+    const f32x4 own_ml = f32x4{own_m, own_l, 0.f, 0.f};
     float M = -INFINITY, L = 0.f;
     f32x4 acc[NG];
 #pragma unroll
