@@ -65,11 +65,14 @@ __global__ __launch_bounds__(256) void lra_cache_append_kernel(PagedK a) {
     }
 }
 
-// Gather: workgroup = (block b of the context, KV head h), 256 threads.  The
-// dim-major V page is turned into rows through LDS.
+// Gather: workgroup = (block b of the context, KV head h), 256 threads.  Every
+// access is 16 bytes: K chunks move as they are; the dim-major V page (32
+// bytes per dim) is turned into rows through LDS (a 16-byte read of 8 tokens
+// of one dim, scattered to the 8 rows; then each thread writes 8 dims of one
+// row); the LR rows of the block go with head 0.
 template <int D, int R>
 __global__ __launch_bounds__(256) void lra_cache_gather_kernel(PagedK a) {
-    __shared__ bf16 s_v[D][PAGE + 2];
+    __shared__ __attribute__((aligned(16))) bf16 s_v[PAGE][D + 8];  // row pitch D + 8: 16-byte aligned rows
     const int b = blockIdx.x / a.h_kv;
     const int h = blockIdx.x % a.h_kv;
     const int key0 = b * PAGE;
@@ -78,19 +81,28 @@ __global__ __launch_bounds__(256) void lra_cache_gather_kernel(PagedK a) {
     const size_t kv_page = (size_t)a.h_kv * D * PAGE;
     const bf16* kp = a.k_pool + (size_t)pid * kv_page + (size_t)h * D * PAGE;
     const bf16* vp = a.v_pool + (size_t)pid * kv_page + (size_t)h * D * PAGE;
-    for (int e = threadIdx.x; e < (D / 8) * PAGE; e += blockDim.x) {
+    const int tid = threadIdx.x;
+    // K: chunk e = (dim group e / PAGE, token e % PAGE)
+    for (int e = tid; e < (D / 8) * PAGE; e += blockDim.x) {
         const int dg = e / PAGE, t = e % PAGE;
-        if (t < n)
-            *(bf16x8*)(a.k_out + ((size_t)h * a.kv_len + key0 + t) * D + 8 * dg) = *(const bf16x8*)(kp + e * 8);
+        const bf16x8 v = *(const bf16x8*)(kp + (size_t)e * 8);
+        if (t < n) *(bf16x8*)(a.k_out + ((size_t)h * a.kv_len + key0 + t) * D + 8 * dg) = v;
     }
-    for (int e = threadIdx.x; e < D * PAGE; e += blockDim.x) s_v[e / PAGE][e % PAGE] = vp[e];
+    // V: chunk e = (dim e / 2, tokens 8 (e % 2) ..)
+    for (int e = tid; e < D * 2; e += blockDim.x) {
+        const int c = e / 2, t0 = 8 * (e % 2);
+        const bf16x8 v = *(const bf16x8*)(vp + (size_t)e * 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_v[t0 + j][c] = v[j];
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < PAGE * D; e += blockDim.x) {
-        const int t = e / D, c = e % D;
-        if (t < n) a.v_out[((size_t)h * a.kv_len + key0 + t) * D + c] = s_v[c][t];
+    for (int e = tid; e < PAGE * (D / 8); e += blockDim.x) {
+        const int t = e / (D / 8), cg = e % (D / 8);
+        if (t < n)
+            *(bf16x8*)(a.v_out + ((size_t)h * a.kv_len + key0 + t) * D + 8 * cg) = *(const bf16x8*)&s_v[t][8 * cg];
     }
     if (h == 0) {
-        for (int e = threadIdx.x; e < PAGE * R; e += blockDim.x) {
+        for (int e = tid; e < PAGE * R; e += blockDim.x) {
             const int t = e / R, rk = e % R;
             if (t < n) {
                 a.lk_out[(size_t)(key0 + t) * R + rk] = a.lk_pool[((size_t)pid * PAGE + t) * R + rk];
