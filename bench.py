@@ -234,6 +234,37 @@ def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stat
     return cases[0], ms, nbytes
 
 
+def extra_workload1_fp32(steps, warmup):
+    """The fp32 parity workload (2 agents over one 256-token context, Hq4 Hkv2 d64 r8): call time
+    of its decode (2 requests) and its causal prefill (2 x 16 new tokens).  Launch-latency bound
+    (a 278 KB working set); reported as time only."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    dec, pre = w.config1()
+    s = DecodeSet(dec)
+    d_out = torch.empty_like(s.q)
+    q, agent = _dev(pre.q), _dev(pre.req_agent)
+    k, v, lk, lv, bk, bv = map(_dev, (pre.k_base, pre.v_base, pre.l_k, pre.l_v, pre.b_k, pre.b_v))
+    p_out = torch.empty_like(q)
+
+    def call_d(_):
+        lra.decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
+                   max_req_per_ctx=2, max_ctx_len=256, out=d_out)
+
+    def call_p(_):
+        lra.prefill(q, agent, k, v, lk, lv, bk, bv, out=p_out)
+
+    ms_d = _time_calls(call_d, 1, steps, warmup)
+    ms_p = _time_calls(call_p, 1, steps, warmup)
+    return {"workload": "fp32 parity workload: 2 agents over one 256-token context (240 + 16 new), "
+                        "Hq4 Hkv2 d64 r8; decode of 2 requests and prefill of 2 x 16 tokens",
+            "value": ms_d * 1e3, "unit": "us per decode call", "ms_per_call": ms_d,
+            "prefill_us_per_call": ms_p * 1e3,
+            "roofline": None,
+            "note": "launch-latency bound (278 KB working set): time only, no roofline"}
+
+
 def extra_paged_decode(steps, warmup):
     """32 contexts of U[4096, 65536] tokens, shuffled 16-token pages, r 32 (5+ GB)."""
     import torch
@@ -570,7 +601,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,prefill_rope,"
+    ap.add_argument("--extra", default="workload1_fp32,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,prefill_rope,"
                                        "prefill_paged,paged_decode,lr_build,prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -611,6 +642,7 @@ def main():
                     max(5, args.steps // 10), 3,
                     extra.get("prefill_rope", {}).get("ms_per_call")),
                 "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
+                "workload1_fp32": lambda: extra_workload1_fp32(args.steps, 10),
                 "lr_build": lambda: extra_lr_build(args.steps, 10),
                 "prelr_step": lambda: extra_prelr_step(1, 1)}
         for name in [x for x in args.extra.split(",") if x]:
@@ -618,8 +650,9 @@ def main():
             _log(f"extra: {name}")
             try:
                 extra[name] = fn()
-                _log(f"extra: {name}: {extra[name]['value']:.4g} {extra[name]['unit']}, "
-                     f"{extra[name]['roofline']['frac'] * 100:.1f}% of peak")
+                rl = extra[name].get("roofline")
+                _log(f"extra: {name}: {extra[name]['value']:.4g} {extra[name]['unit']}"
+                     + (f", {rl['frac'] * 100:.1f}% of peak" if rl else ""))
             except lra.LraError as e:
                 extra[name] = {"error": str(e)}
                 _log(f"extra: {name}: {e}")
