@@ -86,7 +86,17 @@ __device__ void row_attend(const F32K& a, const Acc& acc, const float* qrow, int
     const float* bk = a.b_k + (size_t)agent * r * bstride + (size_t)h * d;
     const float* bv = a.b_v + (size_t)agent * r * bstride + (size_t)h * d;
     for (int c = lane; c < d; c += 64) s_q[c] = qrow[c];
-    for (int e = lane; e < r * d; e += 64) s_bk[e] = bk[(size_t)(e / d) * bstride + e % d];
+    // B_k^(h) slice, eight loads per lane in flight at a time (r * d is a multiple of 512)
+    for (int e0 = lane; e0 < r * d; e0 += 512) {
+        float bb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + 64 * u;
+            bb[u] = bk[(size_t)(e / d) * bstride + e % d];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s_bk[e0 + 64 * u] = bb[u];
+    }
     __syncthreads();
     if (lane < r) {
         float t = 0.f;
@@ -104,8 +114,21 @@ __device__ void row_attend(const F32K& a, const Acc& acc, const float* qrow, int
         if (j < n_vis) {
             float dot = 0.f;
             if (!rope) {
-                for (int c = 0; c < d; ++c) dot += s_q[c] * acc.K(j, c);
-                for (int t = 0; t < r; ++t) dot += s_qb[t] * acc.LK(j, t);
+                // loads requested eight (four) at a time; FMAs in dimension order
+                for (int c = 0; c < d; c += 8) {  // d is a multiple of 8
+                    float kv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) kv[u] = acc.K(j, c + u);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) dot += s_q[c + u] * kv[u];
+                }
+                for (int t = 0; t < r; t += 4) {  // r is a multiple of 4
+                    float lv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) lv[u] = acc.LK(j, t + u);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) dot += s_qb[t + u] * lv[u];
+                }
             } else {
                 // rebuild the adapter key at head dimension, rotate it, add to K_base
                 const int half = d / 2;
@@ -136,11 +159,27 @@ __device__ void row_attend(const F32K& a, const Acc& acc, const float* qrow, int
         o0 *= alpha;
         o1 *= alpha;
         olr *= alpha;
-        for (int jj = 0; jj < nk; ++jj) {
-            const float pj = s_p[jj];
-            if (lane < d) o0 += pj * acc.V(c0 + jj, lane);
-            if (lane + 64 < d) o1 += pj * acc.V(c0 + jj, lane + 64);
-            if (lane < r) olr += pj * acc.LV(c0 + jj, lane);
+        // eight keys' values are requested before their FMAs (one memory round
+        // trip per eight keys); the FMAs keep key order, so the result is the
+        // same as key by key
+        for (int jj0 = 0; jj0 < nk; jj0 += 8) {
+            float v0[8], v1[8], vl[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = c0 + min(jj0 + u, nk - 1);
+                v0[u] = lane < d ? acc.V(j, lane) : 0.f;
+                v1[u] = lane + 64 < d ? acc.V(j, lane + 64) : 0.f;
+                vl[u] = lane < r ? acc.LV(j, lane) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (jj0 + u < nk) {
+                    const float pj = s_p[jj0 + u];
+                    if (lane < d) o0 += pj * v0[u];
+                    if (lane + 64 < d) o1 += pj * v1[u];
+                    if (lane < r) olr += pj * vl[u];
+                }
+            }
         }
         __syncthreads();
     }
@@ -149,7 +188,13 @@ __device__ void row_attend(const F32K& a, const Acc& acc, const float* qrow, int
     const float inv = 1.0f / l;
     for (int c = lane, k = 0; c < d; c += 64, ++k) {
         float o = (k == 0) ? o0 : o1;
-        for (int t = 0; t < r; ++t) o += s_olr[t] * bv[(size_t)t * bstride + c];
+        for (int t0 = 0; t0 < r; t0 += 4) {  // four B_v rows in flight; FMAs in rank order
+            float bb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bb[u] = bv[(size_t)(t0 + u) * bstride + c];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o += s_olr[t0 + u] * bb[u];
+        }
         orow[c] = o * inv;
     }
 }
