@@ -1,8 +1,9 @@
-"""HIP-graph capture of the hot path: an LR-cache build (split over d_model, workspace in use),
-a RoPE prefill and a split-K decode recorded once in a torch CUDA graph, then replayed with new
-inputs copied in eagerly between replays.  Every replay equals the eager calls on the same inputs
-bit for bit, and eager calls between replays still do: the kernels take fixed buffers, reset their
-own workspace counters and add no memset nodes."""
+"""HIP-graph capture and stream concurrency of the hot path.  An LR-cache build (split over
+d_model, workspace in use), a RoPE prefill and a split-K decode are recorded once in a torch CUDA
+graph, then replayed with new inputs copied in eagerly between replays: every replay equals the
+eager calls on the same inputs bit for bit, and eager calls between replays still do (the kernels
+take fixed buffers, reset their own workspace counters and add no memset nodes).  Two decode
+streams with their own workspaces running at once equal the same calls run in turn."""
 import numpy as np
 import pytest
 
@@ -97,3 +98,36 @@ def test_graph_replays_equal_eager():
     # the decode workspace's per-unit counters and queue words are back at zero
     n_units = 2 * 8
     assert int(d_ws[:4 * (n_units + 2)].view(torch.int32).abs().sum()) == 0
+
+
+def test_concurrent_streams_equal_sequential():
+    """Two decode calls with their own workspaces on two streams (default priority) running at
+    the same time give the bits of the same calls run one after the other: the library keeps no
+    global mutable state between calls."""
+    import torch
+    import attention_shared_base_amd as lra
+    cases = [w.make_decode(95 + i, dtype="bf16", ctx_lens=[4000, 2500], reqs=[(0, 0), (0, 1), (1, 1)],
+                           n_agents=2, h_q=32, h_kv=8, d=128, r=16, shuffle=True, name=f"stream {i}")
+             for i in range(2)]
+    devs = [DecodeDev(c) for c in cases]
+    wss = [torch.zeros(lra.decode_workspace_size(
+        n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=3, n_ctx=2,
+        max_req_per_ctx=d.max_req_per_ctx, max_ctx_len=d.max_ctx_len), dtype=torch.uint8,
+        device="cuda") for d in devs]
+    outs = [torch.empty_like(d.q) for d in devs]
+    for d, o, ws in zip(devs, outs, wss):
+        d.run(out=o, workspace=ws)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(5):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        for d, o, ws, st in zip(devs, outs, wss, streams):
+            with torch.cuda.stream(st):
+                for _ in range(3):
+                    d.run(out=o, workspace=ws)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], ref[i]), f"stream {i}, round {rep}"
