@@ -19,8 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "liblra_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.hip", "decode_bf16.hip", "decode_rope_bf16.hip", "prefill_bf16.hip", "attn_f32.hip",
-           "lr_build.hip", "naive_expand.hip", "paged.hip"]
+SOURCES = ["api.hip", "decode_bf16.hip", "decode_pa_bf16.hip", "decode_rope_bf16.hip", "prefill_bf16.hip",
+           "attn_f32.hip", "lr_build.hip", "naive_expand.hip", "paged.hip"]
 # per-source extra flags: the RoPE decode keeps MFMA results in VGPRs (its rotation
 # reads them on the VALU)
 EXTRA_FLAGS = {"decode_rope_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -1,10 +1,12 @@
-// Paged decode entry: plain and per-agent-LR modes of the decode kernel
-// (decode_kernel.h); the RoPE mode is built in decode_rope_bf16.hip.
+// Paged decode entry: the shared-LR mode of the decode kernel (decode_kernel.h);
+// the per-agent-LR mode is built in decode_pa_bf16.hip and the RoPE mode in
+// decode_rope_bf16.hip (translation units of their own, compiled in parallel).
 #include "decode_kernel.h"
 
 namespace lra {
 
 lra_status launch_decode_rope_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+lra_status launch_decode_pa_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 
 lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
     const int d = a.head_dim, r = a.rank;
@@ -15,10 +17,9 @@ lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStrea
         }
         return launch_decode_rope_bf16(a, p, s);
     }
-    const bool per_agent = a.lr_stride != 0;
-#define LRA_CASE(D_, R_)            \
-    if (d == D_ && r == R_)         \
-        return per_agent ? launch_dr<D_, R_, MODE_PER_AGENT>(a, p, s) : launch_dr<D_, R_, MODE_SHARED>(a, p, s);
+    if (a.lr_stride != 0) return launch_decode_pa_bf16(a, p, s);
+#define LRA_CASE(D_, R_) \
+    if (d == D_ && r == R_) return launch_dr<D_, R_, MODE_SHARED>(a, p, s);
     LRA_CASE(128, 16)
     LRA_CASE(128, 32)
     LRA_CASE(128, 8)
