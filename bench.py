@@ -396,6 +396,57 @@ def extra_naive_decode(steps, warmup, base_ms):
     }
 
 
+def extra_agent_scaling(steps, warmup):
+    """Cross-agent cache sharing: the primary workload's 4 shared 8192-token contexts (two
+    rotated sets of caches) decoded by 1, 2, 4, 8 and 16 requests per context, each with its own
+    agent (B_k, B_v), beside the naive baseline that materialises every request's caches.  A row
+    group holds 16 query rows (4 requests at 4 query heads per KV head): up to 4 agents per context
+    every K/V page is read once, beyond that once per row group."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    sets = [DecodeSet(w.config2(layer=i)) for i in range(2)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    n_ag = 16
+    b_k = _randn_bf16((n_ag, 16, 8 * 128), 0.05, g)
+    b_v = _randn_bf16((n_ag, 16, 8 * 128), 0.05, g)
+    table = {}
+    for rpc in (1, 2, 4, 8, 16):
+        n_req = 4 * rpc
+        qs = [_randn_bf16((n_req, 32, 128), 1.0, g) for _ in sets]
+        crs = torch.arange(0, n_req + 1, rpc, dtype=torch.int32, device="cuda")
+        agent = torch.arange(n_req, dtype=torch.int32, device="cuda") % rpc
+        out = torch.empty((n_req, 32, 128), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(max(16, lra.decode_workspace_size(
+            n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=n_req, n_ctx=4,
+            max_req_per_ctx=rpc, max_ctx_len=8192)), dtype=torch.uint8, device="cuda")
+        scratch = {}
+
+        def call(i):
+            st = sets[i]
+            lra.decode(qs[i], crs, agent, st.k, st.v, st.lk, st.lv, st.bt, st.clen, b_k, b_v,
+                       max_req_per_ctx=rpc, max_ctx_len=8192, out=out, workspace=ws)
+
+        def call_naive(i):
+            st = sets[i]
+            lra.naive_decode(qs[i], crs, agent, st.k, st.v, st.lk, st.lv, st.bt, st.clen, b_k, b_v,
+                             max_req_per_ctx=rpc, max_ctx_len=8192, scratch=scratch)
+
+        ms = _time_calls(call, len(sets), steps, warmup)
+        ms_naive = _time_calls(call_naive, len(sets), max(4, steps // 20), 2)
+        table[str(rpc)] = {"decode_us": ms * 1e3, "naive_us": ms_naive * 1e3,
+                           "decode_tokens_per_s": n_req / (ms * 1e-3)}
+        del scratch, ws
+        torch.cuda.empty_cache()
+    t1, t4, t16 = (table[k]["decode_us"] for k in ("1", "4", "16"))
+    return {"workload": "decode over 4 shared 8192-token contexts, Hq32 Hkv8 d128 r16, with 1, 2, 4, "
+                        "8, 16 requests (agents) per context; method and naive materialising baseline",
+            "value": t4 / t1, "unit": "x (time at 4 agents per context / time at 1)",
+            "time_16_vs_1": t16 / t1, "per_agents": table, "roofline": None,
+            "note": "scaling study: sharing the base and LR caches across agents"}
+
+
 def extra_prefill_rope(steps, warmup, n_sets=2):
     """512 new tokens over a 16384-token shared context, 4 agents, RoPE 5e5 on the adapter key."""
     import torch
@@ -601,7 +652,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="workload1_fp32,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,prefill_rope,"
+    ap.add_argument("--extra", default="workload1_fp32,agent_scaling,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,prefill_rope,"
                                        "prefill_paged,paged_decode,lr_build,prelr_step",
                     help="comma-separated extra legs to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -643,6 +694,7 @@ def main():
                     extra.get("prefill_rope", {}).get("ms_per_call")),
                 "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
                 "workload1_fp32": lambda: extra_workload1_fp32(args.steps, 10),
+                "agent_scaling": lambda: extra_agent_scaling(max(20, args.steps // 2), 5),
                 "lr_build": lambda: extra_lr_build(args.steps, 10),
                 "prelr_step": lambda: extra_prelr_step(1, 1)}
         for name in [x for x in args.extra.split(",") if x]:
