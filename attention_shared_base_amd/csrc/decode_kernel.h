@@ -800,17 +800,18 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 
     if (!a.persistent) {
         // one item per workgroup.  XCD-aware placement: workgroup b runs on XCD
-        // b % 8; remap so that the KV heads of one (context, chunk) — which
-        // share its L_k/L_v pages — are consecutive on one XCD and hit the same L2.
+        // b % 8; remap so that the KV heads and row groups of one (context,
+        // chunk) — which share its L_k/L_v pages, and per head its K/V pages —
+        // are consecutive on one XCD and hit the same L2 at about the same time.
         const int nb = gridDim.x;
         const int b = blockIdx.x;
         const int bp = (b & 7) * (nb >> 3) + (b >> 3);
         const int h = bp % a.h_kv;
         int rest = bp / a.h_kv;
-        const int split = rest % a.n_split;
-        rest /= a.n_split;
         const int rg = rest % a.n_rg;
-        const int ctx = rest / a.n_rg;
+        rest /= a.n_rg;
+        const int split = rest % a.n_split;
+        const int ctx = rest / a.n_split;
         if (ctx < a.n_ctx) process(ctx, rg, h, split, nullptr, nullptr);
         return;
     }
