@@ -75,6 +75,7 @@ struct DecodeK {
     int32_t n_ctx, n_pages, max_blocks, n_agents;
     int32_t h_q, h_kv, g, rpg, n_rg, n_split;
     int32_t n_units;
+    int32_t n_req;
     int32_t persistent;  // 1: workgroups pull (context, row group, head, chunk) items from a queue
     float scale_log2;
     const float* rope_cos;  // RoPE: [rope_rows, D/2] tables of the keys' positions
@@ -153,6 +154,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     constexpr bool ROPE = MODE == MODE_ROPE;
     constexpr bool PA = MODE == MODE_PER_AGENT;
     constexpr int NQ = PA ? PA_REQ : 1;
+    // request -> agent table fetched at kernel start (see below); the RoPE and
+    // per-agent rank-32 instances keep scalar loads, as their registers are full
+    constexpr bool AGENT_TAB = !ROPE && !(PA && R == 32);
     using StepT = Step<D, R, NQ>;
     constexpr int NJ = StepT::NJ;
     constexpr int NDT = StepT::NDT;
@@ -198,6 +202,16 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                  "s"(a.ctx_len), "s"(a.ctx_req_start), "s"(a.q), "s"(a.b_k), "s"(a.req_agent));
     asm volatile("" ::"s"(a.n_ctx), "s"(a.n_pages), "s"(a.max_blocks), "s"(a.n_agents), "s"(a.h_q),
                  "s"(a.h_kv), "s"(a.g), "s"(a.rpg), "s"(a.n_rg), "s"(a.n_split));
+    // agent ids of requests 0..63 (lane i: request i), fetched by one vector load
+    // before any cache load.  With up to 64 requests the prologue takes its
+    // group's ids from here instead of a dependent scalar load, which would queue
+    // behind every CU's first cache loads; a wait for this load never waits for
+    // those.  Entries past n_req read as zero through the buffer range.
+    int agent_tab = 0;
+    if constexpr (AGENT_TAB)
+        agent_tab = (int)__builtin_amdgcn_raw_buffer_load_b32(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.req_agent), (short)0, 4 * min(a.n_req, 64), 0x00020000),
+            4 * lane, 0, 0);
 
     // ---- one work item: chunk `split` of row group rg of context ctx, KV head h
     // `queue`: persistent mode's queue (NULL otherwise); the next item's index is
@@ -287,11 +301,23 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     const bf16* kbase = a.k_pool + (size_t)h * D * PAGE;
     const bf16* vbase = a.v_pool + (size_t)h * D * PAGE;
 
-    // agent ids of the group's first four requests: requested before the step
-    // loads, so that waiting for them does not wait for those
+    // agent ids of the group's first four requests, from the table above; with
+    // more than 64 requests, from a table reloaded at the group's first request
     int agent0[4];
+    if constexpr (AGENT_TAB) {
+        int tab = agent_tab, tab0 = 0;
+        if (a.n_req > 64) {
+            tab = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.req_agent), (short)0, 4 * a.n_req, 0x00020000),
+                4 * (req0 + lane), 0, 0);
+            tab0 = req0;
+        }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) agent0[u] = a.req_agent[req0 + min(u, nreq - 1)];
+        for (int u = 0; u < 4; ++u) agent0[u] = __builtin_amdgcn_readlane(tab, req0 - tab0 + min(u, nreq - 1));
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) agent0[u] = a.req_agent[req0 + min(u, nreq - 1)];
+    }
     // per-agent LR caches: the step loads address the agents' pools
     int agent_of[4];
 #pragma unroll
@@ -360,15 +386,6 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     };
 
 
-    // ---- the first DEPTH-1 steps' loads go out before the prologue's dependent chain
-    StepT buf[DEPTH];
-#pragma unroll
-    for (int i = 0; i < DEPTH - 1; ++i)
-        if (i < NPRE) load(buf[i], pid[i]);
-    StepRope<D> rope_buf;
-    if constexpr (ROPE) load_rope(rope_buf, 0);
-    __builtin_amdgcn_sched_barrier(0);
-
     // ---- query operand (B of the score MFMA): lane holds dims 32j+8*q4.. of row
     // n16.  Loaded unconditionally (rows past nrows read row 0 and are zeroed
     // just before use): a branch here would drain the step loads in flight.
@@ -390,6 +407,43 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         }
     }
 
+    // ---- B_k rows of one group of four requests (operands of the pre-projection
+    // below).  With the agent table the first group's go out here, with the
+    // query, ahead of the first step's cache loads: loads complete in issue
+    // order, so the pre-projection then waits for neither the stream nor a
+    // scalar round trip queued behind it.
+    const size_t bcols = (size_t)a.h_kv * D;
+    auto bk_issue = [&](const int s0, bf16x8 (&bk)[4][NRT][NJ]) __attribute__((always_inline)) {
+        int agent[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) agent[u] = s0 == 0 ? agent0[u] : a.req_agent[req0 + min(s0 + u, nreq - 1)];
+        asm volatile("" ::"s"(agent[0]), "s"(agent[1]), "s"(agent[2]), "s"(agent[3]));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sm_agent[s0 + u] = agent[u];  // s0 + u < 16: s0 < nreq <= 16
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ag = min(max(agent[u], 0), a.n_agents - 1);
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int rank = 16 * rt + n16;
+                const bf16* bp_ = a.b_k + ((size_t)ag * R + min(rank, R - 1)) * bcols + (size_t)h * D + 8 * q4;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bk[u][rt][j] = ldg((const bf16x8*)(bp_ + 32 * j));
+            }
+        }
+    };
+    bf16x8 bk0[4][NRT][NJ];
+    if constexpr (AGENT_TAB) bk_issue(0, bk0);
+
+    // ---- then the first DEPTH-1 steps' loads, before the prologue's dependent chain
+    StepT buf[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i)
+        if (i < NPRE) load(buf[i], pid[i]);
+    StepRope<D> rope_buf;
+    if constexpr (ROPE) load_rope(rope_buf, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- pre-projection qB = q B_k^(h)T, one MFMA tile per request of the group.
     // C lane layout: rank 16*rt + 4*q4 + v of row n16 — already the B operand
     // layout of the rank-r score MFMA.  The agent ids of up to four requests
@@ -398,7 +452,6 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     f32x4 qbacc[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) qbacc[rt] = zf4();
-    const size_t bcols = (size_t)a.h_kv * D;
     if constexpr (ROPE) {
         // ---- RoPE: stage B_k^(h)T of every request of the group in LDS as the A
         // operand of dK^T = B_k^(h)T L_k^T: entry (request u, dim tile, lane l)
@@ -455,30 +508,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         }
         __syncthreads();
     } else {
-    for (int s0 = 0; s0 < nreq; s0 += 4) {
-        int agent[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) agent[u] = s0 == 0 ? agent0[u] : a.req_agent[req0 + min(s0 + u, nreq - 1)];
-        asm volatile("" ::"s"(agent[0]), "s"(agent[1]), "s"(agent[2]), "s"(agent[3]));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sm_agent[s0 + u] = agent[u];  // s0 + u < 16: s0 < nreq <= 16
-        bf16x8 bk[4][NRT][NJ];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int ag = min(max(agent[u], 0), a.n_agents - 1);
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                const int rank = 16 * rt + n16;
-                const bf16* bp_ = a.b_k + ((size_t)ag * R + min(rank, R - 1)) * bcols + (size_t)h * D + 8 * q4;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) bk[u][rt][j] = ldg((const bf16x8*)(bp_ + 32 * j));
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // every B_k load issued before the first wait
-        if (s0 == 0) {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) qf[j] = row_ok ? qf[j] : zero8();
-        }
+    auto bk_mfma = [&](const int s0, const bf16x8 (&bk)[4][NRT][NJ]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -489,6 +519,19 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                     c = mfma16x16x32(16 * rt + n16 < R ? bk[u][rt][j] : zero8(), qf[j], c);
                 if (n16 / g == s0 + u) qbacc[rt] = c;
             }
+    };
+    if constexpr (!AGENT_TAB) {
+        bk_issue(0, bk0);
+        __builtin_amdgcn_sched_barrier(0);  // every B_k load issued before the first wait
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qf[j] = row_ok ? qf[j] : zero8();
+    bk_mfma(0, bk0);
+    for (int s0 = 4; s0 < nreq; s0 += 4) {
+        bf16x8 bk[4][NRT][NJ];
+        bk_issue(s0, bk);
+        __builtin_amdgcn_sched_barrier(0);  // every B_k load issued before the first wait
+        bk_mfma(s0, bk);
     }
     }
     bf16x8 qb;
@@ -1021,6 +1064,7 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.n_rg = p.n_rg;
     k.n_split = p.n_split;
     k.n_units = p.n_units;
+    k.n_req = a.n_req;
     k.persistent = p.persistent;
     k.scale_log2 = a.scale * LRA_LOG2E;
     k.rope_cos = a.rope_cos;

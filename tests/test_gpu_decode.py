@@ -68,6 +68,16 @@ def test_decode_small_shuffled(label, h_q, h_kv, d, r, lens, rpc):
     _check(case)
 
 
+def test_decode_more_than_64_requests():
+    """85 requests over 29 contexts of 3 (the row groups straddle request 64): past 64
+    requests the kernel reads each group's agent ids from a table loaded at the group's
+    first request instead of the one it fetches for requests 0..63."""
+    lens = [(97 * c) % 700 + 1 for c in range(29)]
+    reqs = [(c, (c + 2 * i) % 5) for c in range(29) for i in range(3)][:85]
+    case = w.make_decode(43, dtype="bf16", ctx_lens=lens, reqs=reqs, n_agents=5, h_q=8, h_kv=2,
+                         d=64, r=8, name="85 requests")
+    _check(case)
+
 @pytest.mark.parametrize("r", [32, 4])
 def test_decode_fp32_ragged(r):
     reqs = [(0, 0), (0, 1), (1, 1), (2, 0)]
