@@ -162,7 +162,11 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     constexpr int NDT = StepT::NDT;
     constexpr int NRT = StepT::NRT;
     constexpr int DR = D + R;
-    constexpr int SP = DR + 1;  // LDS row pitch (odd: no bank aliasing across rows)
+    // LDS row pitch: 4 x an odd number of floats, so rows start 16-byte aligned
+    // (vector reads and writes) and the 16 rows of a 16-byte access fall on 16
+    // distinct 4-bank groups (an odd multiplier is invertible mod 16)
+    constexpr int SP = ((DR / 4 + 1) | 1) * 4;
+    static_assert(DR % 4 == 0 && SP > DR, "row pitch");
     constexpr int CHUNK = WAVES * SPW * KEYS_PER_STEP;
 
     // RoPE: B_k^(h)T operands of up to ROWS requests (one per row when g = 1),
@@ -709,16 +713,10 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     // ---- merge the four wavefronts through LDS
     if constexpr (ROPE) __syncthreads();  // every B_k operand read before sm_o (same LDS) is written
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sm_o[wave][n16][16 * dt + 4 * q4] = acc[dt];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sm_o[wave][n16][16 * dt + 4 * q4 + v] = acc[dt][v];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int rank = 16 * rt + 4 * q4 + v;
-            if (rank < R) sm_o[wave][n16][D + rank] = acc_lr[rt][v];
-        }
+    for (int rt = 0; rt < NRT; ++rt)  // ranks 16 rt + 4 q4 .. + 3 (R is a multiple of 4)
+        if (16 * rt + 4 * q4 < R) *(f32x4*)&sm_o[wave][n16][D + 16 * rt + 4 * q4] = acc_lr[rt];
     if (q4 == 0) {
         sm_m[wave][n16] = m_run;
         sm_l[wave][n16] = l_run;
@@ -753,13 +751,10 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
             const int gi = min(cl + 16 * k, DR / 4 - 1);
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float o = 0.f;
-#pragma unroll
-                for (int w = 0; w < WAVES; ++w) o += wt[w] * sm_o[w][n][4 * gi + e];
-                og[k][e] = o;
-            }
+            for (int w = 0; w < WAVES; ++w) o += wt[w] * *(const f32x4*)&sm_o[w][n][4 * gi];
+            og[k] = o;
         }
     }
     // the combined partial into LDS (columns 4 gi .. of this thread only), for
