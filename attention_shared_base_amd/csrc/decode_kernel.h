@@ -763,10 +763,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
             const int gi = cl + 16 * k;
-            if (gi < DR / 4) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sm_o[0][n][4 * gi + e] = og[k][e];
-            }
+            if (gi < DR / 4) *(f32x4*)&sm_o[0][n][4 * gi] = og[k];
         }
         if (cl == 0) sm_L[n] = L;
     };
@@ -993,8 +990,7 @@ __device__ __forceinline__ void merge_partials(const DecodeK& a, int unit, int o
     for (int k = 0; k < NG; ++k) {
         const int gi = cl + 16 * k;
         if (gi < DR / 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[n][4 * gi + e] = acc[k][e];
+            *(f32x4*)&o[n][4 * gi] = acc[k];
         }
     }
     if (cl == 0) L_row[n] = L;
@@ -1014,14 +1010,21 @@ __device__ __forceinline__ void finalize_rows(const DecodeK& a, const float (*o)
     const float L = L_row[n];
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     const int c0 = cl * CPT;
+    // 16-byte LDS reads: the row pitch is a multiple of 4 floats, c0 of CPT
     float acc[CPT];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) acc[k] = o[n][c0 + k];
+    for (int k = 0; k < CPT; k += 4) {
+        const f32x4 v = *(const f32x4*)&o[n][c0 + k];
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-        const float w = o[n][D + t];
+        for (int e = 0; e < 4; ++e) acc[k + e] = v[e];
+    }
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) acc[k] += w * (float)bv.r[t][k];
+    for (int t4 = 0; t4 < R; t4 += 4) {
+        const f32x4 w4 = *(const f32x4*)&o[n][D + t4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) acc[k] += w4[e] * (float)bv.r[t4 + e][k];
     }
     typename BvCols<D, R>::vec res;
 #pragma unroll
