@@ -76,7 +76,16 @@ def test_decode_more_than_64_requests():
     reqs = [(c, (c + 2 * i) % 5) for c in range(29) for i in range(3)][:85]
     case = w.make_decode(43, dtype="bf16", ctx_lens=lens, reqs=reqs, n_agents=5, h_q=8, h_kv=2,
                          d=64, r=8, name="85 requests")
-    _check(case)
+    d, _, ref = _check(case)
+    # 512-token chunks (split-K merges), one workgroup per chunk and persistent workgroups
+    try:
+        os.environ["LRA_DECODE_CHUNK"] = "512"
+        for per in ("0", "1"):
+            os.environ["LRA_DECODE_PERSISTENT"] = per
+            assert_parity(host(d.run()), ref, "bf16", f"85 requests, 512-token chunks, persistent={per}")
+    finally:
+        os.environ.pop("LRA_DECODE_CHUNK", None)
+        os.environ.pop("LRA_DECODE_PERSISTENT", None)
 
 @pytest.mark.parametrize("r", [32, 4])
 def test_decode_fp32_ragged(r):
