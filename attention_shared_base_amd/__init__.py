@@ -72,10 +72,10 @@ def load():
     lib.lra_attn_decode.restype = I32
     lib.lra_attn_decode.argtypes = [
         ctypes.POINTER(Dims), P, I32, P, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, I32,
-        P, P, I32, P, P, P, P, ctypes.c_size_t, P]
+        P, P, I32, P, P, I32, P, P, ctypes.c_size_t, P]
     lib.lra_attn_prefill.restype = I32
     lib.lra_attn_prefill.argtypes = [
-        ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, P, P]
+        ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, I32, P, P]
     lib.lra_lr_cache_build.restype = I32
     lib.lra_lr_cache_build.argtypes = [I32, P, I32, I32, P, P, I32, I32, P, P, ctypes.c_int64,
                                        ctypes.c_int64, P, ctypes.c_size_t, P]
@@ -88,7 +88,7 @@ def load():
     lib.lra_attn_prefill_paged.restype = I32
     lib.lra_attn_prefill_paged.argtypes = [
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, P, I32, P, P,
-        P, P, ctypes.c_size_t, P]
+        I32, P, P, ctypes.c_size_t, P]
     lib.lra_cache_append.restype = I32
     lib.lra_cache_append.argtypes = [ctypes.POINTER(Dims), I32, P, P, P, P, P, P, P, P, P, I32,
                                      I32, P]
@@ -121,6 +121,10 @@ def _dtype_code(t):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rows(t):
+    return 0 if t is None else int(t.shape[0])
 
 
 def _stream(t, stream):
@@ -212,7 +216,8 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
         ctypes.byref(dims), _ptr(q), n_req, _ptr(ctx_req_start), n_ctx, max_req_per_ctx,
         _ptr(req_agent), _ptr(k_pool), _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, page,
         _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
-        _ptr(rope_cos), _ptr(rope_sin), _ptr(out), _ptr(workspace), wsz, _stream(q, stream)))
+        _ptr(rope_cos), _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), wsz,
+        _stream(q, stream)))
     return out
 
 
@@ -253,7 +258,7 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, 
     _check(lib.lra_attn_prefill(
         ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_base), _ptr(v_base),
         kv_len, _ptr(l_k), _ptr(l_v), _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
-        _ptr(rope_sin), _ptr(out), _stream(q, stream)))
+        _ptr(rope_sin), _rows(rope_cos), _ptr(out), _stream(q, stream)))
     return out
 
 
@@ -404,7 +409,8 @@ def prefill_paged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_ro
         ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_pool), _ptr(v_pool),
         _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _ptr(block_table_row),
         block_table_row.shape[0], kv_len, _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
-        _ptr(rope_sin), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q, stream)))
+        _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(q, stream)))
     return out
 
 

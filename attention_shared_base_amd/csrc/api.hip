@@ -165,7 +165,7 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
                            int32_t page_size, const int32_t* block_table, int32_t max_blocks,
                            const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
                            const void* b_v, int32_t n_agents, const float* rope_cos,
-                           const float* rope_sin, void* out, void* workspace,
+                           const float* rope_sin, int32_t rope_rows, void* out, void* workspace,
                            size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
@@ -200,6 +200,12 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
         return fail(LRA_ERR_NULL_PTR, "rope_cos and rope_sin must be both NULL or both set");
     if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin)))
         return fail(LRA_ERR_MISALIGNED, "rope tables are not 16-byte aligned");
+    if (rope_cos && rope_rows < (max_ctx_len > 1 ? max_ctx_len : 1))
+        return fail(LRA_ERR_BAD_SHAPE, "rope tables hold %d rows < max(max_ctx_len, 1) = %d", rope_rows,
+                    max_ctx_len > 1 ? max_ctx_len : 1);
+    if (dims->lr_agent_stride > 0 && dims->lr_agent_stride < (long long)n_pages * page_size * dims->rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < one agent's LR pool (n_pages*page_size*r = %lld)",
+                    (long long)dims->lr_agent_stride, (long long)n_pages * page_size * dims->rank);
 
     lra::DecodeArgs a;
     a.q = q;
@@ -215,6 +221,7 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
     a.b_v = b_v;
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
+    a.rope_rows = rope_cos ? rope_rows : 0;
     a.out = out;
     a.workspace = workspace;
     a.lr_stride = dims->lr_agent_stride;
@@ -253,7 +260,7 @@ lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, 
                             const int32_t* req_agent, const void* k_base, const void* v_base,
                             int32_t kv_len, const void* l_k, const void* l_v, const void* b_k,
                             const void* b_v, int32_t n_agents, const float* rope_cos,
-                            const float* rope_sin, void* out, void* stream) {
+                            const float* rope_sin, int32_t rope_rows, void* out, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
@@ -275,7 +282,12 @@ lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, 
     if (rope_cos) {
         REQUIRE_PTR(rope_cos);
         REQUIRE_PTR(rope_sin);
+        if (rope_rows < kv_len)
+            return fail(LRA_ERR_BAD_SHAPE, "rope tables hold %d rows < kv_len %d", rope_rows, kv_len);
     }
+    if (dims->lr_agent_stride > 0 && dims->lr_agent_stride < (long long)kv_len * dims->rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < one agent's LR cache (kv_len*r = %lld)",
+                    (long long)dims->lr_agent_stride, (long long)kv_len * dims->rank);
     lra::PrefillArgs a;
     a.q = q;
     a.req_agent = req_agent;
@@ -313,8 +325,8 @@ lra_status lra_attn_prefill_paged(const lra_dims* dims, const void* q, int32_t n
                                   const void* lk_pool, const void* lv_pool, int32_t n_pages,
                                   int32_t page_size, const int32_t* block_table, int32_t max_blocks,
                                   int32_t kv_len, const void* b_k, const void* b_v, int32_t n_agents,
-                                  const float* rope_cos, const float* rope_sin, void* out,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+                                  const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
@@ -369,12 +381,14 @@ lra_status lra_attn_prefill_paged(const lra_dims* dims, const void* q, int32_t n
     if (rope_cos) {
         REQUIRE_PTR(rope_cos);
         REQUIRE_PTR(rope_sin);
+        if (rope_rows < kv_len)
+            return fail(LRA_ERR_BAD_SHAPE, "rope tables hold %d rows < kv_len %d", rope_rows, kv_len);
     }
     if (n_req == 0) return LRA_OK;
     st = lra::launch_cache_gather_bf16(g, (hipStream_t)stream);
     if (st != LRA_OK) return st;
     return lra_attn_prefill(dims, q, n_req, q_len, req_agent, g.k_out, g.v_out, kv_len, g.lk_out,
-                            g.lv_out, b_k, b_v, n_agents, rope_cos, rope_sin, out, stream);
+                            g.lv_out, b_k, b_v, n_agents, rope_cos, rope_sin, rope_rows, out, stream);
 }
 
 lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* slot_mapping,

@@ -31,6 +31,7 @@ struct F32K {
     float* out;
     int32_t n_req, n_ctx, n_pages, max_blocks, n_agents;
     int32_t q_len, kv_len;  // prefill
+    int32_t max_len;        // decode: max_ctx_len (longer contexts are cut to it)
     int32_t h_q, h_kv, d, r;
     float scale;
     int64_t lr_stride;  // per-agent LR caches: elements between agents' caches (0: shared)
@@ -212,7 +213,8 @@ __global__ __launch_bounds__(64) void lra_decode_f32_kernel(F32K a) {
         if (a.ctx_req_start[mid] <= req) lo = mid; else hi = mid - 1;
     }
     const int ctx = lo;
-    const int len = min(a.ctx_len[ctx], a.max_blocks * PAGE);
+    // clamped to max_ctx_len as well: the RoPE tables hold that many rows
+    const int len = min(min(a.ctx_len[ctx], a.max_blocks * PAGE), a.max_len);
     float* orow = a.out + ((size_t)req * a.h_q + hq) * a.d;
     if (len <= 0) {
         for (int c = threadIdx.x; c < a.d; c += 64) orow[c] = 0.f;
@@ -258,6 +260,7 @@ F32K common(const lra::DecodeArgs& d) {
     k.n_ctx = d.n_ctx;
     k.n_pages = d.n_pages;
     k.max_blocks = d.max_blocks;
+    k.max_len = d.max_ctx_len;
     k.n_agents = d.n_agents;
     k.h_q = d.h_q;
     k.h_kv = d.h_kv;

@@ -81,6 +81,7 @@ struct DecodeK {
     const float* rope_cos;  // RoPE: [rope_rows, D/2] tables of the keys' positions
     const float* rope_sin;
     int32_t rope_rows;
+    int32_t max_len;    // max_ctx_len: longer contexts are cut to it (the workspace is sized for it)
     int64_t lr_stride;  // per-agent LR caches: elements between agents' pools (0: one shared cache)
 };
 
@@ -259,7 +260,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     }
     const int g = a.g;
     const int nrows = nreq * g;
-    const int len = min(len_raw, a.max_blocks * PAGE);
+    // lengths are clamped to max_ctx_len: the host sized the chunk count and the
+    // workspace for it, and a longer context must not add chunks past them
+    const int len = min(min(len_raw, a.max_blocks * PAGE), a.max_len);
 
     if (len <= 0) {  // empty context: defined as zero output
         if (split == 0) {
@@ -864,7 +867,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
             const int c = base + lane;
             int v = 0;
             if (c < a.n_ctx) {
-                const int len = min(a.ctx_len[c], a.max_blocks * PAGE);
+                const int len = min(min(a.ctx_len[c], a.max_blocks * PAGE), a.max_len);
                 v = (len > 0 ? (len + CHUNK - 1) / CHUNK : 1) * a.n_rg * a.h_kv;
             }
 #pragma unroll
@@ -1067,7 +1070,8 @@ lra_status launch_t(const lra::DecodeArgs& a, const lra::DecodePlan& p, hipStrea
     k.scale_log2 = a.scale * LRA_LOG2E;
     k.rope_cos = a.rope_cos;
     k.rope_sin = a.rope_sin;
-    k.rope_rows = a.max_ctx_len;
+    k.rope_rows = a.rope_rows;
+    k.max_len = a.max_ctx_len;
     k.lr_stride = a.lr_stride;
     int grid = p.grid;
     if (p.persistent) {

@@ -48,10 +48,11 @@ struct DecodeArgs {
     const int32_t* ctx_len;
     const void* b_k;
     const void* b_v;
-    const float* rope_cos;  // NULL: no RoPE on the adapter key; else [max_ctx_len, d/2]
+    const float* rope_cos;  // NULL: no RoPE on the adapter key; else [rope_rows, d/2]
     const float* rope_sin;
     void* out;
     void* workspace;
+    int32_t rope_rows;      // rows of the RoPE tables (>= max(max_ctx_len, 1) when given)
     int32_t n_req, n_ctx, n_pages, max_blocks, max_ctx_len, n_agents;
     int32_t h_q, h_kv, head_dim, rank;
     float scale;
@@ -70,7 +71,7 @@ struct PrefillArgs {
     const void* l_v;
     const void* b_k;
     const void* b_v;
-    const float* rope_cos;
+    const float* rope_cos;  // NULL: no RoPE on the adapter key; else [rope_rows >= kv_len, d/2]
     const float* rope_sin;
     void* out;
     int32_t n_req, q_len, kv_len, n_agents;

@@ -63,7 +63,7 @@ typedef int32_t lra_status;
 #define LRA_F32 0
 #define LRA_BF16 1
 
-#define LRA_ABI_VERSION 3
+#define LRA_ABI_VERSION 4
 
 typedef struct lra_dims {
     int32_t n_q_heads;   /* H_q */
@@ -111,7 +111,8 @@ const char* lra_last_error(void);
  *   lv_pool        [n_pages, r, page_size]                 device (rank-major)
  *                  With dims->lr_agent_stride > 0 these are n_agents pools
  *                  lr_agent_stride elements apart (stride >= n_pages *
- *                  page_size * r), agent a's at a * lr_agent_stride; request
+ *                  page_size * r, else LRA_ERR_BAD_SHAPE), agent a's at
+ *                  a * lr_agent_stride; request
  *                  i reads req_agent[i]'s pool through the same block table.
  *   block_table    [n_ctx, max_blocks] int32               device
  *                  logical token t of context c is in page
@@ -122,13 +123,20 @@ const char* lra_last_error(void);
  *   ctx_len        [n_ctx] int32, 0 <= ctx_len[c] <= max_ctx_len,
  *                  max_ctx_len <= max_blocks * page_size   device
  *                  The newest token is part of the context; a context of
- *                  length 0 yields zero output rows.
+ *                  length 0 yields zero output rows.  A length above
+ *                  max_ctx_len (device data the host cannot check) is cut to
+ *                  max_ctx_len: the chunk count, the workspace and the RoPE
+ *                  rows are sized for it, so the call stays in bounds and
+ *                  leaves the workspace counters at zero.
  *   b_k, b_v       [n_agents, r, H_kv * d]; head h uses columns h*d .. h*d+d-1
  *   rope_cos,
  *   rope_sin       NULL (no rotation of the adapter key term) or both
- *                  [max(max_ctx_len, 1), d/2] fp32 device tables of
+ *                  [rope_rows, d/2] fp32 device tables of
  *                  cos/sin(pos * theta^(-2i/d)) (lra_rope_table_build); the
- *                  key at token index j of a context has position j.  K_base
+ *                  key at token index j of a context has position j.
+ *   rope_rows      rows of each table; with tables it must be at least
+ *                  max(max_ctx_len, 1) (else LRA_ERR_BAD_SHAPE); ignored
+ *                  without them.  K_base
  *                  is expected already rotated; the adapter key term
  *                  L_k B_k is rebuilt at head dimension for each request and
  *                  rotated (rotate-half pairing i, i+d/2) before it meets the
@@ -162,7 +170,7 @@ lra_status lra_attn_decode(const lra_dims* dims,
                            const int32_t* block_table, int32_t max_blocks,
                            const int32_t* ctx_len, int32_t max_ctx_len,
                            const void* b_k, const void* b_v, int32_t n_agents,
-                           const float* rope_cos, const float* rope_sin,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                            void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -180,12 +188,15 @@ lra_status lra_attn_decode(const lra_dims* dims,
  *   v_base     [H_kv, kv_len, d]               device
  *   l_k, l_v   [kv_len, r]                     device; with
  *              dims->lr_agent_stride > 0, one [kv_len, r] cache per agent,
- *              agent a's at a * lr_agent_stride elements
+ *              agent a's at a * lr_agent_stride elements (stride >=
+ *              kv_len * r, else LRA_ERR_BAD_SHAPE)
  *   b_k, b_v   [n_agents, r, H_kv * d]         device
  *   rope_cos,
  *   rope_sin   NULL (no rotation of the adapter key term) or both
- *              [kv_len, d/2] fp32 device tables of cos/sin(pos * theta^(-2i/d))
- *              (see lra_rope_table_build).  K_base is expected already rotated;
+ *              [rope_rows, d/2] fp32 device tables of cos/sin(pos * theta^(-2i/d))
+ *              (see lra_rope_table_build), rope_rows >= kv_len (else
+ *              LRA_ERR_BAD_SHAPE; ignored without tables).  K_base is expected
+ *              already rotated;
  *              the kernel rotates only L_k B_k (rotate-half pairing i, i+d/2)
  *              before adding it to K_base.
  *   out        [n_req, q_len, H_q, d]          device
@@ -197,7 +208,7 @@ lra_status lra_attn_prefill(const lra_dims* dims,
                             const void* k_base, const void* v_base, int32_t kv_len,
                             const void* l_k, const void* l_v,
                             const void* b_k, const void* b_v, int32_t n_agents,
-                            const float* rope_cos, const float* rope_sin,
+                            const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                             void* out, void* stream);
 
 /*
@@ -226,7 +237,7 @@ lra_status lra_attn_prefill_paged(const lra_dims* dims,
                                   const int32_t* block_table, int32_t max_blocks,
                                   int32_t kv_len,
                                   const void* b_k, const void* b_v, int32_t n_agents,
-                                  const float* rope_cos, const float* rope_sin,
+                                  const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                                   void* out, void* workspace, size_t workspace_bytes,
                                   void* stream);
 /*

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = lra.load()
-    assert lra.abi_version() == 3
+    assert lra.abi_version() == 4
     for s in range(7):
         assert lib.lra_status_str(s).decode().startswith("LRA_")
     assert b"unknown" in lib.lra_status_str(99)
@@ -53,14 +53,14 @@ def call_decode(dm, **over):
     # call needs a workspace and every case below fails validation before launch.
     args = dict(q=A, n_req=16, crs=A, n_ctx=4, mrpc=4, agent=A, k=A, v=A, lk=A, lv=A,
                 n_pages=2048, page=16, bt=A, max_blocks=512, clen=A, max_ctx=8192, bk=A, bv=A,
-                n_agents=4, cos=None, sin=None, out=A, ws=A, ws_bytes=1 << 30)
+                n_agents=4, cos=None, sin=None, rows=8192, out=A, ws=A, ws_bytes=1 << 30)
     args.update(over)
     st = lib.lra_attn_decode(ctypes.byref(dm), args["q"], args["n_req"], args["crs"], args["n_ctx"],
                              args["mrpc"], args["agent"], args["k"], args["v"], args["lk"],
                              args["lv"], args["n_pages"], args["page"], args["bt"],
                              args["max_blocks"], args["clen"], args["max_ctx"], args["bk"],
-                             args["bv"], args["n_agents"], args["cos"], args["sin"], args["out"],
-                             args["ws"], args["ws_bytes"], None)
+                             args["bv"], args["n_agents"], args["cos"], args["sin"], args["rows"],
+                             args["out"], args["ws"], args["ws_bytes"], None)
     return st, lib.lra_last_error().decode()
 
 
@@ -90,8 +90,12 @@ def call_decode(dm, **over):
     (dims(), {"ws": None}, 1),
     (dims(), {"cos": A}, 1),                 # rope tables go in pairs
     (lra.Dims(32, 8, 128, 16, 1, 0.0, -1), {}, 2),   # negative LR stride
-    (lra.Dims(32, 8, 128, 16, 1, 0.0, 4096), {"cos": A, "sin": A}, 3),  # per-agent LR + RoPE
+    (lra.Dims(32, 8, 128, 16, 1, 0.0, 2048 * 16 * 16), {"cos": A, "sin": A}, 3),  # per-agent LR + RoPE
     (dims(), {"cos": A, "sin": ctypes.c_void_p(0x100004)}, 4),
+    (dims(), {"cos": A, "sin": A, "rows": 8191}, 2),          # tables shorter than max_ctx_len
+    (dims(), {"cos": A, "sin": A, "rows": 0, "max_ctx": 0}, 2),  # at least one row
+    # one LR pool per agent: the stride must cover n_pages * page * r elements
+    (lra.Dims(32, 8, 128, 16, 1, 0.0, 2048 * 16 * 16 - 1), {}, 2),
 ])
 def test_decode_validation(dm, over, want):
     st, msg = call_decode(dm, **over)
@@ -102,18 +106,18 @@ def test_decode_validation(dm, over, want):
 def test_decode_null_dims():
     lib = lra.load()
     st = lib.lra_attn_decode(None, A, 1, A, 1, 1, A, A, A, A, A, 1, 16, A, 1, A, 16, A, A, 1, None,
-                             None, A, A, 0, None)
+                             None, 0, A, A, 0, None)
     assert st == 1
 
 
 def call_prefill(dm, **over):
     lib = lra.load()
     a = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, kv_len=256, lk=A, lv=A, bk=A, bv=A,
-             n_agents=2, cos=None, sin=None, out=A)
+             n_agents=2, cos=None, sin=None, rows=256, out=A)
     a.update(over)
     st = lib.lra_attn_prefill(ctypes.byref(dm), a["q"], a["n_req"], a["q_len"], a["agent"], a["k"],
                               a["v"], a["kv_len"], a["lk"], a["lv"], a["bk"], a["bv"],
-                              a["n_agents"], a["cos"], a["sin"], a["out"], None)
+                              a["n_agents"], a["cos"], a["sin"], a["rows"], a["out"], None)
     return st, lib.lra_last_error().decode()
 
 
@@ -125,10 +129,17 @@ def call_prefill(dm, **over):
     ({"v": None}, 1),
     ({"lk": ctypes.c_void_p(0x100004)}, 4),
     ({"n_req": -3}, 2),
+    ({"cos": A, "sin": A, "rows": 255}, 2),   # RoPE tables shorter than kv_len
 ])
 def test_prefill_validation(over, want):
     st, msg = call_prefill(dims(), **over)
     assert st == want, msg
+
+
+def test_prefill_per_agent_stride():
+    # one LR cache per agent: the stride must cover kv_len * r elements
+    st, msg = call_prefill(lra.Dims(32, 8, 128, 16, 1, 0.0, 256 * 16 - 1))
+    assert st == 2 and "lr_agent_stride" in msg
 
 
 def test_prefill_zero_requests_is_a_no_op():
@@ -226,20 +237,21 @@ def test_paged_prefill_and_append_validation():
 
     def pp(**o):
         a = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, lk=A, lv=A, n_pages=64, page=16, bt=A,
-                 max_blocks=16, kv_len=256, bk=A, bv=A, n_agents=2, cos=None, sin=None, out=A,
-                 ws=A, ws_bytes=1 << 30)
+                 max_blocks=16, kv_len=256, bk=A, bv=A, n_agents=2, cos=None, sin=None, rows=256,
+                 out=A, ws=A, ws_bytes=1 << 30)
         a.update(o)
         return lib.lra_attn_prefill_paged(ctypes.byref(o.pop("dm", dm)), a["q"], a["n_req"], a["q_len"],
                                           a["agent"], a["k"], a["v"], a["lk"], a["lv"], a["n_pages"],
                                           a["page"], a["bt"], a["max_blocks"], a["kv_len"], a["bk"],
-                                          a["bv"], a["n_agents"], a["cos"], a["sin"], a["out"],
-                                          a["ws"], a["ws_bytes"], None)
+                                          a["bv"], a["n_agents"], a["cos"], a["sin"], a["rows"],
+                                          a["out"], a["ws"], a["ws_bytes"], None)
     assert pp(max_blocks=15) == 2            # 15 blocks cannot hold 256 tokens
     assert pp(ws_bytes=1) == 5
     assert pp(ws=None) == 1
     assert pp(kv_len=8) == 2                  # kv_len < q_len
     assert pp(page=32) == 3
     assert pp(cos=A) == 1
+    assert pp(cos=A, sin=A, rows=255) == 2    # RoPE tables shorter than kv_len
 
     def ap(**o):
         a = dict(n=4, slots=A, k=A, v=A, lk=A, lv=A, kp=A, vp=A, lkp=A, lvp=A, n_pages=8, page=16)

@@ -199,3 +199,41 @@ def test_decode_persistent_queue():
         assert np.all(o[[6, 7]] == 0.0)  # requests on the empty context
     assert np.array_equal(outs[1], outs[2])
     assert np.max(np.abs(outs[1] - outs[0])) < 4e-3
+
+
+@pytest.mark.parametrize("persistent", ["0", "1"])
+def test_decode_context_longer_than_max_ctx_len(persistent):
+    """A context length above max_ctx_len (device data the host cannot check) is cut to
+    max_ctx_len: the call stays inside the workspace it was sized for, leaves the
+    merge counters at zero, and a following valid call on the same workspace still
+    matches the oracle."""
+    import copy
+
+    import torch
+    import attention_shared_base_amd as lra
+    reqs = [(0, 0), (0, 1), (1, 1), (2, 0)]
+    case = w.make_decode(47, dtype="bf16", ctx_lens=[3000, 5000, 1500], reqs=reqs, n_agents=2,
+                         h_q=32, h_kv=8, d=128, r=16, shuffle=True, name="ctx_len > max_ctx_len")
+    d = DecodeDev(case)
+    cut = 2000
+    try:
+        os.environ["LRA_DECODE_CHUNK"] = "512"
+        os.environ["LRA_DECODE_PERSISTENT"] = persistent
+        n_ws = lra.decode_workspace_size(n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1,
+                                         n_req=4, n_ctx=3, max_req_per_ctx=2, max_ctx_len=cut)
+        ws = torch.zeros(lra.decode_workspace_size(
+            n_q_heads=32, n_kv_heads=8, head_dim=128, rank=16, dtype=1, n_req=4, n_ctx=3,
+            max_req_per_ctx=2, max_ctx_len=d.max_ctx_len), dtype=torch.uint8, device="cuda")
+        assert 0 < n_ws <= ws.numel()
+        got = host(lra.decode(d.q, d.crs, d.agent, d.k, d.v, d.lk, d.lv, d.bt, d.clen, d.b_k, d.b_v,
+                              max_req_per_ctx=2, max_ctx_len=cut, workspace=ws))
+        torch.cuda.synchronize()
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0  # counters and queue at zero
+        cut_case = copy.copy(case)
+        cut_case.ctx_len = np.minimum(case.ctx_len, cut).astype(np.int32)
+        assert_parity(got, oracle_decode(cut_case), "bf16", f"contexts cut to {cut}")
+        full = host(d.run(workspace=ws))
+    finally:
+        os.environ.pop("LRA_DECODE_CHUNK", None)
+        os.environ.pop("LRA_DECODE_PERSISTENT", None)
+    assert_parity(full, oracle_decode(case), "bf16", "following valid call")
