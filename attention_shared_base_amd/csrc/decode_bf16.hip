@@ -15,7 +15,12 @@ lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStrea
             set_error("decode: RoPE on the adapter key with per-agent LR caches is not supported");
             return LRA_ERR_UNSUPPORTED;
         }
-        return launch_decode_rope_bf16(a, p, s);
+        // The RoPE mode always runs one workgroup per chunk.  Its persistent
+        // (chunk-queue) form is switched off: a GPU memory fault was observed
+        // with it (rank 32, 512-token chunks) whose cause has not been found.
+        DecodePlan q = p;
+        q.persistent = 0;
+        return launch_decode_rope_bf16(a, q, s);
     }
     if (a.lr_stride != 0) return launch_decode_pa_bf16(a, p, s);
 #define LRA_CASE(D_, R_) \

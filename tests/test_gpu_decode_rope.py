@@ -111,14 +111,22 @@ def test_decode_rope_equals_last_prefill_row():
     assert metrics(out, pre[:, -1])[1] < 1e-2
 
 
-def test_decode_rope_persistent_and_splits():
-    """Persistent queue and chunk sizes with RoPE: same rows, workspace back to zero."""
+@pytest.mark.skip(reason="the RoPE decode's persistent (chunk-queue) form is switched off: a GPU "
+                         "memory fault was observed with it (rank 32, 512-token chunks) and its cause "
+                         "has not been found; the library never launches it")
+def test_decode_rope_persistent_queue():
+    """Persistent workgroups with RoPE on the adapter key (not launched; see the reason)."""
+
+
+def test_decode_rope_splits():
+    """Chunk sizes with RoPE (one workgroup per chunk; the RoPE decode never runs its
+    persistent form, also when asked to): same rows, workspace back to zero."""
     import torch
     import attention_shared_base_amd as lra
     reqs = [(c, c % 3) for c in range(5) for _ in range(2)] + [(5, 1)]
     case = w.make_decode(53, dtype="bf16", ctx_lens=[3000, 1, 9000, 0, 4500, 700], reqs=reqs,
                          n_agents=3, h_q=32, h_kv=8, d=128, r=32, shuffle=True, b_sigma=0.2,
-                         name="rope persistent")
+                         name="rope splits")
     d = DecodeDev(case)
     live = [i for i, (c, _) in enumerate(reqs) if c != 3]
     ref = oracle_decode(case, requests=live, rope_theta=THETA)
@@ -129,7 +137,7 @@ def test_decode_rope_persistent_and_splits():
                                          n_req=len(reqs), n_ctx=6, max_req_per_ctx=d.max_req_per_ctx,
                                          max_ctx_len=d.max_ctx_len)
         ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
-        for chunk, per in (("512", "0"), ("512", "1"), ("512", "1"), ("256", "0"), ("4096", "0")):
+        for chunk, per in (("512", "0"), ("512", "0"), ("256", "0"), ("4096", "0")):
             os.environ["LRA_DECODE_CHUNK"] = chunk
             os.environ["LRA_DECODE_PERSISTENT"] = per
             print(f"[decode rope] chunk {chunk} persistent {per}", flush=True)
@@ -139,6 +147,6 @@ def test_decode_rope_persistent_and_splits():
         os.environ.pop("LRA_DECODE_CHUNK", None)
         os.environ.pop("LRA_DECODE_PERSISTENT", None)
     for o in outs:
-        assert_parity(o[live], ref[live], "bf16", "rope persistent / splits")
+        assert_parity(o[live], ref[live], "bf16", "rope splits")
         assert np.all(o[[6, 7]] == 0.0)
-    assert np.array_equal(outs[1], outs[2])
+    assert np.array_equal(outs[0], outs[1])  # the same call twice: the same bits
