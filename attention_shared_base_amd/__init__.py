@@ -16,7 +16,7 @@ import os
 __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
-    "prefill_paged", "prefill_paged_workspace_size", "cache_append",
+    "prefill_paged", "prefill_paged_workspace_size", "cache_append", "decode_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build",
     "lra_lr_cache_build_workspace_size", "lra_rope_table_build",
     "lra_naive_expand_pages", "lra_attn_prefill_paged_workspace_size", "lra_attn_prefill_paged",
-    "lra_cache_append",
+    "lra_cache_append", "lra_attn_decode_noalloc",
 )
 
 
@@ -73,6 +73,10 @@ def load():
     lib.lra_attn_decode.argtypes = [
         ctypes.POINTER(Dims), P, I32, P, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, I32,
         P, P, I32, P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.lra_attn_decode_noalloc.restype = I32
+    lib.lra_attn_decode_noalloc.argtypes = [
+        ctypes.POINTER(Dims), P, I32, P, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, I32,
+        P, P, I32, P, P, I32, P, P]
     lib.lra_attn_prefill.restype = I32
     lib.lra_attn_prefill.argtypes = [
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, I32, P, P]
@@ -218,6 +222,45 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
         _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
         _ptr(rope_cos), _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), wsz,
         _stream(q, stream)))
+    return out
+
+
+def decode_noalloc(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table,
+                   ctx_len, b_k, b_v, out, *, max_req_per_ctx, max_ctx_len, rope_cos=None,
+                   rope_sin=None, softmax_scale=0.0, stream=None):
+    """Decode that allocates nothing (``lra_attn_decode_noalloc``): the arguments of
+    ``decode`` without a workspace; ``out`` [n_req, H_q, d] must be given.  The split-K
+    scratch is the library's own per-GPU array, so calls that overlap on one GPU race."""
+    import torch
+    lib = load()
+    n_req, h_q, d = q.shape
+    n_pages, h_kv, d8, page, eight = k_pool.shape
+    _need(d8 * 8 == d and eight == 8, "k_pool must be [n_pages, H_kv, d/8, page, 8]")
+    r = lk_pool.shape[-1]
+    n_ctx, max_blocks = block_table.shape
+    n_agents = b_k.shape[0]
+    per_agent = lk_pool.dim() == 4
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
+                    ("lv_pool", lv_pool), ("b_k", b_k), ("b_v", b_v), ("out", out)):
+        _contig(name, t)
+        _need(_dtype_code(t) == dt, f"{name} dtype differs from q")
+    for name, t in (("ctx_req_start", ctx_req_start), ("req_agent", req_agent),
+                    ("block_table", block_table), ("ctx_len", ctx_len)):
+        _contig(name, t)
+        _need(t.dtype == torch.int32, f"{name} must be int32")
+    _need(tuple(out.shape) == tuple(q.shape), "out must be [n_req, H_q, d]")
+    lead = (n_agents,) if per_agent else ()
+    _need(tuple(v_pool.shape) == (n_pages, h_kv, d, page), "v_pool must be [n_pages, H_kv, d, page]")
+    _need(tuple(lk_pool.shape) == lead + (n_pages, page, r), "lk_pool must be [(n_agents,) n_pages, page, r]")
+    _need(tuple(lv_pool.shape) == lead + (n_pages, r, page), "lv_pool must be [(n_agents,) n_pages, r, page]")
+    _need((rope_cos is None) == (rope_sin is None), "rope_cos and rope_sin go together")
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale, n_pages * page * r if per_agent else 0)
+    _check(lib.lra_attn_decode_noalloc(
+        ctypes.byref(dims), _ptr(q), n_req, _ptr(ctx_req_start), n_ctx, max_req_per_ctx,
+        _ptr(req_agent), _ptr(k_pool), _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, page,
+        _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
+        _ptr(rope_cos), _ptr(rope_sin), _rows(rope_cos), _ptr(out), _stream(q, stream)))
     return out
 
 

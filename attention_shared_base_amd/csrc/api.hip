@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "lra_internal.h"
 
 namespace {
@@ -158,15 +160,63 @@ size_t lra_attn_decode_workspace_size(const lra_dims* dims, int32_t n_req, int32
     return p.ws_total;
 }
 
-lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
-                           const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
-                           const int32_t* req_agent, const void* k_pool, const void* v_pool,
-                           const void* lk_pool, const void* lv_pool, int32_t n_pages,
-                           int32_t page_size, const int32_t* block_table, int32_t max_blocks,
-                           const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
-                           const void* b_v, int32_t n_agents, const float* rope_cos,
-                           const float* rope_sin, int32_t rope_rows, void* out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- scratch of lra_attn_decode_noalloc: a file-scope device array, one copy
+// per GPU.  Its first NOALLOC_COUNTER_BYTES hold the merge counters and the
+// persistent queue words, the rest the chunk partials.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t NOALLOC_COUNTER_BYTES = LRA_DECODE_NOALLOC_COUNTER_BYTES;
+constexpr size_t NOALLOC_SCRATCH_BYTES = LRA_DECODE_NOALLOC_SCRATCH_BYTES;
+static_assert(NOALLOC_COUNTER_BYTES % 256 == 0 && NOALLOC_SCRATCH_BYTES > NOALLOC_COUNTER_BYTES, "scratch layout");
+__device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+// zero-fill of the counter words (a kernel, so callers under graph capture
+// record no memset node)
+__global__ void lra_zero_words_kernel(int32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch.  The first call on a device
+// looks the address up (with that device current) and clears the counter words
+// on `stream`; every completed decode leaves them at zero again.
+lra_status noalloc_scratch(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+        return fail(LRA_ERR_HIP, "decode_noalloc: no current device (or device index >= %d)", MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(LRA_ERR_HIP, "decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        const int n = (int)(NOALLOC_COUNTER_BYTES / sizeof(int32_t));
+        hipLaunchKernelGGL(lra_zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, (int32_t*)ptr, n);
+        const lra_status st = lra::check_launch("lra_zero_words_kernel");
+        if (st != LRA_OK) return st;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LRA_OK;
+}
+
+lra_status decode_entry(const lra_dims* dims, const void* q, int32_t n_req,
+                        const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
+                        const int32_t* req_agent, const void* k_pool, const void* v_pool,
+                        const void* lk_pool, const void* lv_pool, int32_t n_pages,
+                        int32_t page_size, const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
+                        const void* b_v, int32_t n_agents, const float* rope_cos,
+                        const float* rope_sin, int32_t rope_rows, void* out, void* workspace,
+                        size_t workspace_bytes, bool noalloc, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
@@ -246,6 +296,21 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
     lra::DecodePlan p;
     if (!lra::decode_plan(*dims, n_req, n_ctx, max_req_per_ctx, max_ctx_len, &p))
         return fail(LRA_ERR_BAD_SHAPE, "decode: problem too large to plan");
+    if (noalloc) {
+        // counters and partials at fixed offsets of the library's scratch
+        if (p.ws_counter_bytes > NOALLOC_COUNTER_BYTES || p.ws_part_bytes > NOALLOC_SCRATCH_BYTES - NOALLOC_COUNTER_BYTES)
+            return fail(LRA_ERR_WORKSPACE_TOO_SMALL,
+                        "decode_noalloc: needs %zu counter and %zu partial bytes; the scratch holds %zu and %zu",
+                        p.ws_counter_bytes, p.ws_part_bytes, NOALLOC_COUNTER_BYTES,
+                        NOALLOC_SCRATCH_BYTES - NOALLOC_COUNTER_BYTES);
+        if (n_req == 0) return LRA_OK;
+        void* ptr = nullptr;
+        const lra_status sst = noalloc_scratch((hipStream_t)stream, &ptr);
+        if (sst != LRA_OK) return sst;
+        a.workspace = ptr;
+        p.ws_counter_bytes = NOALLOC_COUNTER_BYTES;
+        return lra::launch_decode_bf16(a, p, (hipStream_t)stream);
+    }
     if (p.ws_total > 0) {
         if (!workspace) return fail(LRA_ERR_NULL_PTR, "workspace is NULL (need %zu bytes)", p.ws_total);
         if (!aligned16(workspace)) return fail(LRA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
@@ -254,6 +319,42 @@ lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
     }
     if (n_req == 0) return LRA_OK;
     return lra::launch_decode_bf16(a, p, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+lra_status lra_attn_decode(const lra_dims* dims, const void* q, int32_t n_req,
+                           const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
+                           const int32_t* req_agent, const void* k_pool, const void* v_pool,
+                           const void* lk_pool, const void* lv_pool, int32_t n_pages,
+                           int32_t page_size, const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
+                           const void* b_v, int32_t n_agents, const float* rope_cos,
+                           const float* rope_sin, int32_t rope_rows, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return decode_entry(dims, q, n_req, ctx_req_start, n_ctx, max_req_per_ctx, req_agent, k_pool, v_pool,
+                        lk_pool, lv_pool, n_pages, page_size, block_table, max_blocks, ctx_len, max_ctx_len,
+                        b_k, b_v, n_agents, rope_cos, rope_sin, rope_rows, out, workspace, workspace_bytes,
+                        false, stream);
+}
+
+lra_status lra_attn_decode_noalloc(const lra_dims* dims, const void* q, int32_t n_req,
+                                   const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
+                                   const int32_t* req_agent, const void* k_pool, const void* v_pool,
+                                   const void* lk_pool, const void* lv_pool, int32_t n_pages,
+                                   int32_t page_size, const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* ctx_len, int32_t max_ctx_len, const void* b_k,
+                                   const void* b_v, int32_t n_agents, const float* rope_cos,
+                                   const float* rope_sin, int32_t rope_rows, void* out, void* stream) {
+    if (dims && dims->dtype != LRA_BF16) {
+        g_err[0] = 0;
+        return fail(LRA_ERR_UNSUPPORTED, "decode_noalloc: bf16 only (the fp32 path uses no scratch)");
+    }
+    return decode_entry(dims, q, n_req, ctx_req_start, n_ctx, max_req_per_ctx, req_agent, k_pool, v_pool,
+                        lk_pool, lv_pool, n_pages, page_size, block_table, max_blocks, ctx_len, max_ctx_len,
+                        b_k, b_v, n_agents, rope_cos, rope_sin, rope_rows, out, nullptr, 0, true, stream);
 }
 
 lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, int32_t q_len,

@@ -175,6 +175,38 @@ lra_status lra_attn_decode(const lra_dims* dims,
                            void* stream);
 
 /*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result and bits as lra_attn_decode
+ * without the workspace (bf16 only: the fp32 path needs no scratch and returns
+ * LRA_ERR_UNSUPPORTED here).  The split-K partials, merge counters and chunk
+ * queue live in the library's own device array of
+ * LRA_DECODE_NOALLOC_SCRATCH_BYTES per GPU (the first
+ * LRA_DECODE_NOALLOC_COUNTER_BYTES of it hold the counters), held from the
+ * first call on that GPU until the process ends.  The first call on a GPU
+ * clears the counters with a small kernel on `stream`; every completed call
+ * leaves them at zero again.  A call whose counters (n_units + 2 int32, where
+ * n_units = n_ctx x row groups x H_kv) or partials do not fit returns
+ * LRA_ERR_WORKSPACE_TOO_SMALL before any HIP call.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (several streams
+ * or host threads) race: the caller must order them.
+ */
+#define LRA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define LRA_DECODE_NOALLOC_COUNTER_BYTES ((size_t)64 << 10)
+lra_status lra_attn_decode_noalloc(const lra_dims* dims,
+                                   const void* q, int32_t n_req,
+                                   const int32_t* ctx_req_start, int32_t n_ctx, int32_t max_req_per_ctx,
+                                   const int32_t* req_agent,
+                                   const void* k_pool, const void* v_pool,
+                                   const void* lk_pool, const void* lv_pool,
+                                   int32_t n_pages, int32_t page_size,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* ctx_len, int32_t max_ctx_len,
+                                   const void* b_k, const void* b_v, int32_t n_agents,
+                                   const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                                   void* out, void* stream);
+
+/*
  * Chunked prefill over one shared context (LRAgent §3: agents compute only the
  * newly appended context; App. B: accumulated length L = L_p + L_c; App. D.1:
  * key adapter rebuilt before RoPE).  The q_len new tokens are the last q_len

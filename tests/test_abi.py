@@ -287,3 +287,20 @@ def test_lr_build_workspace_size():
     # rank 4: partial rows padded to one 16-column tile
     assert ws(n_tok=4096, rank=4) == 256 + 64 * 4 * 64 * 16 * 4
     assert ws(n_tok=0) == 0
+
+
+def test_decode_noalloc_limits_and_dtype():
+    """The allocation-free decode rejects, before any HIP call, problems whose split-K
+    partials exceed its fixed scratch, and the fp32 path (which needs none)."""
+    lib = lra.load()
+    dm = dims()
+
+    def call(dm_, n_ctx, mrpc, max_ctx):
+        return lib.lra_attn_decode_noalloc(ctypes.byref(dm_), A, n_ctx * mrpc, A, n_ctx, mrpc, A, A,
+                                           A, A, A, 1 << 20, 16, A, 1 << 16, A, max_ctx, A, A, 4,
+                                           None, None, 0, A, None)
+    # 1024 contexts x 64k tokens: 8192 units x 16 chunks of partials (about 1.3 GB)
+    assert call(dm, 1024, 1, 65536) == 5
+    assert "scratch" in lib.lra_last_error().decode()
+    assert call(dims(dt=0), 1, 1, 256) == 3
+    assert call(dims(d=96), 1, 1, 256) == 3
