@@ -9,21 +9,25 @@ value = requests (= new tokens) per second.  The roofline object is for that
 decode kernel (HBM bound): algorithmic bytes per launch / average launch time
 from HIP events on the launch stream.
 
-Extra legs in the same run (``extra``): chunked prefill with RoPE on the adapter
-key term (512 new tokens over 16384, 4 agents; TFLOP/s vs bf16 MFMA peak),
-paged decode over 32 shuffled contexts of 4k-64k tokens (GB/s vs HBM peak),
-the LR-cache build of one 4096-token layer (GB/s), and one whole PreLRShared
-step (32 layers x (LR build + 8 agents' prefill of 4096 over 131072), TFLOP/s).
-
-cpu_baseline: the float64 oracle on the host cores, on the primary workload's
-first input set (all 16 requests, repeated until >= 10 s), as requests/s.
+Extra legs in the same run (``extra``), each with its roofline, per-call
+median / p10 / p90, the float64 oracle timed on the host cores
+(``cpu_baseline``) and a parity check of the timed outputs against the oracle:
+the fp32 parity workload, decode variants (RoPE on the adapter key, the rank-4
+qkvo setting, one LR cache per agent, the naive materialising baseline, the
+cross-agent sharing sweep), chunked prefill with RoPE (512 new tokens over
+16384, 4 agents) from contiguous caches and from shuffled pages, paged decode
+over 32 shuffled contexts of 4k-64k tokens, the LR-cache build of one 4096-token
+layer, and one whole PreLRShared step (32 layers x (LR build + 8 agents'
+prefill of 4096 over 131072)).
 
 Inputs of sets that fit the 256 MB Infinity Cache are rotated over several
-independent buffer sets so timed calls read HBM, not the cache.
+independent buffer sets (>= 512 MB together) so timed calls read HBM.
 """
 from __future__ import annotations
 
 import argparse
+import contextlib
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +41,10 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s + HBM GB/s % peak; prefill TFLOP/s % MFMA peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS = 2e-2, 1e-2, 1e-5
+# False (--no-oracle, for profiling runs): legs skip the oracle timing and parity
+CHECK = True
+UNCHECKED = {"cpu_baseline": None, "parity": None, "note_oracle": "oracle not run (--no-oracle)"}
 
 
 # ----------------------------------------------------------------------------- accounting
@@ -93,9 +101,13 @@ def _dev(a):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
-    if a.dtype == np.int32:
-        return torch.from_numpy(a).to("cuda")
     return torch.from_numpy(a).to("cuda")
+
+
+def _host(t):
+    """Device tensor -> float64 numpy (exact widening of bf16 / fp32)."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
 def _randn_bf16(shape, sigma, gen):
@@ -140,43 +152,138 @@ def _call_stats(fn, n_sets, n_calls):
             "p90": float(np.percentile(t, 90)), "calls": n_calls}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16__decode_4ctx_x_8192_r16__hbm_traffic.txt")
-TRAFFIC_SOURCES = ("attention_shared_base_amd/csrc/decode_kernel.h", "attention_shared_base_amd/csrc/decode_bf16.hip",
-                   "attention_shared_base_amd/csrc/api.hip")
-
-
-def measured_traffic():
-    """HBM bytes per launch of the primary decode kernel from the committed counter
-    summary, or None if the kernel sources changed since the counters were taken."""
-    import hashlib
-    try:
-        kv = {}
-        for line in open(TRAFFIC_FILE):
-            if line.startswith("#") or ":" not in line:
-                continue
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-        h = hashlib.sha256()
-        for src in TRAFFIC_SOURCES:
-            h.update(open(os.path.join(ROOT, src), "rb").read())
-        if h.hexdigest()[:16] != kv.get("source_sha256"):
-            return None
-        return int(kv["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+def _timed(fn, n_sets, steps, warmup, stat_calls=None):
+    """(ms per call over the timed region, per-call statistics)."""
+    ms = _time_calls(fn, n_sets, steps, warmup)
+    stats = _call_stats(fn, n_sets, stat_calls if stat_calls else max(10, min(steps, 100)))
+    return ms, stats
 
 
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-# ----------------------------------------------------------------------------- legs
+# ----------------------------------------------------------------------------- HBM traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic__all_legs.txt")
+CSRC = os.path.join(ROOT, "attention_shared_base_amd", "csrc")
+
+
+def kernel_sources_sha():
+    """sha256 (16 hex digits) over every kernel source of the library."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(leg):
+    """HBM bytes per launch of a leg's dominant kernel from the committed counter
+    summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain-copy calibration),
+    with its source; (None, reason) when the kernel sources changed since."""
+    try:
+        rows, sha = {}, None
+        for line in open(TRAFFIC_FILE):
+            line = line.strip()
+            if line.startswith("source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith("leg "):
+                f = dict(kv.split("=", 1) for kv in line.split()[2:])
+                rows[line.split()[1]] = f
+        if sha != kernel_sources_sha():
+            return None, "counters were taken on other kernel sources"
+        if leg not in rows:
+            return None, "no counter record for this leg"
+        return int(rows[leg]["traffic_bytes_per_launch"]), \
+            f"profiles/{os.path.basename(TRAFFIC_FILE)} (rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE; " \
+            f"kernel {rows[leg]['kernel']})"
+    except (OSError, KeyError, ValueError) as e:
+        return None, f"no counter summary ({type(e).__name__})"
+
+
+def _roofline(leg, bound, achieved, bytes_or_flops=None):
+    peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
+    rl = {"bound": bound, "achieved": achieved, "peak": peak,
+          "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": achieved / peak}
+    traffic, src = measured_traffic(leg)
+    rl["traffic"] = traffic
+    rl["traffic_source"] = src
+    return rl
+
+
+# ----------------------------------------------------------------------------- oracle timing
+
+def _host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+@contextlib.contextmanager
+def _one_core():
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            yield
+    except ImportError:  # pragma: no cover
+        yield
+
+
+def _oracle_run(fn, min_seconds):
+    """Run fn at least once and until min_seconds have passed: (first result, calls, seconds)."""
+    t0 = time.perf_counter()
+    res = fn()
+    reps = 1
+    while time.perf_counter() - t0 < min_seconds:
+        fn()
+        reps += 1
+    return res, reps, time.perf_counter() - t0
+
+
+def _cpu(value, unit, sample, threads=None):
+    return {"value": value, "unit": unit, "cores": int(threads if threads else _blas_threads()),
+            "kind": "oracle", "sample": sample, "host_cores": _host_cores()}
+
+
+def _parity(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = got - ref
+    max_abs = float(np.max(np.abs(err)))
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300))
+    ok = bool(np.all(np.isfinite(got))) and (
+        max_abs <= F32_MAX_ABS if dtype == "f32" else (max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2))
+    return {"checked": what, "max_abs": max_abs, "rel_l2": rel,
+            "bar": "max-abs 1e-5" if dtype == "f32" else "max-abs 2e-2 and rel-L2 1e-2", "pass": ok}
+
+
+# ----------------------------------------------------------------------------- decode legs
 
 class DecodeSet:
-    def __init__(self, case):
+    """A seeded decode case uploaded in the kernel's page layouts."""
+
+    def __init__(self, case, per_agent_lr=None):
         import workloads as w
         k, v, lk, lv = w.decode_device_layout(case.k_pool, case.v_pool, case.lk_pool, case.lv_pool)
-        self.q, self.k, self.v, self.lk, self.lv = map(_dev, (case.q, k, v, lk, lv))
+        self.case = case
+        self.q, self.k, self.v = map(_dev, (case.q, k, v))
+        if per_agent_lr is None:
+            self.lk, self.lv = _dev(lk), _dev(lv)
+        else:  # [n_agents, n_pages, page, r] logical pools, one per agent
+            lk_pa, lv_pa = per_agent_lr
+            self.lk = _dev(lk_pa)
+            self.lv = _dev(np.ascontiguousarray(lv_pa.transpose(0, 1, 3, 2)))
         self.crs = _dev(case.ctx_req_start())
         self.agent = _dev(case.req_agent)
         self.bt = _dev(case.block_table)
@@ -185,33 +292,55 @@ class DecodeSet:
         self.out = None
 
 
-def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stats=None, rank=16):
-    import torch
-    import attention_shared_base_amd as lra
+def _oracle_decode(case, rope_theta=None, requests=None, per_agent_lr=None):
+    import oracle
+    import workloads as w
+    rope = None
+    if rope_theta is not None:
+        rope = oracle.rope_tables(max(int(case.ctx_len.max()), 1), case.d, rope_theta)
+    lk, lv = (case.lk_pool, case.lv_pool) if per_agent_lr is None else per_agent_lr
+    return oracle.decode_paged(w.widen(case.q), case.req_ctx, case.req_agent, w.widen(case.k_pool),
+                               w.widen(case.v_pool), w.widen(lk), w.widen(lv), case.block_table,
+                               case.ctx_len, w.widen(case.b_k), w.widen(case.b_v), rope=rope,
+                               requests=requests)
+
+
+def _decode_cases(n_sets, rank=16):
     import workloads as w
     if rank == 16:
-        cases = [w.config2(layer=i) for i in range(n_sets)]
-    else:  # the same shapes and draws at another rank
-        cases = [w.make_decode(2, dtype="bf16", ctx_lens=[8192] * 4, reqs=[(b // 4, b % 4) for b in range(16)],
-                               n_agents=4, h_q=32, h_kv=8, d=128, r=rank, shuffle=False, layer=i)
-                 for i in range(n_sets)]
-    sets = [DecodeSet(c) for c in cases]
+        return [w.config2(layer=i) for i in range(n_sets)]
+    # the same shapes and draws at another rank
+    return [w.make_decode(2, dtype="bf16", ctx_lens=[8192] * 4, reqs=[(b // 4, b % 4) for b in range(16)],
+                          n_agents=4, h_q=32, h_kv=8, d=128, r=rank, shuffle=False, layer=i)
+            for i in range(n_sets)]
+
+
+def _per_agent_lr(case, layer):
+    """One seeded LR pool per agent, [n_agents, n_pages, page, r] (logical layout)."""
+    import workloads as w
+    from workloads.synth import TAG_LK, TAG_LV
+    shape = (case.n_agents,) + tuple(case.lk_pool.shape)
+    return (w.draw(102, TAG_LK, shape, 1.0, "bf16", layer), w.draw(102, TAG_LV, shape, 1.0, "bf16", layer))
+
+
+def run_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, rank=16):
+    """Time lra_attn_decode over n_sets rotated seeded sets of the primary workload's shapes.
+    Returns (case of set 0, ms per call, per-call stats, algorithmic bytes, set 0's output,
+    set 0's per-agent LR pools or None)."""
+    import torch
+    import attention_shared_base_amd as lra
+    cases = _decode_cases(n_sets, rank)
+    pa = [_per_agent_lr(c, i) for i, c in enumerate(cases)] if per_agent else [None] * n_sets
+    sets = [DecodeSet(c, p) for c, p in zip(cases, pa)]
     c0 = cases[0]
     mrpc = int(np.bincount(c0.req_ctx).max())
     max_len = int(c0.ctx_len.max())
-    ws = torch.zeros(lra.decode_workspace_size(
+    ws = torch.zeros(max(16, lra.decode_workspace_size(
         n_q_heads=32, n_kv_heads=8, head_dim=128, rank=rank, dtype=1, n_req=c0.n_req,
         n_ctx=c0.n_ctx, max_req_per_ctx=mrpc, max_ctx_len=max_len,
-        lr_agent_stride=1 if per_agent else 0), dtype=torch.uint8, device="cuda")
+        lr_agent_stride=1 if per_agent else 0)), dtype=torch.uint8, device="cuda")
     for s in sets:
         s.out = torch.empty_like(s.q)
-        if per_agent:
-            # one LR cache per agent (BaseShared): the agents' pools, own draws
-            g = torch.Generator(device="cuda")
-            g.manual_seed(11)
-            n_ag = s.b_k.shape[0]
-            s.lk = _randn_bf16((n_ag,) + tuple(s.lk.shape), 1.0, g)
-            s.lv = _randn_bf16((n_ag,) + tuple(s.lv.shape), 1.0, g)
     cos = sin = None
     if rope_theta is not None:
         cos, sin = lra.rope_table(rope_theta, 128, max_len)
@@ -222,181 +351,112 @@ def primary_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, stat
                    max_req_per_ctx=mrpc, max_ctx_len=max_len, rope_cos=cos, rope_sin=sin,
                    out=s.out, workspace=ws)
 
-    ms = _time_calls(call, n_sets, steps, warmup)
-    if stats is not None:
-        stats.update(_call_stats(call, n_sets, max(20, min(steps, 200))))
+    ms, stats = _timed(call, n_sets, steps, warmup, max(20, min(steps, 200)))
     nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, rank)
     if rope_theta is not None:
         nbytes += 2 * max_len * 64 * 4  # the cos / sin rows, read once
     if per_agent:  # every agent of a context reads its own L_k, L_v rows
         n_ag_ctx = len(np.unique(c0.req_agent[c0.req_ctx == 0]))
         nbytes += int(c0.ctx_len.sum()) * 2 * rank * 2 * (n_ag_ctx - 1)
-    return cases[0], ms, nbytes
+    return c0, ms, stats, nbytes, _host(sets[0].out), pa[0]
 
 
-def extra_workload1_fp32(steps, warmup):
-    """The fp32 parity workload (2 agents over one 256-token context, Hq4 Hkv2 d64 r8): call time
-    of its decode (2 requests) and its causal prefill (2 x 16 new tokens).  Launch-latency bound
-    (a 278 KB working set); reported as time only."""
-    import torch
-    import attention_shared_base_amd as lra
-    import workloads as w
-    dec, pre = w.config1()
-    s = DecodeSet(dec)
-    d_out = torch.empty_like(s.q)
-    q, agent = _dev(pre.q), _dev(pre.req_agent)
-    k, v, lk, lv, bk, bv = map(_dev, (pre.k_base, pre.v_base, pre.l_k, pre.l_v, pre.b_k, pre.b_v))
-    p_out = torch.empty_like(q)
-
-    def call_d(_):
-        lra.decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
-                   max_req_per_ctx=2, max_ctx_len=256, out=d_out)
-
-    def call_p(_):
-        lra.prefill(q, agent, k, v, lk, lv, bk, bv, out=p_out)
-
-    ms_d = _time_calls(call_d, 1, steps, warmup)
-    ms_p = _time_calls(call_p, 1, steps, warmup)
-    return {"workload": "fp32 parity workload: 2 agents over one 256-token context (240 + 16 new), "
-                        "Hq4 Hkv2 d64 r8; decode of 2 requests and prefill of 2 x 16 tokens",
-            "value": ms_d * 1e3, "unit": "us per decode call", "ms_per_call": ms_d,
-            "prefill_us_per_call": ms_p * 1e3,
-            "roofline": None,
-            "note": "launch-latency bound (278 KB working set): time only, no roofline"}
-
-
-def extra_paged_decode(steps, warmup):
-    """32 contexts of U[4096, 65536] tokens, shuffled 16-token pages, r 32 (5+ GB)."""
-    import torch
-    import attention_shared_base_amd as lra
-    import workloads as w
-    lens = w.config4_lengths()
-    table, n_pages = w.page_table(4, lens, shuffle=True, max_blocks=65536 // 16)
-    h_q, h_kv, d, r, n_req = 32, 8, 128, 32, 32
-    g = torch.Generator(device="cuda")
-    g.manual_seed(4)
-    k = _randn_bf16((n_pages, h_kv, d // 8, 16, 8), 1.0, g)
-    v = _randn_bf16((n_pages, h_kv, d, 16), 1.0, g)
-    lk = _randn_bf16((n_pages, 16, r), 1.0, g)
-    lv = _randn_bf16((n_pages, r, 16), 1.0, g)
-    q = _randn_bf16((n_req, h_q, d), 1.0, g)
-    b_k = _randn_bf16((8, r, h_kv * d), 0.05, g)
-    b_v = _randn_bf16((8, r, h_kv * d), 0.05, g)
-    crs = _dev(np.arange(33, dtype=np.int32))
-    agent = _dev((np.arange(32) % 8).astype(np.int32))
-    bt, clen = _dev(table), _dev(lens.astype(np.int32))
-    out = torch.empty_like(q)
-    max_len = int(lens.max())
-    ws = torch.zeros(lra.decode_workspace_size(
-        n_q_heads=h_q, n_kv_heads=h_kv, head_dim=d, rank=r, dtype=1, n_req=n_req, n_ctx=32,
-        max_req_per_ctx=1, max_ctx_len=max_len), dtype=torch.uint8, device="cuda")
-
-    def call(_):
-        lra.decode(q, crs, agent, k, v, lk, lv, bt, clen, b_k, b_v, max_req_per_ctx=1,
-                   max_ctx_len=max_len, out=out, workspace=ws)
-
-    ms = _time_calls(call, 1, steps, warmup)
-    nbytes = decode_bytes(lens, n_req, 8, h_q, h_kv, d, r)
+def _decode_leg(name, workload, case, ms, stats, nbytes, got, oracle_fn, oracle_min_s, **extra):
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": "paged decode: 32 contexts of U[4096,65536] tokens (sum %d), shuffled "
-                        "16-token pages, 32 requests over 8 agents, Hq32 Hkv8 d128 r32, bf16"
-                        % int(lens.sum()),
-            "value": n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-            "algorithmic_bytes": nbytes}
+    leg = {"workload": workload, "value": case.n_req / (ms * 1e-3), "unit": "tokens/s",
+           "ms_per_call": ms, "call_us": stats,
+           "roofline": _roofline(name, "hbm", gbs),
+           "algorithmic_bytes": nbytes}
+    leg.update(UNCHECKED)
+    if CHECK:
+        ref, reps, el = _oracle_run(oracle_fn, oracle_min_s)
+        leg["cpu_baseline"] = _cpu(reps * case.n_req / el, "tokens/s",
+                                   f"full call (all {case.n_req} requests) on the timed set 0, "
+                                   f"{reps}x in {el:.1f} s, float64 NumPy")
+        leg["parity"] = _parity(got, ref, "bf16", f"set 0, all {case.n_req} requests")
+        del leg["note_oracle"]
+    leg.update(extra)
+    return leg
 
 
-def extra_decode_rope(steps, warmup, base_ms):
+def leg_decode_rope(steps, warmup, base_ms):
     """The primary decode workload with RoPE (theta 5e5) on the adapter key term: each
     request's key adapter is rebuilt at head dimension and rotated per page."""
-    case, ms, nbytes = primary_decode(steps, warmup, 4, rope_theta=500000.0)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {
-        "workload": "decode with RoPE on the adapter key: 16 requests over 4 shared 8192-token "
-                    "contexts, Hq32 Hkv8 d128 r16, theta 5e5, bf16",
-        "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
-        "time_vs_no_rope": ms / base_ms,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "algorithmic_bytes": nbytes,
-    }
+    case, ms, stats, nbytes, got, _ = run_decode(steps, warmup, 4, rope_theta=500000.0)
+    return _decode_leg(
+        "decode_rope", "decode with RoPE on the adapter key: 16 requests over 4 shared 8192-token "
+        "contexts, Hq32 Hkv8 d128 r16, theta 5e5, bf16", case, ms, stats, nbytes, got,
+        lambda: _oracle_decode(case, rope_theta=500000.0), 3.0, time_vs_no_rope=ms / base_ms if base_ms else None)
 
 
-def extra_decode_qkvo_r4(steps, warmup):
+def leg_decode_qkvo_r4(steps, warmup):
     """The pages' query/key/value/output LoRA setting (LRAgent App. D.1): rank 4 with RoPE on
-    the adapter key, against the plain rank-4 call on the same shapes (the cost of the key
-    rebuild at the pages' rank)."""
-    _, ms_plain, _ = primary_decode(steps, warmup, 4, rank=4)
-    case, ms, nbytes = primary_decode(steps, warmup, 4, rope_theta=500000.0, rank=4)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {
-        "workload": "decode, rank-4 LoRA with RoPE on the adapter key (qkvo setting): 16 requests "
-                    "over 4 shared 8192-token contexts, Hq32 Hkv8 d128 r4, theta 5e5, bf16",
-        "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
-        "ms_per_call_without_rope": ms_plain, "time_vs_no_rope": ms / ms_plain,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "algorithmic_bytes": nbytes,
-    }
+    the adapter key, against the plain rank-4 call on the same shapes."""
+    _, ms_plain, _, _, _, _ = run_decode(steps, warmup, 4, rank=4)
+    case, ms, stats, nbytes, got, _ = run_decode(steps, warmup, 4, rope_theta=500000.0, rank=4)
+    return _decode_leg(
+        "decode_qkvo_r4", "decode, rank-4 LoRA with RoPE on the adapter key (qkvo setting): 16 "
+        "requests over 4 shared 8192-token contexts, Hq32 Hkv8 d128 r4, theta 5e5, bf16",
+        case, ms, stats, nbytes, got, lambda: _oracle_decode(case, rope_theta=500000.0), 3.0,
+        ms_per_call_without_rope=ms_plain, time_vs_no_rope=ms / ms_plain)
 
 
-def extra_decode_per_agent(steps, warmup, base_ms):
+def leg_decode_per_agent(steps, warmup, base_ms):
     """The primary decode workload with one LR cache per agent (BaseShared / PreLRShared with
     per-agent A): each request reads its agent's L_k, L_v pages beside the shared base pages."""
-    case, ms, nbytes = primary_decode(steps, warmup, 4, per_agent=True)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {
-        "workload": "decode with one LR cache per agent: 16 requests over 4 shared 8192-token "
-                    "contexts (4 agents each), Hq32 Hkv8 d128 r16, bf16",
-        "value": case.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
-        "time_vs_shared_lr": ms / base_ms,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "algorithmic_bytes": nbytes,
-    }
+    case, ms, stats, nbytes, got, pa = run_decode(steps, warmup, 4, per_agent=True)
+    return _decode_leg(
+        "decode_per_agent", "decode with one LR cache per agent: 16 requests over 4 shared "
+        "8192-token contexts (4 agents each), Hq32 Hkv8 d128 r16, bf16", case, ms, stats, nbytes,
+        got, lambda: _oracle_decode(case, per_agent_lr=pa), 3.0, time_vs_shared_lr=ms / base_ms if base_ms else None)
 
 
-def extra_naive_decode(steps, warmup, base_ms):
+def leg_naive_decode(steps, warmup, base_ms, primary_cpu):
     """Baseline of the Flash-LoRA comparison on the primary decode workload: every
     request's K, V materialised at head dimension (expansion kernel), then plain decode
     attention over the per-request caches.  Reported next to the method's time."""
-    import torch
-    import attention_shared_base_amd as lra
     import workloads as w
+    import attention_shared_base_amd as lra
     n_sets = 2
     cases = [w.config2(layer=i) for i in range(n_sets)]
     sets = [DecodeSet(c) for c in cases]
     c0 = cases[0]
     mrpc = int(np.bincount(c0.req_ctx).max())
     max_len = int(c0.ctx_len.max())
-    scratch = {}
+    scratch = [{} for _ in sets]
+    outs = [None] * n_sets
 
     def call(i):
         s = sets[i]
-        lra.naive_decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
-                         max_req_per_ctx=mrpc, max_ctx_len=max_len, scratch=scratch)
+        outs[i] = lra.naive_decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k,
+                                   s.b_v, max_req_per_ctx=mrpc, max_ctx_len=max_len,
+                                   scratch=scratch[i])
 
-    ms = _time_calls(call, n_sets, steps, warmup)
+    ms, stats = _timed(call, n_sets, steps, warmup, 10)
     n_tok = int(c0.ctx_len[c0.req_ctx].sum())
     # bytes the baseline moves: base K, V read and the expanded K, V written per request,
     # the expanded K, V read again by the attention (per KV head, bf16)
-    kv_req = n_tok * 8 * 128 * 2 * 2
-    nbytes = 3 * kv_req
+    nbytes = 3 * n_tok * 8 * 128 * 2 * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {
+    req = [0, 5, 10, 15]
+    leg = {
         "workload": "baseline without Flash-LoRA-Attention: primary decode workload with each "
                     "request's K = K_base + L_k B_k, V = V_base + L_v B_v written to HBM, then "
                     "plain decode attention over the per-request caches",
-        "value": c0.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms,
-        "method_speedup": ms / base_ms,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "algorithmic_bytes": nbytes,
+        "value": c0.n_req / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "call_us": stats,
+        "method_speedup": ms / base_ms if base_ms else None,
+        "roofline": _roofline("naive_decode", "hbm", gbs), "algorithmic_bytes": nbytes,
+        "cpu_baseline": dict(primary_cpu, sample="the primary leg's oracle timing (the same "
+                                                 "workload; the oracle materialises in either case)"),
+        "parity": None,
     }
+    if CHECK:
+        ref = _oracle_decode(c0, requests=req)
+        leg["parity"] = _parity(_host(outs[0])[req], ref[req], "bf16", f"set 0, requests {req}")
+    return leg
 
 
-def extra_agent_scaling(steps, warmup):
+def leg_agent_scaling(steps, warmup, primary_cpu):
     """Cross-agent cache sharing: the primary workload's 4 shared 8192-token contexts (two
     rotated sets of caches) decoded by 1, 2, 4, 8 and 16 requests per context, each with its own
     agent (B_k, B_v), beside the naive baseline that materialises every request's caches.  A row
@@ -444,98 +504,250 @@ def extra_agent_scaling(steps, warmup):
                         "8, 16 requests (agents) per context; method and naive materialising baseline",
             "value": t4 / t1, "unit": "x (time at 4 agents per context / time at 1)",
             "time_16_vs_1": t16 / t1, "per_agents": table, "roofline": None,
-            "note": "scaling study: sharing the base and LR caches across agents"}
+            "cpu_baseline": dict(primary_cpu, sample="the primary leg's oracle timing: the oracle's "
+                                                     "cost is per request, whatever the sharing"),
+            "parity": None,
+            "note": "scaling study (ratio, no roofline): sharing the base and LR caches across agents; "
+                    "its kernels are the primary leg's, checked there and in the tests"}
 
 
-def extra_prefill_rope(steps, warmup, n_sets=2):
-    """512 new tokens over a 16384-token shared context, 4 agents, RoPE 5e5 on the adapter key."""
+def leg_paged_decode(steps, warmup):
+    """Seeded paged decode: 32 contexts of U[4096, 65536] tokens, shuffled 16-token pages,
+    32 requests over 8 agents, r 32 (about 5.4 GB of caches, beyond the Infinity Cache)."""
     import torch
     import attention_shared_base_amd as lra
-    n_req, q_len, kv_len, h_q, h_kv, d, r = 4, 512, 16896, 32, 8, 128, 16
-    g = torch.Generator(device="cuda")
-    g.manual_seed(3)
+    import workloads as w
+    t0 = time.perf_counter()
+    case = w.config4()
+    s = DecodeSet(case)
+    _log(f"paged_decode: seeded inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    lens = case.ctx_len
+    max_len = int(lens.max())
+    s.out = torch.empty_like(s.q)
+    ws = torch.zeros(lra.decode_workspace_size(
+        n_q_heads=32, n_kv_heads=8, head_dim=128, rank=32, dtype=1, n_req=32, n_ctx=32,
+        max_req_per_ctx=1, max_ctx_len=max_len), dtype=torch.uint8, device="cuda")
+
+    def call(_):
+        lra.decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
+                   max_req_per_ctx=1, max_ctx_len=max_len, out=s.out, workspace=ws)
+
+    ms, stats = _timed(call, 1, steps, warmup, 10)
+    nbytes = decode_bytes(lens, 32, 8, 32, 8, 128, 32)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    got = _host(s.out)
+    # oracle on a sample of requests (shortest, longest and two more), timed and scaled to the
+    # whole call by context tokens (the oracle's work is linear in them)
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 18})
+    del s
+    torch.cuda.empty_cache()
+    leg = {"workload": "paged decode: 32 contexts of U[4096,65536] tokens (sum %d), shuffled "
+                        "16-token pages, 32 requests over 8 agents, Hq32 Hkv8 d128 r32, bf16"
+                        % int(lens.sum()),
+            "value": 32 / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "call_us": stats,
+            "roofline": _roofline("paged_decode", "hbm", gbs), "algorithmic_bytes": nbytes,
+            "data": "seeded host generator (workload 4 of the tests)"}
+    leg.update(UNCHECKED)
+    if CHECK:
+        sub = w.decode_subset(case, sample)  # only the sampled contexts' pages (data movement)
+        ref, reps, el = _oracle_run(lambda: _oracle_decode(sub), 0.0)
+        tok_sample = int(lens[sample].sum())
+        t_call = el / reps * int(lens.sum()) / tok_sample
+        leg["cpu_baseline"] = _cpu(32 / t_call, "tokens/s",
+                                   f"requests {sample} ({tok_sample} of {int(lens.sum())} context "
+                                   f"tokens) in {el / reps:.1f} s, scaled to the whole call by tokens")
+        leg["parity"] = _parity(got[sample], ref, "bf16", f"requests {sample}")
+        del leg["note_oracle"]
+    return leg
+
+
+def leg_workload1_fp32(steps, warmup):
+    """The fp32 parity workload (2 agents over one 256-token context, Hq4 Hkv2 d64 r8): call time
+    of its decode (2 requests) and its causal prefill (2 x 16 new tokens).  Launch-latency bound
+    (a 278 KB working set); reported as time only."""
+    import torch
+    import attention_shared_base_amd as lra
+    import oracle
+    import workloads as w
+    dec, pre = w.config1()
+    s = DecodeSet(dec)
+    d_out = torch.empty_like(s.q)
+    q, agent = _dev(pre.q), _dev(pre.req_agent)
+    k, v, lk, lv, bk, bv = map(_dev, (pre.k_base, pre.v_base, pre.l_k, pre.l_v, pre.b_k, pre.b_v))
+    p_out = torch.empty_like(q)
+
+    def call_d(_):
+        lra.decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k, s.b_v,
+                   max_req_per_ctx=2, max_ctx_len=256, out=d_out)
+
+    def call_p(_):
+        lra.prefill(q, agent, k, v, lk, lv, bk, bv, out=p_out)
+
+    ms_d, stats_d = _timed(call_d, 1, steps, warmup)
+    ms_p, stats_p = _timed(call_p, 1, steps, warmup)
+    o_dec = lambda: _oracle_decode(dec)  # noqa: E731
+    o_pre = lambda: oracle.prefill(w.widen(pre.q), pre.req_agent, w.widen(pre.k_base),  # noqa: E731
+                                   w.widen(pre.v_base), w.widen(pre.l_k), w.widen(pre.l_v),
+                                   w.widen(pre.b_k), w.widen(pre.b_v))
+    leg = {"workload": "fp32 parity workload: 2 agents over one 256-token context (240 + 16 new), "
+                        "Hq4 Hkv2 d64 r8; decode of 2 requests and prefill of 2 x 16 tokens",
+            "value": ms_d * 1e3, "unit": "us per decode call", "higher_is_better": False,
+            "ms_per_call": ms_d, "call_us": stats_d,
+            "prefill_us_per_call": ms_p * 1e3, "prefill_call_us": stats_p,
+            "roofline": None,
+            "note": "launch-latency bound (278 KB working set): time only, no roofline"}
+    leg.update(UNCHECKED)
+    if CHECK:
+        ref_d, rd, ed = _oracle_run(o_dec, 2.0)
+        ref_p, rp, ep = _oracle_run(o_pre, 2.0)
+        with _one_core():
+            _, rd1, ed1 = _oracle_run(o_dec, 1.0)
+            _, rp1, ep1 = _oracle_run(o_pre, 1.0)
+        leg["cpu_baseline"] = _cpu(ed / rd * 1e6, "us per decode call",
+                                   f"full decode call repeated {rd}x in {ed:.1f} s; prefill "
+                                   f"{ep / rp * 1e6:.0f} us per call")
+        leg["cpu_baseline_1core"] = _cpu(ed1 / rd1 * 1e6, "us per decode call",
+                                         f"one BLAS thread: decode {rd1}x in {ed1:.1f} s; prefill "
+                                         f"{ep1 / rp1 * 1e6:.0f} us per call", threads=1)
+        leg["parity"] = {"decode": _parity(_host(d_out), ref_d, "f32", "both requests"),
+                         "prefill": _parity(_host(p_out), ref_p, "f32", "all 2 x 16 rows")}
+        del leg["note_oracle"]
+    return leg
+
+
+# ----------------------------------------------------------------------------- prefill legs
+
+def _oracle_prefill(case, rows=None, requests=None, l_k=None, l_v=None):
+    import oracle
+    import workloads as w
+    rope = (oracle.rope_tables(case.kv_len, case.d, case.rope_theta)
+            if case.rope_theta is not None else None)
+    q = w.widen(case.q)
+    agents = case.req_agent
+    if requests is not None:
+        q, agents = q[requests], agents[requests]
+    return oracle.prefill(q, agents, w.widen(case.k_base), w.widen(case.v_base),
+                          w.widen(case.l_k) if l_k is None else l_k,
+                          w.widen(case.l_v) if l_v is None else l_v,
+                          w.widen(case.b_k), w.widen(case.b_v), rope=rope, rows=rows)
+
+
+def leg_prefill_rope(steps, warmup, n_sets=6):
+    """Seeded workload 3: 512 new tokens over a 16384-token shared context, 4 agents, RoPE 5e5
+    on the adapter key; n_sets independent sets of about 86 MB rotated."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    cases = [w.config3(layer=i) for i in range(n_sets)]
     sets = []
-    for _ in range(n_sets):
-        sets.append(dict(
-            q=_randn_bf16((n_req, q_len, h_q, d), 1.0, g),
-            k=_randn_bf16((h_kv, kv_len, d), 1.0, g), v=_randn_bf16((h_kv, kv_len, d), 1.0, g),
-            lk=_randn_bf16((kv_len, r), 1.0, g), lv=_randn_bf16((kv_len, r), 1.0, g),
-            bk=_randn_bf16((4, r, h_kv * d), 0.05, g), bv=_randn_bf16((4, r, h_kv * d), 0.05, g)))
-    agent = _dev(np.arange(4, dtype=np.int32))
-    cos, sin = lra.rope_table(500000.0, d, kv_len)
-    for s in sets:
-        s["out"] = torch.empty_like(s["q"])
+    for c in cases:
+        sets.append(dict(q=_dev(c.q), k=_dev(c.k_base), v=_dev(c.v_base), lk=_dev(c.l_k),
+                         lv=_dev(c.l_v), bk=_dev(c.b_k), bv=_dev(c.b_v)))
+        sets[-1]["out"] = torch.empty_like(sets[-1]["q"])
+    c0 = cases[0]
+    agent = _dev(c0.req_agent)
+    cos, sin = lra.rope_table(500000.0, 128, c0.kv_len)
 
     def call(i):
         s = sets[i]
         lra.prefill(s["q"], agent, s["k"], s["v"], s["lk"], s["lv"], s["bk"], s["bv"],
                     rope_cos=cos, rope_sin=sin, out=s["out"])
 
-    ms = _time_calls(call, n_sets, steps, warmup)
-    fl = prefill_flops(n_req, q_len, kv_len, h_q, h_kv, d, r, rope=True)
+    ms, stats = _timed(call, n_sets, steps, warmup, 20)
+    got = _host(sets[0]["out"])
+    fl = prefill_flops(4, 512, c0.kv_len, 32, 8, 128, 16, rope=True)
     tf = fl / (ms * 1e-3) / 1e12
-    return {"workload": "chunked prefill: 512 new tokens over 16384 shared, 4 agents, RoPE "
+    set_mb = sum(t.numel() * t.element_size() for t in sets[0].values()) / 1e6
+    leg = {"workload": "chunked prefill: 512 new tokens over 16384 shared, 4 agents, RoPE "
                         "theta 5e5 on the adapter key term, Hq32 Hkv8 d128 r16, bf16",
-            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None},
-            "algorithmic_flops": fl}
+            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms, "call_us": stats,
+            "roofline": _roofline("prefill_rope", "mfma", tf), "algorithmic_flops": fl,
+            "input_sets_rotated": n_sets, "input_set_mb": set_mb,
+            "data": "seeded host generator (workload 3 of the tests), one draw per set"}
+    leg.update(UNCHECKED)
+    if CHECK:
+        ref, reps, el = _oracle_run(lambda: _oracle_prefill(c0), 0.0)
+        leg["cpu_baseline"] = _cpu(fl / el * reps / 1e12, "TFLOP/s",
+                                   f"full call (4 requests x 512 rows) on set 0 in {el:.1f} s")
+        leg["parity"] = _parity(got, ref, "bf16", "set 0, all 4 x 512 x 32 rows")
+        del leg["note_oracle"]
+    return leg
 
 
-def extra_prefill_paged(steps, warmup, base_ms):
-    """The prefill leg's workload with the context in shuffled 16-token pages
-    (lra_attn_prefill_paged: staging of the context's rows, then the prefill)."""
+def leg_prefill_paged(steps, warmup, base_ms, n_sets=6):
+    """Workload 3 with the context in shuffled 16-token pages (lra_attn_prefill_paged)."""
     import torch
     import attention_shared_base_amd as lra
-    n_req, q_len, kv_len, h_q, h_kv, d, r = 4, 512, 16896, 32, 8, 128, 16
-    n_pages = kv_len // 16
-    g = torch.Generator(device="cuda")
-    g.manual_seed(5)
+    import oracle
+    import workloads as w
+    cases = [w.config3(layer=i) for i in range(n_sets)]
+    c0 = cases[0]
+    kv_len = c0.kv_len
+    n_pages = (kv_len + 15) // 16
     sets = []
-    for _ in range(2):
-        sets.append(dict(
-            q=_randn_bf16((n_req, q_len, h_q, d), 1.0, g),
-            k=_randn_bf16((n_pages, h_kv, d // 8, 16, 8), 1.0, g),
-            v=_randn_bf16((n_pages, h_kv, d, 16), 1.0, g),
-            lk=_randn_bf16((n_pages, 16, r), 1.0, g), lv=_randn_bf16((n_pages, r, 16), 1.0, g),
-            bk=_randn_bf16((4, r, h_kv * d), 0.05, g), bv=_randn_bf16((4, r, h_kv * d), 0.05, g),
-            bt=torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32)))
-    agent = _dev(np.arange(4, dtype=np.int32))
-    cos, sin = lra.rope_table(500000.0, d, kv_len)
-    ws = torch.empty(lra.prefill_paged_workspace_size(n_q_heads=h_q, n_kv_heads=h_kv, head_dim=d,
-                                                      rank=r, kv_len=kv_len),
+    for i, c in enumerate(cases):
+        ids = w.rng_for(300 + i, 12).permutation(n_pages)
+        kp, lkp = w.paginate(c.k_base, c.l_k, ids, n_pages, 16)
+        vp, lvp = w.paginate(c.v_base, c.l_v, ids, n_pages, 16)
+        k, v, lk, lv = w.decode_device_layout(kp, vp, lkp, lvp)
+        sets.append(dict(q=_dev(c.q), k=_dev(k), v=_dev(v), lk=_dev(lk), lv=_dev(lv),
+                         bk=_dev(c.b_k), bv=_dev(c.b_v), bt=_dev(ids.astype(np.int32))))
+        sets[-1]["out"] = torch.empty_like(sets[-1]["q"])
+        if i == 0:
+            pools0 = (kp, vp, lkp, lvp, ids)
+    agent = _dev(c0.req_agent)
+    cos, sin = lra.rope_table(500000.0, 128, kv_len)
+    ws = torch.empty(lra.prefill_paged_workspace_size(n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                                      rank=16, kv_len=kv_len) + 16,
                      dtype=torch.uint8, device="cuda")
-    for s in sets:
-        s["out"] = torch.empty_like(s["q"])
 
     def call(i):
         s = sets[i]
         lra.prefill_paged(s["q"], agent, s["k"], s["v"], s["lk"], s["lv"], s["bt"], kv_len,
                           s["bk"], s["bv"], rope_cos=cos, rope_sin=sin, out=s["out"], workspace=ws)
 
-    ms = _time_calls(call, 2, steps, warmup)
-    fl = prefill_flops(n_req, q_len, kv_len, h_q, h_kv, d, r, rope=True)
+    ms, stats = _timed(call, n_sets, steps, warmup, 20)
+    got = _host(sets[0]["out"])
+    fl = prefill_flops(4, 512, kv_len, 32, 8, 128, 16, rope=True)
     tf = fl / (ms * 1e-3) / 1e12
-    return {"workload": "paged chunked prefill: the prefill leg's workload (512 new tokens over "
+    kp, vp, lkp, lvp, ids = pools0
+
+    def oracle_paged():  # the oracle gathers the pages itself, then prefills (request 0)
+        kb, lk = oracle.gather_pages(w.widen(kp), w.widen(lkp), ids, kv_len)
+        vb, lv = oracle.gather_pages(w.widen(vp), w.widen(lvp), ids, kv_len)
+        return oracle.prefill(w.widen(c0.q[:1]), c0.req_agent[:1], kb, vb, lk, lv, w.widen(c0.b_k),
+                              w.widen(c0.b_v), rope=oracle.rope_tables(kv_len, 128, 500000.0))
+
+    leg = {"workload": "paged chunked prefill: the prefill leg's workload (512 new tokens over "
                         "16384, 4 agents, RoPE) with the context in shuffled 16-token pages",
-            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms,
+            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms, "call_us": stats,
             "time_vs_contiguous": ms / base_ms if base_ms else None,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None},
-            "algorithmic_flops": fl}
+            "roofline": _roofline("prefill_paged", "mfma", tf), "algorithmic_flops": fl,
+            "input_sets_rotated": n_sets,
+            "data": "seeded host generator (workload 3), shuffled pages per set"}
+    leg.update(UNCHECKED)
+    if CHECK:
+        ref, reps, el = _oracle_run(oracle_paged, 0.0)
+        leg["cpu_baseline"] = _cpu(fl / 4 / (el / reps) / 1e12, "TFLOP/s",
+                                   f"request 0 of 4 (page gather + 512 rows) on set 0 in "
+                                   f"{el / reps:.1f} s; rate of a quarter of the call's flops")
+        leg["parity"] = _parity(got[:1], ref, "bf16", "set 0, request 0 (512 x 32 rows)")
+        del leg["note_oracle"]
+    return leg
 
 
-def extra_lr_build(steps, warmup, n_sets=8):
+def leg_lr_build(steps, warmup, n_sets=8):
+    """Seeded LR-cache build of one 4096-token layer: L = X [A_k | A_v], r 16."""
     import torch
     import attention_shared_base_amd as lra
+    import oracle
+    import workloads as w
     n_tok, d_model, r = 4096, 4096, 16
-    g = torch.Generator(device="cuda")
-    g.manual_seed(5)
-    sets = [dict(x=_randn_bf16((n_tok, d_model), 1.0, g),
-                 ak=_randn_bf16((r, d_model), 1.0 / 64, g), av=_randn_bf16((r, d_model), 1.0 / 64, g),
+    cases = [w.make_lr_build(5, dtype="bf16", n_tok=n_tok, d_model=d_model, r=r, layer=i)
+             for i in range(n_sets)]
+    sets = [dict(x=_dev(c.x), ak=_dev(c.a_k), av=_dev(c.a_v),
                  lk=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda"),
-                 lv=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda"))
-            for _ in range(n_sets)]
+                 lv=torch.empty((n_tok, r), dtype=torch.bfloat16, device="cuda")) for c in cases]
     # one zero-filled workspace for every call (the calls leave it ready)
     n_ws = lra.lr_cache_build_workspace_size(dtype=1, n_tok=n_tok, d_model=d_model, rank=r)
     ws = torch.zeros(max(n_ws, 16), dtype=torch.uint8, device="cuda")
@@ -544,41 +756,52 @@ def extra_lr_build(steps, warmup, n_sets=8):
         s = sets[i]
         lra.lr_cache_build(s["x"], s["ak"], s["av"], s["lk"], s["lv"], workspace=ws)
 
-    ms = _time_calls(call, n_sets, steps, warmup)
+    ms, stats = _timed(call, n_sets, steps, warmup)
     nbytes = lr_build_bytes(n_tok, d_model, r)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": "LR-cache build L = X [A_k|A_v]: X [4096, 4096] bf16, r 16",
-            "value": gbs, "unit": "GB/s", "ms_per_call": ms,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-            "algorithmic_bytes": nbytes}
+    c0 = cases[0]
+    leg = {"workload": "LR-cache build L = X [A_k|A_v]: X [4096, 4096] bf16, r 16",
+            "value": gbs, "unit": "GB/s", "ms_per_call": ms, "call_us": stats,
+            "roofline": _roofline("lr_build", "hbm", gbs), "algorithmic_bytes": nbytes,
+            "input_sets_rotated": n_sets}
+    leg.update(UNCHECKED)
+    if CHECK:
+        (rk, rv), reps, el = _oracle_run(
+            lambda: oracle.lr_cache_build(w.widen(c0.x), w.widen(c0.a_k).T, w.widen(c0.a_v).T), 2.0)
+        got = np.concatenate([_host(sets[0]["lk"]), _host(sets[0]["lv"])], axis=1)
+        leg["cpu_baseline"] = _cpu(nbytes / (el / reps) / 1e9, "GB/s",
+                                   f"X A in float64 on set 0, {reps}x in {el:.1f} s")
+        leg["parity"] = _parity(got, np.concatenate([rk, rv], axis=1), "bf16",
+                                "set 0, all 4096 x 32 outputs")
+        del leg["note_oracle"]
+    return leg
 
 
-def extra_prelr_step(steps, warmup, n_layers=32):
+def leg_prelr_step(steps, warmup, n_layers=32):
     """PreLRShared step: per layer, LR build of 4096 new rows, then 8 agents' prefill.
 
     32 layers of LLaMA-3.1-8B attention shape, each with its own buffers: X
     [4096, 4096], A_k/A_v [16, 4096], K_base/V_base [8, 135168, 128] (131072
     old + 4096 new tokens), L_k/L_v [135168, 16] (old rows given, new rows built
     in the step), per-agent Q [4096, 32, 128] and B [16, 1024].  Inputs are
-    drawn on the GPU (torch Philox) with the same distributions as the seeded
-    host generator; parity of this workload is covered by the tests.
+    drawn on the GPU (torch Philox, 27 GB) with the distributions of the seeded
+    host generator; the last layer's outputs are checked against the oracle.
     """
     import torch
     import attention_shared_base_amd as lra
+    import oracle
     n_new, n_old, d_model, h_q, h_kv, d, r, n_ag = 4096, 131072, 4096, 32, 8, 128, 16, 8
     kv_len = n_old + n_new
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
     layers = []
     for _ in range(n_layers):
-        lk = _randn_bf16((kv_len, r), 1.0, gen)
-        lv = _randn_bf16((kv_len, r), 1.0, gen)
         layers.append(dict(
             x=_randn_bf16((n_new, d_model), 1.0, gen),
             ak=_randn_bf16((r, d_model), 1.0 / 64, gen), av=_randn_bf16((r, d_model), 1.0 / 64, gen),
             k=_randn_bf16((h_kv, kv_len, d), 1.0, gen), v=_randn_bf16((h_kv, kv_len, d), 1.0, gen),
-            lk=lk, lv=lv, q=_randn_bf16((n_ag, n_new, h_q, d), 1.0, gen),
+            lk=_randn_bf16((kv_len, r), 1.0, gen), lv=_randn_bf16((kv_len, r), 1.0, gen),
+            q=_randn_bf16((n_ag, n_new, h_q, d), 1.0, gen),
             bk=_randn_bf16((n_ag, r, h_kv * d), 0.05, gen),
             bv=_randn_bf16((n_ag, r, h_kv * d), 0.05, gen)))
     agent = torch.arange(n_ag, dtype=torch.int32, device="cuda")
@@ -592,17 +815,68 @@ def extra_prelr_step(steps, warmup, n_layers=32):
                                workspace=ws)
             lra.prefill(L["q"], agent, L["k"], L["v"], L["lk"], L["lv"], L["bk"], L["bv"], out=out)
 
-    ms = _time_calls(call, 1, steps, warmup)
-    fl = n_layers * (prefill_flops(n_ag, n_new, kv_len, h_q, h_kv, d, r, rope=False)
-                     + 2 * n_new * d_model * 2 * r)
+    ms, stats = _timed(call, 1, steps, warmup, 3)
+    fl_layer_attn = prefill_flops(n_ag, n_new, kv_len, h_q, h_kv, d, r, rope=False)
+    fl_layer_lr = 2 * n_new * d_model * 2 * r
+    fl = n_layers * (fl_layer_attn + fl_layer_lr)
     tf = fl / (ms * 1e-3) / 1e12
-    return {"workload": "PreLRShared step: 32 layers x (LR build X[4096,4096]·[A_k|A_v] r16, then "
-                        "8 agents' prefill of 4096 new tokens over 131072 shared), Hq32 Hkv8 d128, bf16",
-            "value": tf, "unit": "TFLOP/s", "ms_per_call": ms,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None},
-            "algorithmic_flops": fl}
+    leg = {"workload": "PreLRShared step: 32 layers x (LR build X[4096,4096]·[A_k|A_v] r16, then "
+                       "8 agents' prefill of 4096 new tokens over 131072 shared), Hq32 Hkv8 d128, bf16",
+           "value": tf, "unit": "TFLOP/s", "ms_per_call": ms, "call_us": stats,
+           "roofline": _roofline("prelr_step", "mfma", tf), "algorithmic_flops": fl,
+           "data": "torch Philox draws on the GPU with the seeded generator's distributions"}
+    leg.update(UNCHECKED)
+    if not CHECK:
+        return leg
+    del leg["note_oracle"]
+    # ---- oracle on the last layer (whose rows `out` holds): LR build vs X A in float64, and
+    # attention of 16 sampled rows (first and last included) of all 8 agents given the LR rows
+    # the GPU built.  One (agent, layer) pair is timed at two row counts; the fit
+    # t(n) = a + b n (a: materialising K and V, b: per row) gives the pair's full-call time,
+    # extrapolated x 256 pairs plus 32 LR builds.
+    L = layers[-1]
+    got = _host(out)
+    x, ak, av = _host(L["x"]), _host(L["ak"]), _host(L["av"])
+    (rk, rv), reps_lr, el_lr = _oracle_run(lambda: oracle.lr_cache_build(x, ak.T, av.T), 0.0)
+    lk, lv = _host(L["lk"]), _host(L["lv"])
+    lr_par = _parity(np.concatenate([lk[n_old:], lv[n_old:]], 1), np.concatenate([rk, rv], 1),
+                     "bf16", "last layer's 4096 new LR rows (both caches) vs X A in float64")
+    kb, vb = _host(L["k"]), _host(L["v"])
+    bk, bv = _host(L["bk"]), _host(L["bv"])
+    rows16 = np.unique(np.linspace(0, n_new - 1, 16).astype(np.int64))
+    rows48 = np.unique(np.linspace(0, n_new - 1, 48).astype(np.int64))
+    ok_max, ok_rel, ok = 0.0, 0.0, True
+    t16 = t48 = None
+    for a in range(n_ag):
+        qa = _host(L["q"][a:a + 1])
+        t0 = time.perf_counter()
+        ref = oracle.prefill(qa, np.array([a]), kb, vb, lk, lv, bk, bv, rows=rows16)
+        t = time.perf_counter() - t0
+        if a == 0:
+            t16 = t
+            t0 = time.perf_counter()
+            oracle.prefill(qa, np.array([a]), kb, vb, lk, lv, bk, bv, rows=rows48)
+            t48 = time.perf_counter() - t0
+        p = _parity(got[a:a + 1, rows16], ref, "bf16", "")
+        ok_max, ok_rel, ok = max(ok_max, p["max_abs"]), max(ok_rel, p["rel_l2"]), ok and p["pass"]
+    b_row = max((t48 - t16) / (len(rows48) - len(rows16)), 0.0)
+    a_fix = max(t16 - b_row * len(rows16), 0.0)
+    t_pair = a_fix + b_row * n_new
+    t_total = n_layers * n_ag * t_pair + n_layers * el_lr / reps_lr
+    leg.update({"cpu_baseline": _cpu(fl / t_total / 1e12, "TFLOP/s",
+                                 f"extrapolated: one (agent, layer) pair timed at 16 and 48 query rows "
+                                 f"({t16:.1f} s, {t48:.1f} s; fit {a_fix:.1f} s + {b_row * 1e3:.0f} ms "
+                                 f"per row -> {t_pair:.0f} s per pair), x 256 pairs + 32 LR builds "
+                                 f"({el_lr / reps_lr:.2f} s each) = {t_total / 3600:.1f} h per step"),
+            "parity": {"attention": {"checked": "last layer, 16 rows (first and last included) of "
+                                                "each of the 8 agents, given the GPU-built LR rows",
+                                     "max_abs": ok_max, "rel_l2": ok_rel,
+                                     "bar": "max-abs 2e-2 and rel-L2 1e-2", "pass": ok},
+                       "lr_build": lr_par}})
+    return leg
 
+
+# ----------------------------------------------------------------------------- misc
 
 def copy_calibration(nbytes=1 << 30, reps=10):
     """A plain device-to-device copy of known size, for scaling HBM byte counters."""
@@ -616,34 +890,42 @@ def copy_calibration(nbytes=1 << 30, reps=10):
     print(json.dumps({"copy_calibration_bytes_per_launch": nbytes, "launches": reps}), flush=True)
 
 
-def cpu_baseline(case, min_seconds=10.0):
-    """The float64 oracle, as it stands, on the primary workload's first input set."""
-    import oracle
-    import workloads as w
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    args = [w.widen(x) for x in (case.q, case.k_pool, case.v_pool, case.lk_pool, case.lv_pool,
-                                 case.b_k, case.b_v)]
-    q, kp, vp, lkp, lvp, bk, bv = args
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode_paged(q, case.req_ctx, case.req_agent, kp, vp, lkp, lvp, case.block_table,
-                            case.ctx_len, bk, bv)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    return {"value": reps * case.n_req / el, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"full decode call of the primary workload (16 requests x 8192 keys), "
-                      f"repeated {reps}x in {el:.1f} s, float64 NumPy"}
+def primary_cpu_baselines(case, got, min_seconds=6.0):
+    """The float64 oracle on the primary workload's timed set 0: all BLAS threads, then one."""
+    ref, reps, el = _oracle_run(lambda: _oracle_decode(case), min_seconds)
+    cpu = _cpu(reps * case.n_req / el, "tokens/s",
+               f"full decode call of the primary workload's set 0 (16 requests x 8192 keys), "
+               f"repeated {reps}x in {el:.1f} s, float64 NumPy")
+    with _one_core():
+        _, r1, e1 = _oracle_run(lambda: _oracle_decode(case), 2.0)
+    cpu1 = _cpu(r1 * case.n_req / e1, "tokens/s",
+                f"the same call with one BLAS thread, repeated {r1}x in {e1:.1f} s", threads=1)
+    return cpu, cpu1, _parity(got, ref, "bf16", "set 0, all 16 requests")
 
 
-# ----------------------------------------------------------------------------- main
+def _extra_legs(args, base_ms, primary_cpu, extra=None):
+    """The extra legs by name (base_ms: the primary decode's time, for ratios)."""
+    extra = {} if extra is None else extra
+    pcpu = primary_cpu if primary_cpu else _cpu(None, "tokens/s", "primary leg not run")
+    mid = max(10, args.steps)          # sub-millisecond to millisecond calls
+    slow = max(5, args.steps // 4)     # calls of about a millisecond and more
+    return {"decode_rope": lambda: leg_decode_rope(args.steps, args.warmup, base_ms),
+            "decode_per_agent": lambda: leg_decode_per_agent(args.steps, args.warmup, base_ms),
+            "decode_qkvo_r4": lambda: leg_decode_qkvo_r4(args.steps, args.warmup),
+            "naive_decode": lambda: leg_naive_decode(slow, 3, base_ms, pcpu),
+            "prefill_rope": lambda: leg_prefill_rope(mid, 3),
+            "prefill_paged": lambda: leg_prefill_paged(
+                mid, 3, extra.get("prefill_rope", {}).get("ms_per_call")),
+            "paged_decode": lambda: leg_paged_decode(mid, 3),
+            "workload1_fp32": lambda: leg_workload1_fp32(args.steps, 10),
+            "agent_scaling": lambda: leg_agent_scaling(max(20, args.steps // 2), 5, pcpu),
+            "lr_build": lambda: leg_lr_build(args.steps, 10),
+            "prelr_step": lambda: leg_prelr_step(1, 1)}
+
+
+ALL_LEGS = ("workload1_fp32,agent_scaling,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,"
+            "prefill_rope,prefill_paged,paged_decode,lr_build,prelr_step")
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -652,10 +934,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets of the primary leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra legs")
-    ap.add_argument("--extra", default="workload1_fp32,agent_scaling,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,prefill_rope,"
-                                       "prefill_paged,paged_decode,lr_build,prelr_step",
-                    help="comma-separated extra legs to run")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", default=ALL_LEGS, help="comma-separated extra legs to run")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the primary leg's oracle timing (the extra legs keep theirs)")
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="skip every oracle timing and parity check (profiling runs)")
+    ap.add_argument("--no-primary", action="store_true",
+                    help="skip the primary leg (profiling runs of single extra legs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -674,46 +959,44 @@ def main():
         copy_calibration()
         return
     lra.load()
+    global CHECK
+    CHECK = not args.no_oracle
+
+    if args.no_primary:
+        legs = _extra_legs(args, None, None)
+        for name in [x for x in args.extra.split(",") if x]:
+            _log(f"extra (alone): {name}")
+            print(json.dumps({name: legs[name]()}), flush=True)
+        return
 
     _log("primary: decode, 4 shared contexts x 8192 tokens, 16 requests")
-    call_us = {}
-    case, ms, nbytes = primary_decode(args.steps, args.warmup, args.sets, stats=call_us)
+    case, ms, call_us, nbytes, got, _ = run_decode(args.steps, args.warmup, args.sets)
     gbs = nbytes / (ms * 1e-3) / 1e9
     value = case.n_req / (ms * 1e-3)
     _log(f"primary: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, {value:.0f} tokens/s")
+    cpu = cpu1 = par = None
+    if CHECK and not args.no_cpu_baseline:
+        _log("primary: cpu baseline (oracle)")
+        cpu, cpu1, par = primary_cpu_baselines(case, got)
+    primary_cpu = cpu if cpu else _cpu(None, "tokens/s", "not measured in this run")
 
     extra = {}
     if not args.no_extra:
-        legs = {"decode_rope": lambda: extra_decode_rope(args.steps, args.warmup, ms),
-                "decode_per_agent": lambda: extra_decode_per_agent(args.steps, args.warmup, ms),
-                "decode_qkvo_r4": lambda: extra_decode_qkvo_r4(args.steps, args.warmup),
-                "naive_decode": lambda: extra_naive_decode(max(5, args.steps // 10), 3, ms),
-                "prefill_rope": lambda: extra_prefill_rope(max(5, args.steps // 10), 3),
-                "prefill_paged": lambda: extra_prefill_paged(
-                    max(5, args.steps // 10), 3,
-                    extra.get("prefill_rope", {}).get("ms_per_call")),
-                "paged_decode": lambda: extra_paged_decode(max(5, args.steps // 10), 3),
-                "workload1_fp32": lambda: extra_workload1_fp32(args.steps, 10),
-                "agent_scaling": lambda: extra_agent_scaling(max(20, args.steps // 2), 5),
-                "lr_build": lambda: extra_lr_build(args.steps, 10),
-                "prelr_step": lambda: extra_prelr_step(1, 1)}
+        legs = _extra_legs(args, ms, primary_cpu, extra)
         for name in [x for x in args.extra.split(",") if x]:
             fn = legs[name]
             _log(f"extra: {name}")
+            t0 = time.perf_counter()
             try:
                 extra[name] = fn()
                 rl = extra[name].get("roofline")
                 _log(f"extra: {name}: {extra[name]['value']:.4g} {extra[name]['unit']}"
-                     + (f", {rl['frac'] * 100:.1f}% of peak" if rl else ""))
+                     + (f", {rl['frac'] * 100:.1f}% of peak" if rl else "")
+                     + f" ({time.perf_counter() - t0:.0f} s)")
             except lra.LraError as e:
                 extra[name] = {"error": str(e)}
                 _log(f"extra: {name}: {e}")
             torch.cuda.empty_cache()
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        _log("cpu baseline: oracle")
-        cpu = cpu_baseline(case)
 
     unshared = decode_bytes_unshared(case.ctx_len[case.req_ctx], 32, 8, 128, 16)
     line = {
@@ -737,10 +1020,12 @@ def main():
             "algorithmic_bytes_per_call": nbytes,
             "bytes_if_agents_did_not_share": unshared,
         },
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
+        "roofline": _roofline("primary", "hbm", gbs),
         "cpu_baseline": cpu,
+        "cpu_baseline_1core": cpu1,
+        "parity": par,
         "call_us": call_us,
+        "kernel_sources_sha256": kernel_sources_sha(),
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

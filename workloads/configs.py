@@ -176,6 +176,35 @@ def make_decode(seed, *, dtype, ctx_lens, reqs, n_agents, h_q, h_kv, d, r, page=
         name=name)
 
 
+def decode_subset(case: DecodeCase, requests) -> DecodeCase:
+    """The same decode restricted to ``requests``: their contexts and only those
+    contexts' pages, copied into a compact pool with the block tables renumbered.
+    Pure data movement (every kept value is bit-identical), so that a reference can
+    widen a few requests' caches instead of the whole pool.  The kept requests come
+    in ascending order (requests are grouped by context, so this is context order)."""
+    requests = sorted({int(i) for i in requests})
+    ctxs = sorted({int(case.req_ctx[i]) for i in requests})
+    new_ctx = {c: j for j, c in enumerate(ctxs)}
+    page = case.page
+    nblk = [(int(case.ctx_len[c]) + page - 1) // page for c in ctxs]
+    max_blocks = max(1, max(nblk))
+    old_ids = np.concatenate([case.block_table[c, :n] for c, n in zip(ctxs, nblk)] + [np.zeros(0, np.int32)])
+    table = np.zeros((len(ctxs), max_blocks), dtype=np.int32)
+    off = 0
+    for j, n in enumerate(nblk):
+        table[j, :n] = np.arange(off, off + n)
+        off += n
+    ids = old_ids if off > 0 else np.zeros(1, np.int64)
+    reqs = requests
+    return DecodeCase(
+        dtype=case.dtype, h_q=case.h_q, h_kv=case.h_kv, d=case.d, r=case.r, page=page,
+        q=case.q[reqs], req_ctx=np.array([new_ctx[int(case.req_ctx[i])] for i in reqs], np.int32),
+        req_agent=case.req_agent[reqs], ctx_len=case.ctx_len[ctxs].astype(np.int32),
+        block_table=table, k_pool=case.k_pool[ids], v_pool=case.v_pool[ids],
+        lk_pool=case.lk_pool[ids], lv_pool=case.lv_pool[ids], b_k=case.b_k, b_v=case.b_v,
+        name=f"{case.name} (requests {reqs})")
+
+
 def make_prefill(seed, *, dtype, kv_len, q_len, req_agents, n_agents, h_q, h_kv, d, r,
                  rope_theta=None, q_sigma=1.0, b_sigma=0.05, name="", layer=0):
     n_req = len(req_agents)
