@@ -17,6 +17,7 @@ __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
     "prefill_paged", "prefill_paged_workspace_size", "cache_append", "decode_noalloc",
+    "naive_prefill", "naive_prefill_workspace_size",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +30,8 @@ EXPORTED_SYMBOLS = (
     "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build",
     "lra_lr_cache_build_workspace_size", "lra_rope_table_build",
     "lra_naive_expand_pages", "lra_attn_prefill_paged_workspace_size", "lra_attn_prefill_paged",
-    "lra_cache_append", "lra_attn_decode_noalloc",
+    "lra_cache_append", "lra_attn_decode_noalloc", "lra_naive_prefill_workspace_size",
+    "lra_naive_prefill",
 )
 
 
@@ -96,6 +98,12 @@ def load():
     lib.lra_cache_append.restype = I32
     lib.lra_cache_append.argtypes = [ctypes.POINTER(Dims), I32, P, P, P, P, P, P, P, P, P, I32,
                                      I32, P]
+    lib.lra_naive_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.lra_naive_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), I32, I32]
+    lib.lra_naive_prefill.restype = I32
+    lib.lra_naive_prefill.argtypes = [
+        ctypes.POINTER(Dims), P, I32, I32, P, P, P, I32, P, P, P, P, I32, P, P, I32, P, P,
+        ctypes.c_size_t, P]
     lib.lra_naive_expand_pages.restype = I32
     lib.lra_naive_expand_pages.argtypes = [
         ctypes.POINTER(Dims), I32, P, I32, P, P, P, P, P, I32, I32, P, I32, P, P, P, I32, P, P,
@@ -476,3 +484,53 @@ def cache_append(slot_mapping, k_new, v_new, lk_new, lv_new, k_pool, v_pool, lk_
     _check(lib.lra_cache_append(ctypes.byref(dims), n_tok, _ptr(slot_mapping), _ptr(k_new),
                                 _ptr(v_new), _ptr(lk_new), _ptr(lv_new), _ptr(k_pool), _ptr(v_pool),
                                 _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _stream(k_new, stream)))
+
+
+def naive_prefill_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, n_req, kv_len):
+    """Bytes of the expanded caches ``naive_prefill`` writes (bf16)."""
+    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, LRA_BF16, 0.0)
+    return int(load().lra_naive_prefill_workspace_size(ctypes.byref(dims), n_req, kv_len))
+
+
+def naive_prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, rope_sin=None,
+                  out=None, workspace=None, softmax_scale=0.0, stream=None):
+    """Measurement baseline (not the method, ``lra_naive_prefill``): each request's
+    K_base + rot(L_k B_k) and V_base + L_v B_v written to ``workspace`` (uint8, allocated
+    when not given), then plain causal attention over them.  Arguments as in ``prefill``."""
+    import torch
+    lib = load()
+    n_req, q_len, h_q, d = q.shape
+    h_kv, kv_len, _ = k_base.shape
+    r = l_k.shape[-1]
+    n_agents = b_k.shape[0]
+    per_agent = l_k.dim() == 3
+    lead = (n_agents,) if per_agent else ()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k_base", k_base), ("v_base", v_base), ("l_k", l_k), ("l_v", l_v),
+                    ("b_k", b_k), ("b_v", b_v)):
+        _contig(name, t)
+        _need(_dtype_code(t) == dt, f"{name} dtype differs from q")
+    _contig("req_agent", req_agent)
+    _need(req_agent.dtype == torch.int32 and req_agent.shape == (n_req,), "req_agent [n_req] int32")
+    _need(tuple(v_base.shape) == (h_kv, kv_len, d), "v_base shape")
+    _need(tuple(l_k.shape) == lead + (kv_len, r) and tuple(l_v.shape) == lead + (kv_len, r),
+          "l_k/l_v [(n_agents,) kv_len, r]")
+    _need(tuple(b_k.shape) == (n_agents, r, h_kv * d) and b_v.shape == b_k.shape, "b_k/b_v shape")
+    if rope_cos is not None:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            _contig(name, t)
+            _need(t.dtype == torch.float32 and t.shape[0] >= kv_len and t.shape[1] == d // 2,
+                  f"{name} must be fp32 [>=kv_len, d/2]")
+    if out is None:
+        out = torch.empty_like(q)
+    _contig("out", out)
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale, kv_len * r if per_agent else 0)
+    need = int(lib.lra_naive_prefill_workspace_size(ctypes.byref(dims), n_req, kv_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.lra_naive_prefill(
+        ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_base), _ptr(v_base),
+        kv_len, _ptr(l_k), _ptr(l_v), _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
+        _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(q, stream)))
+    return out

@@ -648,6 +648,100 @@ lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req, const int
     return lra::launch_naive_expand_bf16(a, (hipStream_t)stream);
 }
 
+size_t lra_naive_prefill_workspace_size(const lra_dims* dims, int32_t n_req, int32_t kv_len) {
+    if (check_dims(dims) != LRA_OK || dims->dtype != LRA_BF16 || n_req < 0 || kv_len < 0) return 0;
+    return 2 * (((size_t)n_req * dims->n_kv_heads * kv_len * dims->head_dim * 2 + 255) / 256 * 256);
+}
+
+lra_status lra_naive_prefill(const lra_dims* dims, const void* q, int32_t n_req, int32_t q_len,
+                             const int32_t* req_agent, const void* k_base, const void* v_base,
+                             int32_t kv_len, const void* l_k, const void* l_v, const void* b_k,
+                             const void* b_v, int32_t n_agents, const float* rope_cos,
+                             const float* rope_sin, int32_t rope_rows, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "naive prefill: bf16 only");
+    if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
+    if (q_len < 1) return fail(LRA_ERR_BAD_SHAPE, "q_len %d < 1", q_len);
+    if (kv_len < q_len) return fail(LRA_ERR_BAD_SHAPE, "kv_len %d < q_len %d", kv_len, q_len);
+    if (n_agents < 1) return fail(LRA_ERR_BAD_SHAPE, "n_agents %d < 1", n_agents);
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return fail(LRA_ERR_NULL_PTR, "rope_cos and rope_sin must both be given or both NULL");
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(req_agent);
+    REQUIRE_PTR(k_base);
+    REQUIRE_PTR(v_base);
+    REQUIRE_PTR(l_k);
+    REQUIRE_PTR(l_v);
+    REQUIRE_PTR(b_k);
+    REQUIRE_PTR(b_v);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(workspace);
+    if (rope_cos) {
+        REQUIRE_PTR(rope_cos);
+        REQUIRE_PTR(rope_sin);
+        if (rope_rows < kv_len)
+            return fail(LRA_ERR_BAD_SHAPE, "rope tables hold %d rows < kv_len %d", rope_rows, kv_len);
+    }
+    if (dims->lr_agent_stride > 0 && dims->lr_agent_stride < (long long)kv_len * dims->rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < one agent's LR cache (kv_len*r = %lld)",
+                    (long long)dims->lr_agent_stride, (long long)kv_len * dims->rank);
+    const size_t need = lra_naive_prefill_workspace_size(dims, n_req, kv_len);
+    if (workspace_bytes < need)
+        return fail(LRA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, need);
+    if ((long long)kv_len * 2 * dims->head_dim > 0x7fffffffLL)
+        return fail(LRA_ERR_BAD_SHAPE, "naive prefill: kv_len %d too long", kv_len);
+    if (n_req == 0) return LRA_OK;
+    lra::ExpandContigArgs e;
+    e.req_agent = req_agent;
+    e.k_base = k_base;
+    e.v_base = v_base;
+    e.l_k = l_k;
+    e.l_v = l_v;
+    e.b_k = b_k;
+    e.b_v = b_v;
+    e.rope_cos = rope_cos;
+    e.rope_sin = rope_sin;
+    e.k_out = workspace;
+    e.v_out = (char*)workspace + need / 2;
+    e.lr_stride = dims->lr_agent_stride;
+    e.n_req = n_req;
+    e.kv_len = kv_len;
+    e.n_agents = n_agents;
+    e.h_kv = dims->n_kv_heads;
+    e.head_dim = dims->head_dim;
+    e.rank = dims->rank;
+    st = lra::launch_naive_expand_contig_bf16(e, (hipStream_t)stream);
+    if (st != LRA_OK) return st;
+    lra::PrefillArgs a;
+    a.q = q;
+    a.req_agent = req_agent;
+    a.k_base = e.k_out;
+    a.v_base = e.v_out;
+    a.l_k = l_k;  // unused by the plain mode
+    a.l_v = l_v;
+    a.b_k = b_k;
+    a.b_v = b_v;
+    a.rope_cos = nullptr;  // the expanded keys carry the rotation
+    a.rope_sin = nullptr;
+    a.out = out;
+    a.lr_stride = 0;
+    a.n_req = n_req;
+    a.q_len = q_len;
+    a.kv_len = kv_len;
+    a.n_agents = n_agents;
+    a.h_q = dims->n_q_heads;
+    a.h_kv = dims->n_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.rank = dims->rank;
+    a.scale = eff_scale(dims);
+    a.plain = true;
+    a.kv_req_stride = (int64_t)dims->n_kv_heads * kv_len * dims->head_dim;
+    return lra::launch_prefill_bf16(a, (hipStream_t)stream);
+}
+
 lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos, float* cos_out,
                                 float* sin_out, void* stream) {
     g_err[0] = 0;

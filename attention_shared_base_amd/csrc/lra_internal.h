@@ -78,6 +78,10 @@ struct PrefillArgs {
     int32_t h_q, h_kv, head_dim, rank;
     float scale;
     int64_t lr_stride;  // elements between agents' LR caches (0: one shared LR cache)
+    // measurement baseline only: plain attention (no low-rank terms, L and B
+    // unused) over per-request caches kv_req_stride elements apart
+    bool plain = false;
+    int64_t kv_req_stride = 0;
 };
 
 lra_status launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
@@ -134,6 +138,26 @@ struct ExpandArgs {
 };
 
 lra_status launch_naive_expand_bf16(const ExpandArgs& a, hipStream_t s);
+
+// Contiguous expansion for the prefill baseline: per request, K_base + rot(L_k B_k)
+// and V_base + L_v B_v into [n_req][H_kv][kv_len][d].
+struct ExpandContigArgs {
+    const int32_t* req_agent;
+    const void* k_base;
+    const void* v_base;
+    const void* l_k;
+    const void* l_v;
+    const void* b_k;
+    const void* b_v;
+    const float* rope_cos;
+    const float* rope_sin;
+    void* k_out;
+    void* v_out;
+    int64_t lr_stride;
+    int32_t n_req, kv_len, n_agents, h_kv, head_dim, rank;
+};
+
+lra_status launch_naive_expand_contig_bf16(const ExpandContigArgs& a, hipStream_t s);
 
 // ----------------------------------------------------------------- paged cache
 struct PagedArgs {

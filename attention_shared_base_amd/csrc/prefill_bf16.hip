@@ -69,6 +69,7 @@ struct PrefillK {
     int32_t n_req, q_len, kv_len, n_agents, h_q, h_kv, g, n_qblk;
     float scale_log2;
     int64_t lr_stride;  // per-agent LR caches: elements between agents' caches (0: shared)
+    int64_t kv_req_stride;  // plain mode: elements between requests' K / V caches
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -126,7 +127,10 @@ LRA_DEV float max3(float a, float b, float c) {
     return r;
 }
 
-template <int D, int R, bool ROPE>
+// PLAIN (measurement baseline only): plain attention over per-request K / V
+// caches kv_req_stride elements apart, with no low-rank terms (L, B unused); the
+// row sums still come from the ones row of the value-side tile.
+template <int D, int R, bool ROPE, bool PLAIN>
 __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int RB = 2 * D;                 // bytes per K / V row (and per cos / sin row)
     constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -142,12 +146,12 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int NKR = RW / 16;              // k-steps over rank
     // 16-byte rank chunks of an L tile that come from HBM (rank 4: one chunk,
     // ranks 4-7 zero); the ones row is the first rank of the next chunk
-    constexpr int RCH = R < 8 ? 1 : R / 8;
+    constexpr int RCH = PLAIN ? 0 : (R < 8 ? 1 : R / 8);
     constexpr int ONES_RANK = 8 * RCH;        // = R for R >= 8
     constexpr int NLT = (ONES_RANK + 1 + 31) / 32;  // rank tiles of O_lr incl. the ones row
     constexpr int ONES_T = ONES_RANK / 32;    // tile holding the ones row
     constexpr int ONES_M = ONES_RANK % 32;    // its row inside the tile
-    constexpr int NLK = RW / 8;               // L_k chunks held
+    constexpr int NLK = PLAIN ? 0 : RW / 8;   // L_k chunks held
     constexpr int NLV = 4 * NLT;              // L_v chunks held (ranks, ones row, zeros)
     constexpr int TLK = NLK * 1024;
     constexpr int TLV = NLV * VBS;
@@ -164,6 +168,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     static_assert((R % 8 == 0 && R <= 32) || R == 4, "rank 4, 8, 16, 24 or 32");
     static_assert(NU >= 1 && NI % WAVES == 0, "tile blocks divide over the wavefronts");
     static_assert(RCH <= 4, "L_v DMA uses wavefronts 4..7");
+    static_assert(!(PLAIN && ROPE), "the plain baseline takes pre-rotated keys");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -203,8 +208,8 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     const int n_tiles = (kv_len - q_len + last_tok) / KT + 1;
 
     const size_t hstride = (size_t)kv_len * D;
-    const bf16* kb = a.k_base + (size_t)h * hstride;
-    const bf16* vb = a.v_base + (size_t)h * hstride;
+    const bf16* kb = a.k_base + (size_t)req * a.kv_req_stride + (size_t)h * hstride;
+    const bf16* vb = a.v_base + (size_t)req * a.kv_req_stride + (size_t)h * hstride;
 
     // ---- HBM -> LDS tile DMA.  Block i of a K / V / cos / sin tile: lane l carries
     // row key = i + NI*(l / CPR), chunk l % CPR.  L chunk c: lane l carries key l.
@@ -224,7 +229,8 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         const auto rk = make_rsrc(kb + (size_t)key0 * D, rem * RB);
 #pragma unroll
         for (int u = 0; u < NU; ++u) dma_1k(rk, smem_lds + OFF_K + b * TK + (wave + WAVES * u) * KBS, voff_row[u]);
-        if constexpr (R < 8) {
+        if constexpr (PLAIN) {
+        } else if constexpr (R < 8) {
             if (wave < 4)
                 dma_256(make_rsrc(lk_ag + (size_t)(key0 + 16 * wave) * R,
                                   (uint32_t)max((int)rem - 16 * wave, 0) * (2 * R)),
@@ -250,7 +256,8 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) dma_1k(rv, smem_lds + OFF_V + b * TV + (wave + WAVES * u) * VBS, voff_row[u]);
         const int c = wave - 4;
-        if constexpr (R < 8) {
+        if constexpr (PLAIN) {
+        } else if constexpr (R < 8) {
             if (c >= 0)
                 dma_256(make_rsrc(lv_ag + (size_t)(key0 + 16 * c) * R,
                                   (uint32_t)max((int)rem - 16 * c, 0) * (2 * R)),
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     // ---- qB^T = B_k^(h) Q^T (no RoPE).  A row rho takes rank 16kr + rho with
     // bits 2 and 3 swapped, so that C lane (row, hh) slot e holds rank 16kr + 8hh + e.
     bf16x8 qbf[NKR];
-    if constexpr (!ROPE) {
+    if constexpr (!ROPE && !PLAIN) {
 #pragma unroll
         for (int kr = 0; kr < NKR; ++kr) {
             f32x16 c = {};
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
                 s[mt] = mfma32x32x16(*(const bf16x8*)(kp + mt * KMT + ks * 32), qf[ks], s[mt]);
-        if constexpr (!ROPE) {
+        if constexpr (!ROPE && !PLAIN) {
 #pragma unroll
             for (int kr = 0; kr < NKR; ++kr)
 #pragma unroll
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     __syncthreads();  // every S(0) read done before K(2) lands in buffer 0
 
     // instruction counts of the two overlapped phases (scheduling hints only)
-    constexpr int NS_MFMA = 2 * NKS + (ROPE ? 0 : 2 * NKR);
+    constexpr int NS_MFMA = 2 * NKS + (ROPE || PLAIN ? 0 : 2 * NKR);
     constexpr int NP_MFMA = 4 * (NDT + NLT);
 
     // phase 1 of tile t: S(t+1) from K buffer kb on the matrix cores (a stale
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     const float l_mine = acc_lr[ONES_T][OV];
     const float l_row = __shfl(l_mine, n32 + 32 * OH);
 #pragma unroll
-    for (int kr = 0; kr < NKR; ++kr) {
+    for (int kr = 0; kr < (PLAIN ? 0 : NKR); ++kr) {
         // B_v^T operand: lane (dim 32dt + n32, k-group hh) -> ranks rank_of(kr, e)
         bf16x8 bvt[NDT];
 #pragma unroll
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     }
 }
 
-template <int D, int R, bool ROPE>
+template <int D, int R, bool ROPE, bool PLAIN = false>
 lra_status launch_t(const lra::PrefillArgs& p, hipStream_t s) {
     PrefillK k;
     k.q = (const bf16*)p.q;
@@ -659,6 +666,7 @@ lra_status launch_t(const lra::PrefillArgs& p, hipStream_t s) {
     k.n_qblk = (p.q_len + WAVES * tw - 1) / (WAVES * tw);
     k.scale_log2 = p.scale * LRA_LOG2E;
     k.lr_stride = p.lr_stride;
+    k.kv_req_stride = PLAIN ? p.kv_req_stride : 0;
     // tiles are addressed through 32-bit buffer ranges of kv_len rows of 2*D bytes
     if ((long long)p.kv_len * 2 * D > 0x7fffffffLL) {
         lra::set_error("prefill: kv_len %d too long for 32-bit tile addressing", p.kv_len);
@@ -669,7 +677,7 @@ lra_status launch_t(const lra::PrefillArgs& p, hipStream_t s) {
         lra::set_error("prefill: grid of %lld workgroups too large", grid);
         return LRA_ERR_BAD_SHAPE;
     }
-    hipLaunchKernelGGL((lra_prefill_bf16_kernel<D, R, ROPE>), dim3((unsigned)grid), dim3(512), 0, s, k);
+    hipLaunchKernelGGL((lra_prefill_bf16_kernel<D, R, ROPE, PLAIN>), dim3((unsigned)grid), dim3(512), 0, s, k);
     return lra::check_launch("lra_prefill_bf16_kernel");
 }
 
@@ -698,6 +706,16 @@ lra_status launch_prefill_bf16(const PrefillArgs& p, hipStream_t s) {
     const int g = p.h_q / p.h_kv;
     if (32 % g != 0) {
         set_error("bf16 prefill packs 32 rows per wavefront: H_q/H_kv = %d must divide 32", g);
+        return LRA_ERR_UNSUPPORTED;
+    }
+    if (p.plain) {
+        if (p.rope_cos) {
+            set_error("plain prefill takes pre-rotated keys (no RoPE tables)");
+            return LRA_ERR_UNSUPPORTED;
+        }
+        if (p.head_dim == 128) return launch_t<128, 8, false, true>(p, s);
+        if (p.head_dim == 64) return launch_t<64, 8, false, true>(p, s);
+        set_error("prefill: unsupported head_dim %d", p.head_dim);
         return LRA_ERR_UNSUPPORTED;
     }
     return p.rope_cos ? launch_rope<true>(p, s) : launch_rope<false>(p, s);

@@ -736,6 +736,98 @@ def leg_prefill_paged(steps, warmup, base_ms, n_sets=6):
     return leg
 
 
+def leg_naive_prefill(steps, warmup, base_ms, n_sets=6):
+    """Baseline of the Flash-LoRA comparison on workload 3 (512 new tokens over 16384, 4
+    agents, RoPE): each request's K_base + rot(L_k B_k) and V_base + L_v B_v written to HBM
+    (lra_naive_prefill), then plain causal attention over the per-request caches."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    cases = [w.config3(layer=i) for i in range(n_sets)]
+    sets = []
+    for c in cases:
+        sets.append(dict(q=_dev(c.q), k=_dev(c.k_base), v=_dev(c.v_base), lk=_dev(c.l_k),
+                         lv=_dev(c.l_v), bk=_dev(c.b_k), bv=_dev(c.b_v)))
+        sets[-1]["out"] = torch.empty_like(sets[-1]["q"])
+    c0 = cases[0]
+    agent = _dev(c0.req_agent)
+    cos, sin = lra.rope_table(500000.0, 128, c0.kv_len)
+    ws = torch.empty(lra.naive_prefill_workspace_size(n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                                      rank=16, n_req=4, kv_len=c0.kv_len),
+                     dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        s = sets[i]
+        lra.naive_prefill(s["q"], agent, s["k"], s["v"], s["lk"], s["lv"], s["bk"], s["bv"],
+                          rope_cos=cos, rope_sin=sin, out=s["out"], workspace=ws)
+
+    ms, stats = _timed(call, n_sets, steps, warmup, 20)
+    fl = prefill_flops(4, 512, c0.kv_len, 32, 8, 128, 16, rope=True)
+    tf = fl / (ms * 1e-3) / 1e12
+    leg = {"workload": "baseline without Flash-LoRA-Attention: workload 3 (512 new tokens over "
+                       "16384, 4 agents, RoPE) with each request's K = K_base + rot(L_k B_k), "
+                       "V = V_base + L_v B_v written to HBM, then plain causal attention",
+           "value": tf, "unit": "TFLOP/s (the method's algorithmic flops / baseline time)",
+           "ms_per_call": ms, "call_us": stats,
+           "method_speedup": ms / base_ms if base_ms else None,
+           "roofline": _roofline("naive_prefill", "mfma", tf), "algorithmic_flops": fl,
+           "input_sets_rotated": n_sets}
+    leg.update(UNCHECKED)
+    if CHECK:
+        rows = np.unique(np.linspace(0, 511, 16).astype(np.int64))
+        ref, reps, el = _oracle_run(lambda: _oracle_prefill(c0, rows=rows), 0.0)
+        leg["cpu_baseline"] = _cpu(fl * len(rows) / 512 / (el / reps) / 1e12, "TFLOP/s",
+                                   f"16 of 512 rows of all 4 requests on set 0 in {el / reps:.1f} s, "
+                                   f"scaled by rows (the oracle materialises either way)")
+        leg["parity"] = _parity(_host(sets[0]["out"])[:, rows], ref, "bf16",
+                                "set 0, 16 rows (first and last included) x 4 requests x 32 heads")
+        del leg["note_oracle"]
+    return leg
+
+
+def leg_naive_paged_decode(steps, warmup, base_ms):
+    """Baseline of the Flash-LoRA comparison on workload 4 (32 shuffled contexts of 4k-64k
+    tokens, r 32): each request's K, V expanded to pages of its own, then plain decode."""
+    import torch
+    import attention_shared_base_amd as lra
+    import workloads as w
+    case = w.config4()
+    s = DecodeSet(case)
+    lens = case.ctx_len
+    max_len = int(lens.max())
+    scratch = {}
+    outs = [None]
+
+    def call(_):
+        outs[0] = lra.naive_decode(s.q, s.crs, s.agent, s.k, s.v, s.lk, s.lv, s.bt, s.clen, s.b_k,
+                                   s.b_v, max_req_per_ctx=1, max_ctx_len=max_len, scratch=scratch)
+
+    ms, stats = _timed(call, 1, steps, warmup, 5)
+    n_tok = int(lens.sum())
+    nbytes = 3 * n_tok * 8 * 128 * 2 * 2  # base read, expanded written, expanded read
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    got = _host(outs[0])
+    leg = {"workload": "baseline without Flash-LoRA-Attention: workload 4 (32 contexts of "
+                       "U[4096,65536] tokens, shuffled pages, r 32) with each request's K, V "
+                       "materialised to pages of its own, then plain decode",
+           "value": 32 / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "call_us": stats,
+           "method_speedup": ms / base_ms if base_ms else None,
+           "roofline": _roofline("naive_paged_decode", "hbm", gbs), "algorithmic_bytes": nbytes}
+    leg.update(UNCHECKED)
+    del s, scratch
+    torch.cuda.empty_cache()
+    if CHECK:
+        sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7, 22})
+        sub = w.decode_subset(case, sample)
+        ref, reps, el = _oracle_run(lambda: _oracle_decode(sub), 0.0)
+        t_call = el / reps * n_tok / int(lens[sample].sum())
+        leg["cpu_baseline"] = _cpu(32 / t_call, "tokens/s",
+                                   f"requests {sample} in {el / reps:.1f} s, scaled by context tokens")
+        leg["parity"] = _parity(got[sample], ref, "bf16", f"requests {sample}")
+        del leg["note_oracle"]
+    return leg
+
+
 def leg_lr_build(steps, warmup, n_sets=8):
     """Seeded LR-cache build of one 4096-token layer: L = X [A_k | A_v], r 16."""
     import torch
@@ -917,6 +1009,10 @@ def _extra_legs(args, base_ms, primary_cpu, extra=None):
             "prefill_paged": lambda: leg_prefill_paged(
                 mid, 3, extra.get("prefill_rope", {}).get("ms_per_call")),
             "paged_decode": lambda: leg_paged_decode(mid, 3),
+            "naive_prefill": lambda: leg_naive_prefill(
+                mid, 3, extra.get("prefill_rope", {}).get("ms_per_call")),
+            "naive_paged_decode": lambda: leg_naive_paged_decode(
+                slow, 2, extra.get("paged_decode", {}).get("ms_per_call")),
             "workload1_fp32": lambda: leg_workload1_fp32(args.steps, 10),
             "agent_scaling": lambda: leg_agent_scaling(max(20, args.steps // 2), 5, pcpu),
             "lr_build": lambda: leg_lr_build(args.steps, 10),
@@ -924,7 +1020,8 @@ def _extra_legs(args, base_ms, primary_cpu, extra=None):
 
 
 ALL_LEGS = ("workload1_fp32,agent_scaling,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,"
-            "prefill_rope,prefill_paged,paged_decode,lr_build,prelr_step")
+            "prefill_rope,prefill_paged,naive_prefill,paged_decode,naive_paged_decode,lr_build,"
+            "prelr_step")
 
 
 def main():
@@ -963,10 +1060,12 @@ def main():
     CHECK = not args.no_oracle
 
     if args.no_primary:
-        legs = _extra_legs(args, None, None)
+        done = {}
+        legs = _extra_legs(args, None, None, done)
         for name in [x for x in args.extra.split(",") if x]:
             _log(f"extra (alone): {name}")
-            print(json.dumps({name: legs[name]()}), flush=True)
+            done[name] = legs[name]()
+            print(json.dumps({name: done[name]}), flush=True)
         return
 
     _log("primary: decode, 4 shared contexts x 8192 tokens, 16 requests")

@@ -366,6 +366,31 @@ lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req,
                                   void* k_out, void* v_out, int32_t out_blocks,
                                   void* stream);
 
+/*
+ * Measurement baseline for prefill, not part of the method: the naive
+ * reconstruction of LRAgent §3 / App. B for a chunked prefill.  For every
+ * request i (agent a = req_agent[i]) it writes to the workspace
+ *     K_i = K_base + rot(L_k B_k^(a)),  V_i = V_base + L_v B_v^(a)
+ * ([n_req, H_kv, kv_len, d] each, bf16 rounded to nearest even; rot as in
+ * lra_attn_prefill when RoPE tables are given), then runs plain causal
+ * attention of each request's queries over its own K_i, V_i.  Arguments and
+ * result as in lra_attn_prefill (with lr_agent_stride the agent's own LR rows
+ * are expanded), plus
+ *   workspace   device, caller-owned, >= lra_naive_prefill_workspace_size()
+ *               bytes; holds the expanded caches (2 x n_req x H_kv x kv_len x
+ *               d x 2 bytes), no state is kept between calls
+ * bf16 only.
+ */
+size_t lra_naive_prefill_workspace_size(const lra_dims* dims, int32_t n_req, int32_t kv_len);
+lra_status lra_naive_prefill(const lra_dims* dims,
+                             const void* q, int32_t n_req, int32_t q_len,
+                             const int32_t* req_agent,
+                             const void* k_base, const void* v_base, int32_t kv_len,
+                             const void* l_k, const void* l_v,
+                             const void* b_k, const void* b_v, int32_t n_agents,
+                             const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

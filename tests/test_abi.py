@@ -304,3 +304,27 @@ def test_decode_noalloc_limits_and_dtype():
     assert "scratch" in lib.lra_last_error().decode()
     assert call(dims(dt=0), 1, 1, 256) == 3
     assert call(dims(d=96), 1, 1, 256) == 3
+
+
+def test_naive_prefill_validation():
+    lib = lra.load()
+    dm = dims()
+    need = lib.lra_naive_prefill_workspace_size(ctypes.byref(dm), 4, 1000)
+    assert need == 2 * 4 * 8 * 1000 * 128 * 2
+    assert lib.lra_naive_prefill_workspace_size(ctypes.byref(dims(dt=0)), 4, 1000) == 0
+
+    def call(dm_=dm, **o):
+        a = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, kv_len=256, lk=A, lv=A, bk=A, bv=A,
+                 n_agents=2, cos=None, sin=None, rows=256, out=A, ws=A, wsz=1 << 30)
+        a.update(o)
+        return lib.lra_naive_prefill(ctypes.byref(dm_), a["q"], a["n_req"], a["q_len"], a["agent"],
+                                     a["k"], a["v"], a["kv_len"], a["lk"], a["lv"], a["bk"], a["bv"],
+                                     a["n_agents"], a["cos"], a["sin"], a["rows"], a["out"], a["ws"],
+                                     a["wsz"], None)
+    assert call(dims(dt=0)) == 3
+    assert call(q_len=0) == 2
+    assert call(kv_len=8) == 2
+    assert call(ws=None) == 1
+    assert call(wsz=16) == 5
+    assert call(cos=A, sin=A, rows=255) == 2
+    assert call(n_req=0) == 0

@@ -52,3 +52,62 @@ def test_naive_cfg2_sampled():
     got = _naive(dd)
     ref = oracle_decode(case, requests=[0, 5, 15])
     assert_parity(got[[0, 5, 15]], ref[[0, 5, 15]], "bf16", "cfg2 naive")
+
+
+# ---- the prefill baseline: per-request K_base + rot(L_k B_k), V_base + L_v B_v in HBM, then
+# plain causal attention over them (lra_naive_prefill)
+
+def _naive_prefill(case):
+    import attention_shared_base_amd as lra
+    from gpu_helpers import PrefillDev
+    d = PrefillDev(case)
+    return host(lra.naive_prefill(d.q, d.agent, d.k, d.v, d.lk, d.lv, d.b_k, d.b_v,
+                                  rope_cos=d.cos, rope_sin=d.sin)), d
+
+
+PREFILL_CASES = [
+    # label, h_q, h_kv, d, r, kv_len, q_len, rope
+    ("g4 d128 r16", 32, 8, 128, 16, 300, 70, False),
+    ("g4 d128 r16 rope", 32, 8, 128, 16, 300, 70, True),
+    ("g2 d64 r8 rope", 8, 4, 64, 8, 777, 129, True),
+    ("g8 d128 r32", 16, 2, 128, 32, 129, 129, False),
+    ("g4 d128 r4 rope", 32, 8, 128, 4, 1000, 333, True),
+]
+
+
+@pytest.mark.parametrize("label,h_q,h_kv,d,r,kv_len,q_len,rope", PREFILL_CASES,
+                         ids=[c[0] for c in PREFILL_CASES])
+def test_naive_prefill_matches_oracle_and_method(label, h_q, h_kv, d, r, kv_len, q_len, rope):
+    from gpu_helpers import oracle_prefill
+    case = w.make_prefill(61, dtype="bf16", kv_len=kv_len, q_len=q_len, req_agents=[2, 0, 1],
+                          n_agents=3, h_q=h_q, h_kv=h_kv, d=d, r=r,
+                          rope_theta=500000.0 if rope else None, b_sigma=0.1, name=label)
+    got, dd = _naive_prefill(case)
+    ref = oracle_prefill(case)
+    print(f"[naive prefill] {label}: ", end="", flush=True)
+    ma, rel = assert_parity(got, ref, "bf16", label)
+    print(f"max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
+    assert metrics(got, host(dd.run()))[1] < 1e-2
+
+
+def test_naive_prefill_cfg3_sampled_rows():
+    from gpu_helpers import oracle_prefill
+    case = w.config3()
+    got, _ = _naive_prefill(case)
+    rows = [0, 1, 255, 510, 511]
+    ref = oracle_prefill(case, rows=rows)
+    ma, rel = assert_parity(got[:, rows], ref, "bf16", "cfg3 naive prefill")
+    print(f"[naive prefill] cfg3 sampled rows: max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
+
+
+def test_naive_paged_decode_cfg4_sampled():
+    """The decode baseline on the paged long-trajectory workload: each request's context
+    expanded to pages of its own (32 x up to 4096 pages), then plain decode."""
+    case = w.config4()
+    dd = DecodeDev(case)
+    got = _naive(dd)
+    sample = sorted({int(np.argmin(case.ctx_len)), int(np.argmax(case.ctx_len)), 7, 22})
+    sub = w.decode_subset(case, sample)
+    ref = oracle_decode(sub)
+    ma, rel = assert_parity(got[sample], ref, "bf16", "cfg4 naive decode")
+    print(f"[naive] cfg4 sampled requests {sample}: max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
