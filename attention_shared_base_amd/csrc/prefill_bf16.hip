@@ -32,7 +32,8 @@
 // Data movement.  64-key tiles go HBM -> LDS by buffer_load ... lds (no
 // register staging): one instruction moves 1 KB, lane i's 16 bytes landing at
 // 16*i, and keys past kv_len read as zero through the buffer range.  Each 1 KB
-// block of a K / V / cos / sin tile holds the rows key = i + NI*m of block i,
+// block of a K / V tile (and of the cos / sin rows of key offsets 0..63) holds
+// the rows key = i + NI*m of block i,
 // and consecutive blocks sit 1040 B (K, cos, sin) or 1088 B (V) apart: that
 // spreads the 16 rows a 16-lane row read touches over all 64 banks, and the
 // 4 rows of a transposing read over the four 64-byte bank quarters, with LDS
@@ -43,7 +44,11 @@
 // Pipeline per tile t: K is loaded two tiles ahead and V one tile ahead, so
 // S(t+1) is on the matrix cores while the softmax of S(t) runs on the VALU,
 // followed by P(t)V(t) with the row max of S(t+1) in its shadow; one barrier
-// per tile (two with RoPE: raw K(t+2) lands, K'(t+2) is rebuilt in place).
+// per tile.  With RoPE, K is loaded three tiles ahead into a ring of three
+// buffers and each raw tile is rebuilt in place (K' = K_base + rot(L_k B_k))
+// in the step before its score MFMAs; the rotation angle of a key is that of
+// its tile's first position plus that of its offset in the tile (angle
+// addition from cos / sin rows held in LDS and registers).
 #include <type_traits>
 
 #include "lra_common.h"
@@ -155,12 +160,16 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     constexpr int NLV = 4 * NLT;              // L_v chunks held (ranks, ones row, zeros)
     constexpr int TLK = NLK * 1024;
     constexpr int TLV = NLV * VBS;
+    // K / L_k tile buffers: two, or with RoPE a ring of three (a raw key tile is
+    // rebuilt in place one step before the step whose score MFMAs read it)
+    constexpr int NKB = ROPE ? 3 : 2;
     constexpr int OFF_K = 0;
-    constexpr int OFF_V = OFF_K + 2 * TK;
+    constexpr int OFF_V = OFF_K + NKB * TK;
     constexpr int OFF_LK = OFF_V + 2 * TV;
-    constexpr int OFF_LV = OFF_LK + 2 * TLK;
-    constexpr int OFF_CS = OFF_LV + 2 * TLV;  // RoPE: cos / sin tiles, two buffers
-    constexpr int LDS_BYTES = OFF_CS + (ROPE ? 4 * TK : 0);
+    constexpr int OFF_LV = OFF_LK + NKB * TLK;
+    constexpr int OFF_CS = OFF_LV + 2 * TLV;  // RoPE: cos / sin of key offsets 0..63 (whole kernel)
+    constexpr int OFF_CB = OFF_CS + 2 * TK;   // RoPE: cos / sin rows of each tile's first key, ring of 3
+    constexpr int LDS_BYTES = ROPE ? OFF_CB + NKB * 2048 : OFF_CS;
     constexpr int KMT = (32 / NI) * RB;       // K tile offset of keys 32..63
     constexpr int VKS = (D == 128) ? RB : 2 * RB;   // V offset of the next 16 keys
     constexpr int V8 = (D == 128) ? 8 * VBS : RB;   // V offset of rows +8
@@ -186,9 +195,16 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
 
     const int g = a.g;
     const int TW = 32 / g;  // tokens per wavefront
-    const int qb = blockIdx.x % a.n_qblk;
-    const int h = (blockIdx.x / a.n_qblk) % a.h_kv;
-    const int req = blockIdx.x / (a.n_qblk * a.h_kv);
+    // Work item: KV head outermost, then request, then query block.  Workgroup b
+    // runs on XCD b % 8; when the grid divides by 8, XCD x takes the x-th eighth
+    // of the items, so the workgroups that stream one head's K / V tiles (every
+    // request and query block of it) share one XCD's L2.
+    const int nb = gridDim.x;
+    const int bi = blockIdx.x;
+    const int bp = (nb & 7) == 0 ? (bi & 7) * (nb >> 3) + (bi >> 3) : bi;
+    const int qb = bp % a.n_qblk;
+    const int req = (bp / a.n_qblk) % a.n_req;
+    const int h = bp / (a.n_qblk * a.n_req);
     const int tok_wg = qb * WAVES * TW;
     const int q_len = a.q_len, kv_len = a.kv_len;
     int agent = a.req_agent[req];
@@ -240,12 +256,15 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
                    voff_l + 16 * wave);
         }
         if constexpr (ROPE) {
-            const auto rc = make_rsrc(a.rope_cos + (size_t)key0 * (D / 2), rem * RB);
-            const auto rs = make_rsrc(a.rope_sin + (size_t)key0 * (D / 2), rem * RB);
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                dma_1k(rc, smem_lds + OFF_CS + (2 * b) * TK + (wave + WAVES * u) * KBS, voff_row[u]);
-                dma_1k(rs, smem_lds + OFF_CS + (2 * b + 1) * TK + (wave + WAVES * u) * KBS, voff_row[u]);
+            // The cos / sin rows of the tile's first key.  Lanes 0 .. CPR-1 of the K
+            // offsets voff_row[0] read row `wave` of a resource, so the resource
+            // starts `wave` rows before row key0 (only the first RB bytes of each
+            // 1 KB block are used).
+            if (wave >= WAVES - 2) {
+                const float* tab = wave == WAVES - 2 ? a.rope_cos : a.rope_sin;
+                const uintptr_t base = (uintptr_t)(tab + (size_t)key0 * (D / 2)) - (uintptr_t)wave * RB;
+                dma_1k(make_rsrc((const void*)base, (rem + wave) * RB),
+                       smem_lds + OFF_CB + b * 2048 + (wave - (WAVES - 2)) * 1024, voff_row[0]);
             }
         }
     };
@@ -277,7 +296,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         *(bf16x8*)(smem + OFF_LV + b * TLV + c * VBS + (e % KT) * 16) = v;
     }
     if constexpr (NLK > RCH) {
-        for (int e = tid; e < 2 * (NLK - RCH) * KT; e += 512) {
+        for (int e = tid; e < NKB * (NLK - RCH) * KT; e += 512) {
             const int b = e / ((NLK - RCH) * KT);
             const int c = RCH + (e / KT) % (NLK - RCH);
             *(bf16x8*)(smem + OFF_LK + b * TLK + c * 1024 + (e % KT) * 16) = zero8();
@@ -287,6 +306,18 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     dma_k(0, 0);
     dma_v(0, 0);
     if (n_tiles > 1) dma_k(1, 1);
+    if constexpr (ROPE) {
+        if (n_tiles > 2) dma_k(2, 2);
+        // cos / sin rows 0..63 (the angles of the key offsets inside a tile), kept for
+        // the whole kernel; rows past kv_len read as zero
+        const auto rc = make_rsrc(a.rope_cos, (uint32_t)kv_len * RB);
+        const auto rs = make_rsrc(a.rope_sin, (uint32_t)kv_len * RB);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            dma_1k(rc, smem_lds + OFF_CS + (wave + WAVES * u) * KBS, voff_row[u]);
+            dma_1k(rs, smem_lds + OFF_CS + TK + (wave + WAVES * u) * KBS, voff_row[u]);
+        }
+    }
 
     // ---- query operand (B of S^T): lane holds dims 16*ks + 8*hh .. +7 of its row
     bf16x8 qf[NKS];
@@ -324,56 +355,68 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     }
 
     // ---- RoPE key rebuild K' = K_base + rot_key(L_k B_k^(h)) of one buffer, in place.
-    // Wavefront -> key half kt, dim tile dt (paired with dt + D/64), and a part of
-    // the 8-dim groups b4.  x1/x2 = B_k^T L_k^T for dims 32dt.. and 32dt + D/2..
-    constexpr int HALF_T = D / 64;
-    const int rb_kt = wave & 1;
-    const int rb_dt = (wave >> 1) % HALF_T;
-    const int rb_part = (wave >> 1) / HALF_T;
-    bf16x8 bk1[NKR], bk2[NKR];
+    // On 16x16 MFMA tiles (16 dims x 16 keys, ranks as k, zero padded to 16 or
+    // 32): the tile's 64 keys x D/2 rotation pairs make D/8 (dim tile, key tile)
+    // items, RC = D/64 per wavefront: dim tile r_dt = wave % (D/32) (dims
+    // 16 r_dt .. and D/2 + 16 r_dt ..), key tiles RC (wave / (D/32)) + c.  The C
+    // layout gives lane l dims 16 r_dt + 4 (l/16) + v of key 16 kt + l % 16, so a
+    // lane rotates four (i, i + D/2) pairs of one key per item.
+    // The angle of key offset o of tile T is that of position 64T plus that of o:
+    //   cos = cos_b cos_o - sin_b sin_o,  sin = sin_b cos_o + cos_b sin_o,
+    // with the offset rows o = 0..63 in LDS for the whole kernel and the tile's
+    // base row 64T DMA'd beside its keys.
+    constexpr int RC = D / 64;
+    constexpr int RK = R <= 16 ? 16 : 32;
+    typedef __bf16 bfk __attribute__((ext_vector_type(RK / 4)));
+    const int r_dt = wave % (D / 32);
+    const int r_kt0 = (wave / (D / 32)) * RC;
+    const int r_i0 = 16 * r_dt + 4 * g16;  // this lane's first pair index
+    bfk rbk1, rbk2;  // B_k^T operands: dim 16 r_dt + i16 (and + D/2), ranks (RK/4) g16 ..
     if constexpr (ROPE) {
 #pragma unroll
-        for (int kr = 0; kr < NKR; ++kr)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int rk = 16 * kr + 8 * hh + e;
-                const bool ok = rk < R;
-                const bf16* bp = bk_ag + (size_t)(ok ? rk : 0) * bcols + 32 * rb_dt + n32;
-                bk1[kr][e] = ok ? bp[0] : (bf16)0.0f;
-                bk2[kr][e] = ok ? bp[D / 2] : (bf16)0.0f;
-            }
+        for (int e = 0; e < RK / 4; ++e) {
+            const int rk = (RK / 4) * g16 + e;
+            const bool ok = rk < R;
+            const bf16* bp = bk_ag + (size_t)(ok ? rk : 0) * bcols + 16 * r_dt + i16;
+            rbk1[e] = ok ? bp[0] : (bf16)0.0f;
+            rbk2[e] = ok ? bp[D / 2] : (bf16)0.0f;
+        }
     }
-    auto rebuild = [&](int T, int b) {
-        const int key_l = 32 * rb_kt + n32;
-        f32x16 x1 = {}, x2 = {};
-#pragma unroll
-        for (int kr = 0; kr < NKR; ++kr) {
-            const bf16x8 lb = *(const bf16x8*)(smem + OFF_LK + b * TLK + (2 * kr + hh) * 1024 + key_l * 16);
-            x1 = mfma32x32x16(bk1[kr], lb, x1);
-            x2 = mfma32x32x16(bk2[kr], lb, x2);
+    auto rebuild_item = [&](int b, int c) {
+        const int key_l = 16 * (r_kt0 + c) + i16;
+        const char* lrow = smem + OFF_LK + b * TLK + key_l * 16;
+        f32x4 x1, x2;
+        if constexpr (RK == 16) {
+            const bf16x4 lb = *(const bf16x4*)(lrow + (g16 >> 1) * 1024 + (g16 & 1) * 8);
+            x1 = mfma16x16x16(rbk1, lb, zf4());
+            x2 = mfma16x16x16(rbk2, lb, zf4());
+        } else {
+            const bf16x8 lb = *(const bf16x8*)(lrow + g16 * 1024);
+            x1 = mfma16x16x32(rbk1, lb, zf4());
+            x2 = mfma16x16x32(rbk2, lb, zf4());
         }
         char* krow = smem + OFF_K + b * TK + (key_l % NI) * KBS + (key_l / NI) * RB;
-        const char* crow = smem + OFF_CS + (2 * b) * TK + (key_l % NI) * KBS + (key_l / NI) * RB;
-        const char* srow = crow + TK;
+        const char* crow = smem + OFF_CS + (key_l % NI) * KBS + (key_l / NI) * RB;
+        const f32x4 co = *(const f32x4*)(crow + 4 * r_i0);
+        const f32x4 so = *(const f32x4*)(crow + TK + 4 * r_i0);
+        const f32x4 cb = *(const f32x4*)(smem + OFF_CB + b * 2048 + 4 * r_i0);
+        const f32x4 sb = *(const f32x4*)(smem + OFF_CB + b * 2048 + 1024 + 4 * r_i0);
+        const f32x4 cs = cb * co - sb * so;
+        const f32x4 sn = sb * co + cb * so;
+        bf16x4* r1 = (bf16x4*)(krow + 2 * r_i0);
+        bf16x4* r2 = (bf16x4*)(krow + 2 * (r_i0 + D / 2));
+        bf16x4 k1 = *r1, k2 = *r2;
 #pragma unroll
-        for (int j = 0; j < HALF_T; ++j) {
-            const int b4 = rb_part * HALF_T + j;
-            const int i0 = 32 * rb_dt + 8 * b4 + 4 * hh;
-            const f32x4 cs = *(const f32x4*)(crow + 4 * i0);
-            const f32x4 sn = *(const f32x4*)(srow + 4 * i0);
-            bf16x4* r1 = (bf16x4*)(krow + 2 * i0);
-            bf16x4* r2 = (bf16x4*)(krow + 2 * (i0 + D / 2));
-            bf16x4 k1 = *r1, k2 = *r2;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float u1 = x1[4 * b4 + c], u2 = x2[4 * b4 + c];
-                k1[c] = (bf16)((float)k1[c] + (u1 * cs[c] - u2 * sn[c]));
-                k2[c] = (bf16)((float)k2[c] + (u2 * cs[c] + u1 * sn[c]));
-            }
-            *r1 = k1;
-            *r2 = k2;
+        for (int v = 0; v < 4; ++v) {
+            k1[v] = (bf16)((float)k1[v] + (x1[v] * cs[v] - x2[v] * sn[v]));
+            k2[v] = (bf16)((float)k2[v] + (x2[v] * cs[v] + x1[v] * sn[v]));
         }
-        (void)T;
+        *r1 = k1;
+        *r2 = k2;
+    };
+    auto rebuild = [&](int b) {
+#pragma unroll
+        for (int c = 0; c < RC; ++c) rebuild_item(b, c);
     };
 
     // ---- per-lane LDS operand bases (all further offsets are immediates)
@@ -457,7 +500,9 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     wait_dma();
     __syncthreads();
     if constexpr (ROPE) {
-        rebuild(0, 0);
+        // K'(0), K'(1) rebuilt; K(2) is in its buffer already
+        rebuild(0);
+        if (n_tiles > 1) rebuild(1);
         __syncthreads();
     }
     f32x16 sA[2], sB[2];
@@ -468,7 +513,7 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     // the final division, and bf16 / fp32 hold that range.  The floor keeps rows
     // past q_len (Q = 0, everything masked) free of inf - inf.
     float m_run = __builtin_fmaxf(tile_max(sA), -1e30f);
-    __syncthreads();  // every S(0) read done before K(2) lands in buffer 0
+    __syncthreads();  // every S(0) read done before the next key tile lands in buffer 0
 
     // instruction counts of the two overlapped phases (scheduling hints only)
     constexpr int NS_MFMA = 2 * NKS + (ROPE || PLAIN ? 0 : 2 * NKR);
@@ -482,24 +527,32 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         for (int e = 0; e < 8; ++e)
             pb[ks][e] = (bf16)fast_exp2(__builtin_fmaf(sc[ks >> 1][8 * (ks & 1) + e], sl2, -m_run));
     };
-    auto phase1 = [&](int kb, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pb)[4], auto n_exp_c) {
+    // extra work placed into the phases (RoPE: one key-rebuild item each): its
+    // MFMAs join the MFMA slots of the scheduling hints; its VALU ops are left to
+    // the scheduler (pinning them to MFMA slots measured no faster)
+    constexpr int XM1 = ROPE ? 2 : 0, XV1 = 0;
+    constexpr int XM2 = ROPE && RC > 1 ? 2 : 0, XV2 = 0;
+    auto phase1 = [&](int kb, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pb)[4], auto n_exp_c,
+                      auto&& extra) {
         constexpr int n_exp = decltype(n_exp_c)::value;
         s_tile(kb, sn);
+        extra();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             if (ks < n_exp) exp_p(sc, pb, ks);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
 #pragma unroll
-        for (int i = 0; i < NS_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, 2 * n_exp - 1, 0);  // VALU / transcendental
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               // DS read
+        for (int i = 0; i < NS_MFMA + XM1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 2 * n_exp - 1 + XV1, 0);  // VALU / transcendental
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     // DS read
         }
     };
     // phase 2 of tile t: O += P(t) V(t) from V buffer vb on the matrix cores
     // (exp of keys 16*n_done.. first), row max of S(t+1) on the VALU, then the
     // lazy rescale
-    auto phase2 = [&](int t, int vb, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pb)[4], auto n_done_c) {
+    auto phase2 = [&](int t, int vb, const f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pb)[4], auto n_done_c,
+                      auto&& extra) {
         constexpr int n_done = decltype(n_done_c)::value;
         const bool nxt = t + 1 < n_tiles;
         if (nxt && !full_tile(t + 1)) mask_tile(t + 1, sn);
@@ -507,16 +560,17 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
         for (int ks = 0; ks < 4; ++ks)
             if (ks >= n_done) exp_p(sc, pb, ks);
         pv_tile(vb, pb);
+        extra();
         const float mx = tile_max(sn);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < NP_MFMA / 2; ++i) {
+        for (int i = 0; i < (NP_MFMA + XM2) / 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x402, n_done < 4 ? 4 : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, (n_done < 4 ? 4 : 1) + XV2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
 #pragma unroll
-        for (int i = NP_MFMA / 2; i < NP_MFMA; ++i) {
+        for (int i = (NP_MFMA + XM2) / 2; i < NP_MFMA + XM2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -533,16 +587,15 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
     };
 
     using I2 = std::integral_constant<int, 2>;
-    using I4 = std::integral_constant<int, 4>;
     bf16x8 pb[4];
     if constexpr (!ROPE) {
         // one tile per barrier interval: K(t+2) and V(t+1) land while tile t runs
         auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
             if (t + 2 < n_tiles) dma_k(t + 2, B);
             if (t + 1 < n_tiles) dma_v(t + 1, B ^ 1);
-            phase1(B ^ 1, sc, sn, pb, I2{});
+            phase1(B ^ 1, sc, sn, pb, I2{}, [] {});
             asm volatile("" ::"v"(pb[0]), "v"(pb[1]));  // keys 0..31 of P(t) complete here
-            phase2(t, B, sc, sn, pb, I2{});
+            phase2(t, B, sc, sn, pb, I2{}, [] {});
             wait_dma();
             __syncthreads();
         };
@@ -551,52 +604,35 @@ __global__ __launch_bounds__(512) void lra_prefill_bf16_kernel(PrefillK a) {
             if (t + 1 < n_tiles) step(t + 1, 1, sB, sA);
         }
     } else {
-        // RoPE: the key tile has to be rebuilt (K' = K + rot(L_k B_k)) between its
-        // arrival and its score MFMAs.  Step t runs
-        //   A: O += P(t-1) V(t-1) on the matrix cores, with the row max of S(t)
-        //      and the rebuild of K'(t+1) on the VALU;  barrier;
-        //   B: S(t+1) from K'(t+1) on the matrix cores, P(t) on the VALU.
-        // Step t loads K(t+2) (with its L_k rows and cos / sin tiles) and V(t).
-        // step 0: no P V yet
-        if (n_tiles > 2) dma_k(2, 0);
-        rebuild(1, 1);  // a stale buffer when n_tiles == 1: never read
-        __syncthreads();
-        phase1(1, sA, sB, pb, I4{});
-        wait_dma();
-        __syncthreads();
+        // RoPE: key tiles go through a ring of three buffers.  Step t issues the
+        // DMA of raw K(t+3) (into the buffer K'(t) held) and V(t+1), computes
+        // S(t+1) from K'(t+1) on the matrix cores with P(t) on the VALU, then
+        // P(t) V(t), and rebuilds K'(t+2) = K(t+2) + rot(L_k B_k) in place (raw
+        // K(t+2) landed in step t-1) in the shadow of those MFMAs; one barrier per
+        // step, as without RoPE.  The ring index is a run-time, wave-uniform value.
+        int kb0 = 0;  // t % 3
         auto step = [&](int t, int B, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-            if (t + 2 < n_tiles) dma_k(t + 2, B);
-            dma_v(t, B);
-            if (!full_tile(t)) mask_tile(t, sc);
-            pv_tile(B ^ 1, pb);
-            const float mx = tile_max(sc);
-            rebuild(t + 1, B ^ 1);  // a stale buffer on the last tile: never read
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < NP_MFMA + 2 * NKR; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
-                const float m_new = __builtin_fmaxf(m_run, mx);
-                const float alpha = fast_exp2(m_run - m_new);
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) acc_o[dt] *= alpha;
-#pragma unroll
-                for (int lt = 0; lt < NLT; ++lt) acc_lr[lt] *= alpha;
-                m_run = m_new;
-            }
-            __syncthreads();
-            phase1(B ^ 1, sc, sn, pb, I4{});
+            int k0 = kb0;
+            asm volatile("" : "+s"(k0));  // opaque: one address per buffer use, no per-buffer copies
+            const int k1 = k0 == 2 ? 0 : k0 + 1;
+            const int k2 = k1 == 2 ? 0 : k1 + 1;
+            if (t + 3 < n_tiles) dma_k(t + 3, k0);
+            if (t + 1 < n_tiles) dma_v(t + 1, B ^ 1);
+            // the rebuild of K'(t+2) is interleaved with the score and value MFMAs
+            // (a tile past the end rebuilds a stale buffer that is never read)
+            phase1(k1, sc, sn, pb, I2{}, [&] { rebuild_item(k2, 0); });
+            asm volatile("" ::"v"(pb[0]), "v"(pb[1]));  // keys 0..31 of P(t) complete here
+            phase2(t, B, sc, sn, pb, I2{}, [&] {
+                if constexpr (RC > 1) rebuild_item(k2, 1);
+            });
             wait_dma();
             __syncthreads();
+            kb0 = k1;
         };
-        for (int t = 1; t < n_tiles; t += 2) {
-            step(t, 1, sB, sA);
-            if (t + 1 < n_tiles) step(t + 1, 0, sA, sB);
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(t, 0, sA, sB);
+            if (t + 1 < n_tiles) step(t + 1, 1, sB, sA);
         }
-        pv_tile((n_tiles - 1) & 1, pb);
     }
 
     // ---- epilogue: l from the ones row; O^T += B_v^T O_lr^T; divide; store
