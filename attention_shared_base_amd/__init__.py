@@ -16,7 +16,8 @@ import os
 __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
-    "prefill_paged", "prefill_paged_workspace_size", "cache_append", "decode_noalloc",
+    "prefill_paged", "prefill_paged_staged", "prefill_paged_staged_workspace_size",
+    "cache_append", "decode_noalloc",
     "naive_prefill", "naive_prefill_workspace_size",
 ]
 
@@ -24,12 +25,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "liblra_attn.so")
 
 LRA_F32, LRA_BF16 = 0, 1
+ABI_VERSION = 5  # LRA_ABI_VERSION of include/lra_attn.h
 
 EXPORTED_SYMBOLS = (
     "lra_abi_version", "lra_status_str", "lra_last_error", "lra_attn_decode_workspace_size",
     "lra_attn_decode", "lra_attn_prefill", "lra_lr_cache_build",
     "lra_lr_cache_build_workspace_size", "lra_rope_table_build",
-    "lra_naive_expand_pages", "lra_attn_prefill_paged_workspace_size", "lra_attn_prefill_paged",
+    "lra_naive_expand_pages", "lra_attn_prefill_paged", "lra_attn_prefill_paged_staged_workspace_size",
+    "lra_attn_prefill_paged_staged",
     "lra_cache_append", "lra_attn_decode_noalloc", "lra_naive_prefill_workspace_size",
     "lra_naive_prefill",
 )
@@ -65,6 +68,9 @@ def load():
     lib = ctypes.CDLL(lib_path)
     lib.lra_abi_version.restype = I32
     lib.lra_abi_version.argtypes = []
+    if lib.lra_abi_version() != ABI_VERSION:
+        raise ImportError(f"{lib_path} has ABI {lib.lra_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}: rebuild it")
     lib.lra_status_str.restype = ctypes.c_char_p
     lib.lra_status_str.argtypes = [I32]
     lib.lra_last_error.restype = ctypes.c_char_p
@@ -89,10 +95,14 @@ def load():
     lib.lra_lr_cache_build_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.lra_rope_table_build.restype = I32
     lib.lra_rope_table_build.argtypes = [ctypes.c_double, I32, I32, P, P, P]
-    lib.lra_attn_prefill_paged_workspace_size.restype = ctypes.c_size_t
-    lib.lra_attn_prefill_paged_workspace_size.argtypes = [ctypes.POINTER(Dims), I32]
     lib.lra_attn_prefill_paged.restype = I32
     lib.lra_attn_prefill_paged.argtypes = [
+        ctypes.POINTER(Dims), P, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, P, I32, P, P,
+        I32, P, P]
+    lib.lra_attn_prefill_paged_staged_workspace_size.restype = ctypes.c_size_t
+    lib.lra_attn_prefill_paged_staged_workspace_size.argtypes = [ctypes.POINTER(Dims), I32]
+    lib.lra_attn_prefill_paged_staged.restype = I32
+    lib.lra_attn_prefill_paged_staged.argtypes = [
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, P, I32, P, P,
         I32, P, P, ctypes.c_size_t, P]
     lib.lra_cache_append.restype = I32
@@ -418,24 +428,15 @@ def naive_decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, 
                   out=sc["out"], workspace=sc["ws"], softmax_scale=softmax_scale, stream=stream)
 
 
-def prefill_paged_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, kv_len):
-    """Bytes of workspace ``prefill_paged`` needs for a context of ``kv_len`` tokens (bf16)."""
-    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, LRA_BF16, 0.0)
-    return int(load().lra_attn_prefill_paged_workspace_size(ctypes.byref(dims), kv_len))
-
-
-def prefill_paged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len, b_k,
-                  b_v, *, rope_cos=None, rope_sin=None, out=None, workspace=None,
-                  softmax_scale=0.0, stream=None):
-    """Chunked prefill over one context in the paged pools (``lra_attn_prefill_paged``):
-    q [n_req, q_len, H_q, d]; pools as in ``decode``; block_table_row [max_blocks] int32;
-    ``workspace`` (uint8) is allocated when not given."""
+def _paged_prefill_args(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len,
+                        b_k, b_v, rope_cos, rope_sin, softmax_scale):
     import torch
-    lib = load()
     n_req, q_len, h_q, d = q.shape
-    n_pages, h_kv = k_pool.shape[:2]
-    r = lk_pool.shape[2]
+    n_pages, h_kv, d8, page, eight = k_pool.shape
+    _need(d8 * 8 == d and eight == 8 and page == 16, "k_pool must be [n_pages, H_kv, d/8, 16, 8]")
+    r = lk_pool.shape[-1]
     n_agents = b_k.shape[0]
+    per_agent = lk_pool.dim() == 4
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
                     ("lv_pool", lv_pool), ("b_k", b_k), ("b_v", b_v)):
@@ -444,19 +445,66 @@ def prefill_paged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_ro
     for name, t in (("req_agent", req_agent), ("block_table_row", block_table_row)):
         _contig(name, t)
         _need(t.dtype == torch.int32, f"{name} must be int32")
+    _need(tuple(v_pool.shape) == (n_pages, h_kv, d, page), "v_pool must be [n_pages, H_kv, d, 16]")
+    lead = (n_agents,) if per_agent else ()
+    _need(tuple(lk_pool.shape) == lead + (n_pages, page, r), "lk_pool must be [(n_agents,) n_pages, 16, r]")
+    _need(tuple(lv_pool.shape) == lead + (n_pages, r, page), "lv_pool must be [(n_agents,) n_pages, r, 16]")
+    _need(req_agent.numel() == n_req, "req_agent must hold n_req entries")
     if rope_cos is not None:
         for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
             _contig(name, t)
             _need(t.dtype == torch.float32 and t.shape[0] >= kv_len and t.shape[1] == d // 2,
                   f"{name} must be fp32 [>=kv_len, d/2]")
-    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale)
-    need = int(lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dims), kv_len))
+    dims = _dims(h_q, h_kv, d, r, dt, softmax_scale, n_pages * page * r if per_agent else 0)
+    return dims, (n_req, q_len, n_pages, n_agents)
+
+
+def prefill_paged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len, b_k,
+                  b_v, *, rope_cos=None, rope_sin=None, out=None, softmax_scale=0.0, stream=None):
+    """Chunked prefill over one context read in place from the paged pools
+    (``lra_attn_prefill_paged``): q [n_req, q_len, H_q, d]; pools as in ``decode`` (LR
+    pools [n_pages, 16, r] / [n_pages, r, 16], or with a leading n_agents dimension for
+    one LR cache per agent); block_table_row [max_blocks] int32.  No workspace."""
+    import torch
+    lib = load()
+    dims, (n_req, q_len, n_pages, n_agents) = _paged_prefill_args(
+        q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len, b_k, b_v,
+        rope_cos, rope_sin, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _contig("out", out)
+    _check(lib.lra_attn_prefill_paged(
+        ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_pool), _ptr(v_pool),
+        _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _ptr(block_table_row),
+        block_table_row.shape[0], kv_len, _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
+        _ptr(rope_sin), _rows(rope_cos), _ptr(out), _stream(q, stream)))
+    return out
+
+
+def prefill_paged_staged_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, kv_len):
+    """Bytes of workspace ``prefill_paged_staged`` needs for a context of ``kv_len`` tokens."""
+    dims = _dims(n_q_heads, n_kv_heads, head_dim, rank, LRA_BF16, 0.0)
+    return int(load().lra_attn_prefill_paged_staged_workspace_size(ctypes.byref(dims), kv_len))
+
+
+def prefill_paged_staged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len,
+                         b_k, b_v, *, rope_cos=None, rope_sin=None, out=None, workspace=None,
+                         softmax_scale=0.0, stream=None):
+    """The paged prefill through a contiguous staging copy (``lra_attn_prefill_paged_staged``);
+    arguments as in ``prefill_paged`` (shared LR pools only); ``workspace`` (uint8) is
+    allocated when not given."""
+    import torch
+    lib = load()
+    dims, (n_req, q_len, n_pages, n_agents) = _paged_prefill_args(
+        q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table_row, kv_len, b_k, b_v,
+        rope_cos, rope_sin, softmax_scale)
+    need = int(lib.lra_attn_prefill_paged_staged_workspace_size(ctypes.byref(dims), kv_len))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty_like(q)
     _contig("out", out)
-    _check(lib.lra_attn_prefill_paged(
+    _check(lib.lra_attn_prefill_paged_staged(
         ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_pool), _ptr(v_pool),
         _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _ptr(block_table_row),
         block_table_row.shape[0], kv_len, _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),

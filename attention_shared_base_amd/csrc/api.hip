@@ -416,24 +416,91 @@ lra_status lra_attn_prefill(const lra_dims* dims, const void* q, int32_t n_req, 
     return lra::launch_prefill_bf16(a, (hipStream_t)stream);
 }
 
-size_t lra_attn_prefill_paged_workspace_size(const lra_dims* dims, int32_t kv_len) {
-    if (check_dims(dims) != LRA_OK || dims->dtype != LRA_BF16 || kv_len < 0) return 0;
-    return lra::prefill_paged_workspace(dims->n_kv_heads, dims->head_dim, dims->rank, kv_len);
-}
-
 lra_status lra_attn_prefill_paged(const lra_dims* dims, const void* q, int32_t n_req, int32_t q_len,
                                   const int32_t* req_agent, const void* k_pool, const void* v_pool,
                                   const void* lk_pool, const void* lv_pool, int32_t n_pages,
                                   int32_t page_size, const int32_t* block_table, int32_t max_blocks,
                                   int32_t kv_len, const void* b_k, const void* b_v, int32_t n_agents,
                                   const float* rope_cos, const float* rope_sin, int32_t rope_rows,
-                                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                                  void* out, void* stream) {
+    g_err[0] = 0;
+    lra_status st = check_dims(dims);
+    if (st != LRA_OK) return st;
+    if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "paged prefill: bf16 only");
+    if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+    if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
+    if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
+    if (q_len < 1) return fail(LRA_ERR_BAD_SHAPE, "q_len %d < 1", q_len);
+    if (kv_len < q_len) return fail(LRA_ERR_BAD_SHAPE, "kv_len %d < q_len %d", kv_len, q_len);
+    if (max_blocks < 1 || (long long)max_blocks * page_size < kv_len)
+        return fail(LRA_ERR_BAD_SHAPE, "max_blocks %d cannot hold kv_len %d", max_blocks, kv_len);
+    if (n_agents < 1) return fail(LRA_ERR_BAD_SHAPE, "n_agents %d < 1", n_agents);
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return fail(LRA_ERR_NULL_PTR, "rope_cos and rope_sin must both be given or both NULL");
+    if (dims->lr_agent_stride > 0 && dims->lr_agent_stride < (long long)n_pages * page_size * dims->rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < one agent's LR pool (n_pages*page_size*r = %lld)",
+                    (long long)dims->lr_agent_stride, (long long)n_pages * page_size * dims->rank);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(req_agent);
+    REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool);
+    REQUIRE_PTR(lk_pool);
+    REQUIRE_PTR(lv_pool);
+    REQUIRE_PTR(block_table);
+    REQUIRE_PTR(b_k);
+    REQUIRE_PTR(b_v);
+    REQUIRE_PTR(out);
+    if (rope_cos) {
+        if (rope_rows < kv_len)
+            return fail(LRA_ERR_BAD_SHAPE, "rope tables hold %d rows < kv_len %d", rope_rows, kv_len);
+    }
+    lra::PrefillArgs a;
+    a.q = q;
+    a.req_agent = req_agent;
+    a.k_base = k_pool;
+    a.v_base = v_pool;
+    a.l_k = lk_pool;
+    a.l_v = lv_pool;
+    a.b_k = b_k;
+    a.b_v = b_v;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.out = out;
+    a.lr_stride = dims->lr_agent_stride;
+    a.n_req = n_req;
+    a.q_len = q_len;
+    a.kv_len = kv_len;
+    a.n_agents = n_agents;
+    a.h_q = dims->n_q_heads;
+    a.h_kv = dims->n_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.rank = dims->rank;
+    a.scale = eff_scale(dims);
+    a.block_table = block_table;
+    a.max_blocks = max_blocks;
+    a.n_pages = n_pages;
+    if (n_req == 0) return LRA_OK;
+    return lra::launch_prefill_bf16(a, (hipStream_t)stream);
+}
+
+size_t lra_attn_prefill_paged_staged_workspace_size(const lra_dims* dims, int32_t kv_len) {
+    if (check_dims(dims) != LRA_OK || dims->dtype != LRA_BF16 || kv_len < 0) return 0;
+    return lra::prefill_paged_workspace(dims->n_kv_heads, dims->head_dim, dims->rank, kv_len);
+}
+
+lra_status lra_attn_prefill_paged_staged(const lra_dims* dims, const void* q, int32_t n_req, int32_t q_len,
+                                         const int32_t* req_agent, const void* k_pool, const void* v_pool,
+                                         const void* lk_pool, const void* lv_pool, int32_t n_pages,
+                                         int32_t page_size, const int32_t* block_table, int32_t max_blocks,
+                                         int32_t kv_len, const void* b_k, const void* b_v, int32_t n_agents,
+                                         const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
     if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "paged prefill: bf16 only");
     if (dims->lr_agent_stride != 0)
-        return fail(LRA_ERR_UNSUPPORTED, "paged prefill: shared LR cache only (lr_agent_stride 0)");
+        return fail(LRA_ERR_UNSUPPORTED, "staged paged prefill: shared LR cache only (lr_agent_stride 0)");
     if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
     if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
     if (q_len < 1) return fail(LRA_ERR_BAD_SHAPE, "q_len %d < 1", q_len);

@@ -82,6 +82,10 @@ struct PrefillArgs {
     // unused) over per-request caches kv_req_stride elements apart
     bool plain = false;
     int64_t kv_req_stride = 0;
+    // paged mode: k_base / v_base / l_k / l_v are the page pools of lra_attn_decode
+    // (page_size 16), read through one context's block table
+    const int32_t* block_table = nullptr;  // non-NULL selects the paged mode
+    int32_t max_blocks = 0, n_pages = 0;
 };
 
 lra_status launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);

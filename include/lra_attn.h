@@ -63,7 +63,7 @@ typedef int32_t lra_status;
 #define LRA_F32 0
 #define LRA_BF16 1
 
-#define LRA_ABI_VERSION 4
+#define LRA_ABI_VERSION 5
 
 typedef struct lra_dims {
     int32_t n_q_heads;   /* H_q */
@@ -77,7 +77,8 @@ typedef struct lra_dims {
      * §3, PReCache): agent a's L_k / L_v start lr_agent_stride elements after
      * agent a-1's, in l_k / l_v of lra_attn_prefill and lk_pool / lv_pool of
      * lra_attn_decode (which then packs at most 4 requests per row group and
-     * does not combine it with RoPE).  The paged prefill, the cache append and
+     * does not combine it with RoPE) and lk_pool / lv_pool of
+     * lra_attn_prefill_paged.  The staged paged prefill, the cache append and
      * the naive baseline take 0 only. */
     int64_t lr_agent_stride;
 } lra_dims;
@@ -250,16 +251,20 @@ lra_status lra_attn_prefill(const lra_dims* dims,
  * with k_base/v_base/l_k/l_v taken from the pages: logical token t is in page
  * block_table[t / page_size], slot t % page_size (the q_len new tokens are the
  * last q_len of the kv_len tokens, already appended with lra_cache_append).
- * The context's keys, values and LR rows are first staged contiguously in the
- * workspace (the prefill streams them from there), then attended as in
- * lra_attn_prefill.
+ * The pages are read in place (no staging, no workspace); the output equals
+ * that of lra_attn_prefill over the same tokens laid out contiguously, bit
+ * for bit.
  *   block_table  [max_blocks] int32, this context's row   device
- *   workspace    >= lra_attn_prefill_paged_workspace_size(dims, kv_len) bytes,
- *                device, caller-owned; no state is kept between calls
+ *                entries past ceil(kv_len / page_size) are not read; ids
+ *                outside [0, n_pages) are clamped so reads stay in bounds
+ *                (the result is then unspecified)
+ *   lk_pool,
+ *   lv_pool      with dims->lr_agent_stride > 0: n_agents pools
+ *                lr_agent_stride >= n_pages * page_size * r elements apart
+ *                (else LRA_ERR_BAD_SHAPE); request i reads req_agent[i]'s
  * Other arguments and layouts as in lra_attn_decode / lra_attn_prefill.
  * bf16 only.
  */
-size_t lra_attn_prefill_paged_workspace_size(const lra_dims* dims, int32_t kv_len);
 lra_status lra_attn_prefill_paged(const lra_dims* dims,
                                   const void* q, int32_t n_req, int32_t q_len,
                                   const int32_t* req_agent,
@@ -270,8 +275,30 @@ lra_status lra_attn_prefill_paged(const lra_dims* dims,
                                   int32_t kv_len,
                                   const void* b_k, const void* b_v, int32_t n_agents,
                                   const float* rope_cos, const float* rope_sin, int32_t rope_rows,
-                                  void* out, void* workspace, size_t workspace_bytes,
-                                  void* stream);
+                                  void* out, void* stream);
+/*
+ * The same prefill through a contiguous copy: the context's keys, values and
+ * LR rows are first gathered from the pages into the workspace, then attended
+ * as in lra_attn_prefill.  Kept as a fallback and as a cross-check of the
+ * direct path (identical output); costs an extra read and write of the
+ * context and 2*H_kv*kv_len*d*2 + 2*kv_len*r*2 bytes of workspace.
+ *   workspace    >= lra_attn_prefill_paged_staged_workspace_size(dims, kv_len)
+ *                bytes, device, caller-owned; no state is kept between calls
+ * Shared LR cache only (dims->lr_agent_stride == 0).  bf16 only.
+ */
+size_t lra_attn_prefill_paged_staged_workspace_size(const lra_dims* dims, int32_t kv_len);
+lra_status lra_attn_prefill_paged_staged(const lra_dims* dims,
+                                         const void* q, int32_t n_req, int32_t q_len,
+                                         const int32_t* req_agent,
+                                         const void* k_pool, const void* v_pool,
+                                         const void* lk_pool, const void* lv_pool,
+                                         int32_t n_pages, int32_t page_size,
+                                         const int32_t* block_table, int32_t max_blocks,
+                                         int32_t kv_len,
+                                         const void* b_k, const void* b_v, int32_t n_agents,
+                                         const float* rope_cos, const float* rope_sin,
+                                         int32_t rope_rows, void* out, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 /*
  * Append new tokens to the paged pools (the decode-time and prefill-time write
  * of the base K/V rows and the shared LR rows; LRAgent §3 BaseLRShared: one LR

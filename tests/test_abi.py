@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = lra.load()
-    assert lra.abi_version() == 4
+    assert lra.abi_version() == 5
     for s in range(7):
         assert lib.lra_status_str(s).decode().startswith("LRA_")
     assert b"unknown" in lib.lra_status_str(99)
@@ -43,8 +43,8 @@ def test_version_and_status_strings():
 A = ctypes.c_void_p(0x100000)
 
 
-def dims(h_q=32, h_kv=8, d=128, r=16, dt=1, scale=0.0):
-    return lra.Dims(h_q, h_kv, d, r, dt, scale)
+def dims(h_q=32, h_kv=8, d=128, r=16, dt=1, scale=0.0, stride=0):
+    return lra.Dims(h_q, h_kv, d, r, dt, scale, stride)
 
 
 def call_decode(dm, **over):
@@ -230,28 +230,44 @@ def test_naive_expand_validation(dm, over, want):
 def test_paged_prefill_and_append_validation():
     lib = lra.load()
     dm = dims()
-    # workspace size grows with kv_len and is 0 for an invalid dims
-    assert lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dm), 1000) > \
-        lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dm), 10) > 0
-    assert lib.lra_attn_prefill_paged_workspace_size(ctypes.byref(dims(dt=0)), 10) == 0
+    # the staged path's workspace grows with kv_len and is 0 for an invalid dims
+    assert lib.lra_attn_prefill_paged_staged_workspace_size(ctypes.byref(dm), 1000) > \
+        lib.lra_attn_prefill_paged_staged_workspace_size(ctypes.byref(dm), 10) > 0
+    assert lib.lra_attn_prefill_paged_staged_workspace_size(ctypes.byref(dims(dt=0)), 10) == 0
 
-    def pp(**o):
-        a = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, lk=A, lv=A, n_pages=64, page=16, bt=A,
-                 max_blocks=16, kv_len=256, bk=A, bv=A, n_agents=2, cos=None, sin=None, rows=256,
-                 out=A, ws=A, ws_bytes=1 << 30)
-        a.update(o)
+    base = dict(q=A, n_req=2, q_len=16, agent=A, k=A, v=A, lk=A, lv=A, n_pages=64, page=16, bt=A,
+                max_blocks=16, kv_len=256, bk=A, bv=A, n_agents=2, cos=None, sin=None, rows=256,
+                out=A, ws=A, ws_bytes=1 << 30)
+
+    def pp(**o):  # direct: reads the pages in place, no workspace
+        a = dict(base, **o)
         return lib.lra_attn_prefill_paged(ctypes.byref(o.pop("dm", dm)), a["q"], a["n_req"], a["q_len"],
                                           a["agent"], a["k"], a["v"], a["lk"], a["lv"], a["n_pages"],
                                           a["page"], a["bt"], a["max_blocks"], a["kv_len"], a["bk"],
                                           a["bv"], a["n_agents"], a["cos"], a["sin"], a["rows"],
-                                          a["out"], a["ws"], a["ws_bytes"], None)
-    assert pp(max_blocks=15) == 2            # 15 blocks cannot hold 256 tokens
-    assert pp(ws_bytes=1) == 5
-    assert pp(ws=None) == 1
-    assert pp(kv_len=8) == 2                  # kv_len < q_len
-    assert pp(page=32) == 3
-    assert pp(cos=A) == 1
-    assert pp(cos=A, sin=A, rows=255) == 2    # RoPE tables shorter than kv_len
+                                          a["out"], None)
+
+    def ps(**o):  # staged through a contiguous copy
+        a = dict(base, **o)
+        return lib.lra_attn_prefill_paged_staged(
+            ctypes.byref(o.pop("dm", dm)), a["q"], a["n_req"], a["q_len"], a["agent"], a["k"], a["v"],
+            a["lk"], a["lv"], a["n_pages"], a["page"], a["bt"], a["max_blocks"], a["kv_len"], a["bk"],
+            a["bv"], a["n_agents"], a["cos"], a["sin"], a["rows"], a["out"], a["ws"], a["ws_bytes"], None)
+    for f in (pp, ps):
+        assert f(max_blocks=15) == 2            # 15 blocks cannot hold 256 tokens
+        assert f(kv_len=8) == 2                  # kv_len < q_len
+        assert f(page=32) == 3
+        assert f(cos=A) == 1
+        assert f(cos=A, sin=A, rows=255) == 2    # RoPE tables shorter than kv_len
+        assert f(bt=None) == 1
+        assert f(n_pages=0) == 2
+        assert f(dm=dims(dt=0)) == 3             # bf16 only
+    assert ps(ws_bytes=1) == 5
+    assert ps(ws=None) == 1
+    # per-agent LR pools: the direct path takes them (stride >= one agent's pool), the
+    # staged path does not
+    assert pp(dm=dims(stride=64 * 16 * 16 - 1)) == 2
+    assert ps(dm=dims(stride=64 * 16 * 16)) == 3
 
     def ap(**o):
         a = dict(n=4, slots=A, k=A, v=A, lk=A, lv=A, kp=A, vp=A, lkp=A, lvp=A, n_pages=8, page=16)

@@ -1,5 +1,6 @@
 """GPU checks of the paged serving loop: appending tokens to the page pools
-(lra_cache_append), chunked prefill over a paged context (lra_attn_prefill_paged)
+(lra_cache_append), chunked prefill over a paged context read in place
+(lra_attn_prefill_paged) or through a staging copy (lra_attn_prefill_paged_staged),
 and decode after a decode-time append, against the float64 oracle."""
 import numpy as np
 import pytest
@@ -53,29 +54,109 @@ def test_append_builds_the_page_layout(r):
         assert np.array_equal(g, ref), name
 
 
-@pytest.mark.parametrize("rope", [False, True])
-def test_prefill_paged_equals_contiguous(rope):
-    """Paged prefill = contiguous prefill over the same context (same bits), and the oracle."""
+def _paged_context(case, n_pages, seed, poison=True):
+    """The case's context in shuffled pages of device pools.  With ``poison`` every
+    slot no key of the context occupies (unused pages, the tail of the last page)
+    holds NaN, and the block-table row carries out-of-range ids past the context's
+    blocks: neither may reach the output."""
     import torch
-    import attention_shared_base_amd as lra
-    case = w.make_prefill(63, dtype="bf16", kv_len=777, q_len=100, req_agents=[1, 0], n_agents=2,
-                          h_q=32, h_kv=8, d=128, r=16, rope_theta=500000.0 if rope else None,
-                          b_sigma=0.2, name="paged prefill")
-    n_pages = 60
-    ids = np.random.default_rng(5).permutation(n_pages)[:49]
+    n_blk = (case.kv_len + 15) // 16
+    ids = np.random.default_rng(seed).permutation(n_pages)[:n_blk]
     kp, lkp = w.paginate(case.k_base, case.l_k, ids, n_pages, 16)
     vp, lvp = w.paginate(case.v_base, case.l_v, ids, n_pages, 16)
     pools = [dev(x) for x in w.decode_device_layout(kp, vp, lkp, lvp)]
-    d = PrefillDev(case)
-    table = torch.from_numpy(ids.astype(np.int32)).to("cuda")
-    got = lra.prefill_paged(d.q, d.agent, *pools, table, 777, d.b_k, d.b_v, rope_cos=d.cos,
-                            rope_sin=d.sin)
-    ref_gpu = d.run()
-    assert torch.equal(got, ref_gpu)
-    ref = oracle_prefill(case)
-    print(f"[paged prefill rope={rope}] ", end="", flush=True)
-    ma, rel = assert_parity(host(got), ref, "bf16", "paged prefill")
+    row = ids.astype(np.int32)
+    if poison:
+        k, v, lk, lv = pools
+        unused = torch.from_numpy(np.setdiff1d(np.arange(n_pages), ids)).to("cuda")
+        for t in pools:
+            t[unused] = float("nan")
+        last, tail = int(ids[-1]), case.kv_len - 16 * (n_blk - 1)
+        k[last, :, :, tail:, :] = float("nan")
+        v[last, :, :, tail:] = float("nan")
+        lk[last, tail:, :] = float("nan")
+        lv[last, :, tail:] = float("nan")
+        row = np.concatenate([row, np.array([-7, n_pages + 100, 1 << 30, -1], np.int32)])
+    return pools, torch.from_numpy(row).to("cuda")
+
+
+PAGED_CASES = [
+    # rope, h_q, h_kv, d, r, kv_len, q_len
+    (False, 32, 8, 128, 16, 777, 100),
+    (True, 32, 8, 128, 16, 777, 100),
+    (False, 8, 8, 64, 8, 640, 64),       # kv_len a multiple of the 64-key tile
+    (True, 8, 8, 64, 8, 640, 64),
+    (True, 32, 8, 128, 4, 300, 300),     # the whole context is new
+    (False, 32, 8, 128, 4, 1040, 90),    # kv_len a multiple of the page, not of the tile
+    (False, 16, 4, 128, 32, 1000, 37),
+    (True, 32, 8, 128, 32, 1000, 37),
+    (True, 32, 1, 64, 16, 33, 1),        # one token, 32 query heads per KV head
+    (True, 16, 8, 64, 32, 129, 65),
+]
+
+
+@pytest.mark.parametrize("rope,h_q,h_kv,d,r,kv_len,q_len", PAGED_CASES,
+                         ids=[f"{'rope ' if c[0] else ''}g{c[1] // c[2]} d{c[3]} r{c[4]} kv{c[5]} q{c[6]}"
+                              for c in PAGED_CASES])
+def test_prefill_paged_equals_contiguous(rope, h_q, h_kv, d, r, kv_len, q_len):
+    """Paged prefill reading the pages in place = contiguous prefill over the same context
+    (same bits), also with NaN in every slot outside the context and junk block-table
+    entries past it; the staged path gives the same bits; both match the oracle."""
+    import torch
+    import attention_shared_base_amd as lra
+    case = w.make_prefill(63 + kv_len, dtype="bf16", kv_len=kv_len, q_len=q_len, req_agents=[1, 0],
+                          n_agents=2, h_q=h_q, h_kv=h_kv, d=d, r=r,
+                          rope_theta=500000.0 if rope else None, b_sigma=0.2, name="paged prefill")
+    n_pages = (kv_len + 15) // 16 + 11
+    d_ = PrefillDev(case)
+    ref_gpu = d_.run()
+    print(f"[paged prefill rope={rope} g{h_q // h_kv} d{d} r{r} kv{kv_len} q{q_len}] ", end="", flush=True)
+    for poison in (False, True):
+        pools, table = _paged_context(case, n_pages, 5 + kv_len, poison=poison)
+        got = lra.prefill_paged(d_.q, d_.agent, *pools, table, kv_len, d_.b_k, d_.b_v,
+                                rope_cos=d_.cos, rope_sin=d_.sin)
+        assert torch.equal(got, ref_gpu), f"direct paged != contiguous (poison={poison})"
+        if not poison:  # the staged copy reads whole pages, NaN tails included
+            st = lra.prefill_paged_staged(d_.q, d_.agent, *pools, table, kv_len, d_.b_k, d_.b_v,
+                                          rope_cos=d_.cos, rope_sin=d_.sin)
+            assert torch.equal(st, ref_gpu), "staged paged != contiguous"
+    ma, rel = assert_parity(host(got), oracle_prefill(case), "bf16", "paged prefill")
     print(f"max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
+
+
+def test_prefill_paged_per_agent_lr():
+    """One LR pool per agent ([n_agents, n_pages, 16, r] / [.., r, 16]) through the same block
+    table: equals the contiguous per-agent prefill bit for bit, and the oracle."""
+    import torch
+    import attention_shared_base_amd as lra
+    n_ag, kv_len = 3, 700
+    case = w.make_prefill(91, dtype="bf16", kv_len=kv_len, q_len=90, req_agents=[2, 0, 1, 2],
+                          n_agents=n_ag, h_q=32, h_kv=8, d=128, r=16, b_sigma=0.2,
+                          name="per-agent paged prefill")
+    rng = np.random.default_rng(92)
+    lk = np.stack([w.f32_to_bf16_bits(rng.standard_normal(case.l_k.shape).astype(np.float32))
+                   for _ in range(n_ag)])
+    lv = np.stack([w.f32_to_bf16_bits(rng.standard_normal(case.l_v.shape).astype(np.float32))
+                   for _ in range(n_ag)])
+    n_pages = 50
+    ids = np.random.default_rng(93).permutation(n_pages)[:(kv_len + 15) // 16]
+    kp, _ = w.paginate(case.k_base, case.l_k, ids, n_pages, 16)
+    vp, _ = w.paginate(case.v_base, case.l_v, ids, n_pages, 16)
+    lkps, lvps = [], []
+    for a in range(n_ag):
+        _, lkp = w.paginate(case.k_base, lk[a], ids, n_pages, 16)
+        _, lvp = w.paginate(case.v_base, lv[a], ids, n_pages, 16)
+        k, v, lkd, lvd = w.decode_device_layout(kp, vp, lkp, lvp)
+        lkps.append(lkd)
+        lvps.append(lvd)
+    d_ = PrefillDev(case)
+    table = torch.from_numpy(ids.astype(np.int32)).to("cuda")
+    got = lra.prefill_paged(d_.q, d_.agent, dev(k), dev(v), dev(np.stack(lkps)), dev(np.stack(lvps)),
+                            table, kv_len, d_.b_k, d_.b_v)
+    assert torch.equal(got, d_.run(lk=dev(lk), lv=dev(lv)))
+    ma, rel = assert_parity(host(got), oracle_prefill(case, l_k=w.widen(lk), l_v=w.widen(lv)), "bf16",
+                            "per-agent paged prefill")
+    print(f"[per-agent paged prefill] max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
 
 
 def test_serving_loop_append_prefill_decode():
