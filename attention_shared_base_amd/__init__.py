@@ -106,7 +106,7 @@ def load():
         ctypes.POINTER(Dims), P, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, P, I32, P, P,
         I32, P, P, ctypes.c_size_t, P]
     lib.lra_cache_append.restype = I32
-    lib.lra_cache_append.argtypes = [ctypes.POINTER(Dims), I32, P, P, P, P, P, P, P, P, P, I32,
+    lib.lra_cache_append.argtypes = [ctypes.POINTER(Dims), I32, P, P, P, P, P, I32, P, P, P, P, I32,
                                      I32, P]
     lib.lra_naive_prefill_workspace_size.restype = ctypes.c_size_t
     lib.lra_naive_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), I32, I32]
@@ -389,9 +389,13 @@ def naive_decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, 
     lib = load()
     n_req, h_q, d = q.shape
     n_pages, h_kv = k_pool.shape[:2]
-    r = lk_pool.shape[2]
+    r = lk_pool.shape[-1]
     n_ctx, max_blocks = block_table.shape
     n_agents = b_k.shape[0]
+    per_agent = lk_pool.dim() == 4  # [n_agents, n_pages, 16, r]: one LR pool per agent
+    lead = (n_agents,) if per_agent else ()
+    _need(tuple(lk_pool.shape) == lead + (n_pages, 16, r), "lk_pool must be [(n_agents,) n_pages, 16, r]")
+    _need(tuple(lv_pool.shape) == lead + (n_pages, r, 16), "lv_pool must be [(n_agents,) n_pages, r, 16]")
     out_blocks = max(1, -(-max_ctx_len // 16))
     _need(out_blocks <= max_blocks, "max_ctx_len exceeds the block table")
     sc = scratch if scratch is not None else {}
@@ -412,7 +416,7 @@ def naive_decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, 
         sc["len"] = ctx_len.to(torch.int64)[req_ctx].to(torch.int32).contiguous()
         sc["out"] = torch.empty_like(q)
         sc["ws"] = None
-    dims = _dims(h_q, h_kv, d, r, _dtype_code(q), softmax_scale)
+    dims = _dims(h_q, h_kv, d, r, _dtype_code(q), softmax_scale, n_pages * 16 * r if per_agent else 0)
     _check(lib.lra_naive_expand_pages(
         ctypes.byref(dims), n_req, _ptr(ctx_req_start), n_ctx, _ptr(req_agent), _ptr(k_pool),
         _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _ptr(block_table), max_blocks,
@@ -516,21 +520,29 @@ def prefill_paged_staged(q, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_t
 def cache_append(slot_mapping, k_new, v_new, lk_new, lv_new, k_pool, v_pool, lk_pool, lv_pool,
                  *, n_q_heads=None, stream=None):
     """Write new tokens' K/V rows [n_tok, H_kv, d] and LR rows [n_tok, r] into the paged
-    pools at ``slot_mapping`` [n_tok] int64 (``lra_cache_append``)."""
+    pools at ``slot_mapping`` [n_tok] int64 (``lra_cache_append``).  With one LR pool per
+    agent (lk_pool [n_agents, n_pages, 16, r]) the LR rows are [n_agents, n_tok, r], set a
+    going to agent a's pools."""
     import torch
     lib = load()
     n_tok, h_kv, d = k_new.shape
-    r = lk_new.shape[1]
+    r = lk_new.shape[-1]
     n_pages = k_pool.shape[0]
+    per_agent = lk_pool.dim() == 4
+    n_lr = lk_pool.shape[0] if per_agent else 1
     for name, t in (("k_new", k_new), ("v_new", v_new), ("lk_new", lk_new), ("lv_new", lv_new),
                     ("k_pool", k_pool), ("v_pool", v_pool), ("lk_pool", lk_pool),
                     ("lv_pool", lv_pool), ("slot_mapping", slot_mapping)):
         _contig(name, t)
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (n_tok,), "slot_mapping [n_tok] int64")
-    _need(tuple(v_new.shape) == (n_tok, h_kv, d) and tuple(lv_new.shape) == (n_tok, r), "new row shapes")
-    dims = _dims(n_q_heads or h_kv, h_kv, d, r, _dtype_code(k_new), 0.0)
+    lead = (n_lr,) if per_agent else ()
+    _need(tuple(v_new.shape) == (n_tok, h_kv, d) and tuple(lk_new.shape) == lead + (n_tok, r)
+          and tuple(lv_new.shape) == lead + (n_tok, r), "new row shapes")
+    _need(tuple(lk_pool.shape) == lead + (n_pages, 16, r) and tuple(lv_pool.shape) == lead + (n_pages, r, 16),
+          "LR pool shapes")
+    dims = _dims(n_q_heads or h_kv, h_kv, d, r, _dtype_code(k_new), 0.0, n_pages * 16 * r if per_agent else 0)
     _check(lib.lra_cache_append(ctypes.byref(dims), n_tok, _ptr(slot_mapping), _ptr(k_new),
-                                _ptr(v_new), _ptr(lk_new), _ptr(lv_new), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(v_new), _ptr(lk_new), _ptr(lv_new), n_lr, _ptr(k_pool), _ptr(v_pool),
                                 _ptr(lk_pool), _ptr(lv_pool), n_pages, 16, _stream(k_new, stream)))
 
 

@@ -275,8 +275,6 @@ lra_status decode_entry(const lra_dims* dims, const void* q, int32_t n_req,
     a.out = out;
     a.workspace = workspace;
     a.lr_stride = dims->lr_agent_stride;
-    if (rope_cos && dims->lr_agent_stride != 0 && dims->dtype == LRA_BF16)
-        return fail(LRA_ERR_UNSUPPORTED, "decode: RoPE with per-agent LR caches is not supported");
     a.n_req = n_req;
     a.n_ctx = n_ctx;
     a.n_pages = n_pages;
@@ -561,17 +559,21 @@ lra_status lra_attn_prefill_paged_staged(const lra_dims* dims, const void* q, in
 
 lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* slot_mapping,
                             const void* k_new, const void* v_new, const void* lk_new,
-                            const void* lv_new, void* k_pool, void* v_pool, void* lk_pool,
+                            const void* lv_new, int32_t n_lr, void* k_pool, void* v_pool, void* lk_pool,
                             void* lv_pool, int32_t n_pages, int32_t page_size, void* stream) {
     g_err[0] = 0;
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
     if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "cache append: bf16 only");
-    if (dims->lr_agent_stride != 0)
-        return fail(LRA_ERR_UNSUPPORTED, "cache append: shared LR cache only (lr_agent_stride 0)");
     if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
     if (n_tok < 0) return fail(LRA_ERR_BAD_SHAPE, "n_tok %d < 0", n_tok);
     if (n_pages < 1) return fail(LRA_ERR_BAD_SHAPE, "n_pages %d < 1", n_pages);
+    if (n_lr < 1) return fail(LRA_ERR_BAD_SHAPE, "n_lr %d < 1", n_lr);
+    if (dims->lr_agent_stride == 0 && n_lr != 1)
+        return fail(LRA_ERR_BAD_SHAPE, "n_lr %d LR row sets need per-agent pools (lr_agent_stride > 0)", n_lr);
+    if (dims->lr_agent_stride > 0 && dims->lr_agent_stride < (long long)n_pages * page_size * dims->rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < one agent's LR pool (n_pages*page_size*r = %lld)",
+                    (long long)dims->lr_agent_stride, (long long)n_pages * page_size * dims->rank);
     REQUIRE_PTR(slot_mapping);
     REQUIRE_PTR(k_new);
     REQUIRE_PTR(v_new);
@@ -597,6 +599,8 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
     a.h_kv = dims->n_kv_heads;
     a.head_dim = dims->head_dim;
     a.rank = dims->rank;
+    a.n_lr = n_lr;
+    a.lr_stride = dims->lr_agent_stride;
     return lra::launch_cache_append_bf16(a, (hipStream_t)stream);
 }
 
@@ -667,8 +671,9 @@ lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req, const int
     lra_status st = check_dims(dims);
     if (st != LRA_OK) return st;
     if (dims->dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "naive expand: bf16 only");
-    if (dims->lr_agent_stride != 0)
-        return fail(LRA_ERR_UNSUPPORTED, "naive expand: shared LR cache only (lr_agent_stride 0)");
+    if (dims->lr_agent_stride > 0 && dims->lr_agent_stride < (long long)n_pages * page_size * dims->rank)
+        return fail(LRA_ERR_BAD_SHAPE, "lr_agent_stride %lld < one agent's LR pool (n_pages*page_size*r = %lld)",
+                    (long long)dims->lr_agent_stride, (long long)n_pages * page_size * dims->rank);
     if (page_size != 16) return fail(LRA_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
     if (n_req < 0) return fail(LRA_ERR_BAD_SHAPE, "n_req %d < 0", n_req);
     if (n_ctx < 1) return fail(LRA_ERR_BAD_SHAPE, "n_ctx %d < 1", n_ctx);
@@ -708,6 +713,7 @@ lra_status lra_naive_expand_pages(const lra_dims* dims, int32_t n_req, const int
     a.max_blocks = max_blocks;
     a.n_agents = n_agents;
     a.out_blocks = out_blocks;
+    a.lr_stride = dims->lr_agent_stride;
     a.h_kv = dims->n_kv_heads;
     a.head_dim = dims->head_dim;
     a.rank = dims->rank;

@@ -1,25 +1,24 @@
 // Paged decode entry: the shared-LR mode of the decode kernel (decode_kernel.h);
-// the per-agent-LR mode is built in decode_pa_bf16.hip and the RoPE mode in
-// decode_rope_bf16.hip (translation units of their own, compiled in parallel).
+// the per-agent-LR mode is built in decode_pa_bf16.hip, the RoPE mode in
+// decode_rope_bf16.hip and RoPE with per-agent LR in decode_rope_pa_bf16.hip
+// (translation units of their own, compiled in parallel).
 #include "decode_kernel.h"
 
 namespace lra {
 
 lra_status launch_decode_rope_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 lra_status launch_decode_pa_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+lra_status launch_decode_rope_pa_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 
 lra_status launch_decode_bf16(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
     const int d = a.head_dim, r = a.rank;
     if (a.rope_cos != nullptr) {
-        if (a.lr_stride != 0) {
-            set_error("decode: RoPE on the adapter key with per-agent LR caches is not supported");
-            return LRA_ERR_UNSUPPORTED;
-        }
-        // The RoPE mode always runs one workgroup per chunk.  Its persistent
+        // The RoPE modes always run one workgroup per chunk.  Their persistent
         // (chunk-queue) form is switched off: a GPU memory fault was observed
         // with it (rank 32, 512-token chunks) whose cause has not been found.
         DecodePlan q = p;
         q.persistent = 0;
+        if (a.lr_stride != 0) return launch_decode_rope_pa_bf16(a, q, s);
         return launch_decode_rope_bf16(a, q, s);
     }
     if (a.lr_stride != 0) return launch_decode_pa_bf16(a, p, s);

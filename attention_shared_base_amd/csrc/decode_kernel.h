@@ -138,7 +138,7 @@ struct Step {
 // Modes of the decode kernel: the rank-r score term on the shared LR cache; the
 // adapter key rebuilt and rotated (RoPE); one LR cache per agent (the agent's
 // L_k, L_v rows for its own requests' rows, at most PA_REQ requests per group).
-constexpr int MODE_SHARED = 0, MODE_ROPE = 1, MODE_PER_AGENT = 2;
+constexpr int MODE_SHARED = 0, MODE_ROPE = 1, MODE_PER_AGENT = 2, MODE_ROPE_PER_AGENT = 3;
 constexpr int PA_REQ = 4;
 
 // RoPE: cos, sin of one step's keys (page t, token n16), dims 16*ht + 4*q4 .. +3
@@ -152,8 +152,8 @@ struct StepRope {
 // wavefront (DEPTH - 1 steps of loads in flight).  MODE: see MODE_SHARED ..
 template <int D, int R, int SPW, int DEPTH, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) {
-    constexpr bool ROPE = MODE == MODE_ROPE;
-    constexpr bool PA = MODE == MODE_PER_AGENT;
+    constexpr bool ROPE = MODE == MODE_ROPE || MODE == MODE_ROPE_PER_AGENT;
+    constexpr bool PA = MODE == MODE_PER_AGENT || MODE == MODE_ROPE_PER_AGENT;
     constexpr int NQ = PA ? PA_REQ : 1;
     // request -> agent table fetched at kernel start (see below); the RoPE and
     // per-agent rank-32 instances keep scalar loads, as their registers are full
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
             for (int j = 0; j < NJ; ++j) s[t] = mfma16x16x32(T.k[t][j], qf[j], s[t]);
             if constexpr (MODE == MODE_SHARED) s[t] = mfma16x16x32(T.lk[0][t], qb, s[t]);
-            if constexpr (PA) {
+            if constexpr (PA && !ROPE) {
                 // each request slot's LR rows meet only that request's rows
 #pragma unroll
                 for (int u = 0; u < NQ; ++u) s[t] = mfma16x16x32(T.lk[u][t], my_req == u ? qb : zero8(), s[t]);
@@ -577,8 +577,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
             // adapter key term of each request: dK^T = B_k^(h)T L_k^T (lane =
             // token n16, dims 16*tile + 4*q4 + v), rotated by the token's
             // position, rounded to bf16, contracted with the query rows (all
-            // rows computed, only the request's rows kept)
-            for (int u = 0; u < nreq; ++u) {
+            // rows computed, only the request's rows kept).  With per-agent LR
+            // caches request slot u's own L_k rows are used.
+            auto rebuild_req = [&](int u, const bf16x8 (&lkt)[2]) {
                 const char* bkp = sm_bk + (u * NDT * 64 + lane) * BKW;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
 #pragma unroll
                     for (int tile = 0; tile < NDT; ++tile) {
                         const bf16x8 bop = *(const bf16x8*)(bkp + tile * 64 * BKW);
-                        dk[tile] = mfma16x16x32(bop, T.lk[0][t], zf4());
+                        dk[tile] = mfma16x16x32(bop, lkt[t], zf4());
                     }
 #pragma unroll
                     for (int ht = 0; ht < NDT / 2; ++ht) {
@@ -608,6 +609,14 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                     }
                     if (my_req == u) s[t] = acc_u;
                 }
+            };
+            if constexpr (PA) {
+                // at most NQ requests per row group (the plan's packing)
+#pragma unroll
+                for (int u = 0; u < NQ; ++u)
+                    if (u < nreq) rebuild_req(u, T.lk[u]);
+            } else {
+                for (int u = 0; u < nreq; ++u) rebuild_req(u, T.lk[0]);
             }
         }
         // Tokens at or past the chunk end: score -inf, and their values zeroed

@@ -137,6 +137,7 @@ struct ExpandArgs {
     const void* b_v;
     void* k_out;
     void* v_out;
+    int64_t lr_stride = 0;  // elements between agents' LR pools (0: one shared pool)
     int32_t n_req, n_ctx, n_pages, max_blocks, n_agents, out_blocks;
     int32_t h_kv, head_dim, rank;
 };
@@ -180,6 +181,8 @@ struct PagedArgs {
     void* lk_out;
     void* lv_out;
     int32_t n_tok, n_pages, h_kv, kv_len, head_dim, rank;
+    int32_t n_lr = 1;        // append: LR row sets (one per agent pool)
+    int64_t lr_stride = 0;   // append: elements between agents' LR pools
 };
 
 lra_status launch_cache_append_bf16(const PagedArgs& a, hipStream_t s);

@@ -8,6 +8,7 @@
 // For request i (context c, agent a) and every page b of c's block table:
 //   K_out[page i*out_blocks + b] = K_base[page] + L_k[page] B_k^(a)   (all KV heads)
 //   V_out[page i*out_blocks + b] = V_base[page] + L_v[page] B_v^(a)
+// (L_k, L_v from agent a's pools when the LR caches are per agent).
 // in the decode page layouts (K [H_kv][d/8][16][8], V [H_kv][d][16]), bf16
 // rounded to nearest even.  Plain decode attention over these per-request pages
 // (one context per request, B = 0) then computes the same attention as the
@@ -36,6 +37,7 @@ struct ExpandK {
     const bf16* b_v;
     bf16* k_out;
     bf16* v_out;
+    int64_t lr_stride;  // per-agent LR pools: elements between agents' pools (0: shared)
     int32_t n_req, n_ctx, n_pages, max_blocks, n_agents, h_kv, out_blocks, groups;
 };
 
@@ -76,8 +78,8 @@ __global__ __launch_bounds__(256) void lra_naive_expand_kernel(ExpandK a) {
         const int pid = min(max(bt[b], 0), a.n_pages - 1);
         __syncthreads();  // previous page's L rows no longer read; B staged
         for (int e = tid; e < PAGE * R; e += 256) {
-            s_lk[e / R][e % R] = (float)a.lk_pool[(size_t)pid * PAGE * R + e];
-            s_lv[e / PAGE][e % PAGE] = (float)a.lv_pool[(size_t)pid * PAGE * R + e];
+            s_lk[e / R][e % R] = (float)a.lk_pool[(size_t)agent * a.lr_stride + (size_t)pid * PAGE * R + e];
+            s_lv[e / PAGE][e % PAGE] = (float)a.lv_pool[(size_t)agent * a.lr_stride + (size_t)pid * PAGE * R + e];
         }
         __syncthreads();
         const bf16* kin = a.k_pool + (size_t)pid * kv_page + (size_t)h * D * PAGE;
@@ -284,6 +286,7 @@ lra_status launch_t(const lra::ExpandArgs& p, hipStream_t s) {
     k.n_agents = p.n_agents;
     k.h_kv = p.h_kv;
     k.out_blocks = p.out_blocks;
+    k.lr_stride = p.lr_stride;
     k.groups = (p.out_blocks + PAGES_PER_WG - 1) / PAGES_PER_WG;
     const long long grid = (long long)p.n_req * p.h_kv * k.groups;
     if (grid > 0x7fffffffLL) {

@@ -2,16 +2,16 @@
 // compute only the newly appended context; App. B: the accumulated context is
 // L = L_p + L_c).
 //
-// * Append: the base K/V rows and the shared LR rows of new tokens (a prefill
-//   chunk or one decode token per request) are written into the page pools at
-//   the slots a slot mapping names (slot = page * 16 + offset; negative = skip).
+// * Append: the base K/V rows and the LR rows of new tokens (a prefill chunk or
+//   one decode token per request; one LR row set per agent pool when the LR
+//   caches are per agent) are written into the page pools at the slots a slot
+//   mapping names (slot = page * 16 + offset; negative = skip).
 //   Page layouts are the decode kernel's: K [H_kv][d/8][16][8], V [H_kv][d][16],
 //   L_k [16][r], L_v [r][16].
-// * Gather: one context's pages back to the contiguous per-head rows the
-//   chunked-prefill kernel streams ([H_kv, kv_len, d], [kv_len, r]).  Prefill is
-//   bound by the matrix cores (hundreds of flops per byte of K/V), so staging
-//   its keys and values once costs a few percent of the attention itself and
-//   leaves the prefill kernel's LDS tile layout untouched.
+// * Gather: one context's pages back to the contiguous per-head rows of the
+//   contiguous prefill ([H_kv, kv_len, d], [kv_len, r]): the staged paged
+//   prefill, kept as a fallback and cross-check of the prefill that reads the
+//   pages in place.
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -34,12 +34,14 @@ struct PagedK {
     bf16* v_out;
     bf16* lk_out;
     bf16* lv_out;
-    int32_t n_tok, n_pages, h_kv, kv_len, max_blocks;
+    int64_t lr_stride;  // append: elements between agents' LR pools
+    int32_t n_tok, n_pages, h_kv, kv_len, max_blocks, n_lr;
 };
 
 // Append: workgroup = one token, 256 threads.  Rows k_rows/v_rows are
 // [n_tok, H_kv, d] (the layout a K/V projection produces), lk_rows/lv_rows
-// [n_tok, r].
+// [n_lr, n_tok, r]: row set a goes to the LR pools of agent a (one set for a
+// shared LR cache).
 template <int D, int R>
 __global__ __launch_bounds__(256) void lra_cache_append_kernel(PagedK a) {
     const int tok = blockIdx.x;
@@ -59,9 +61,11 @@ __global__ __launch_bounds__(256) void lra_cache_append_kernel(PagedK a) {
         a.v_pool[pid * kv_page + (size_t)h * D * PAGE + (size_t)c * PAGE + t] =
             a.v_rows[((size_t)tok * a.h_kv + h) * D + c];
     }
-    for (int e = threadIdx.x; e < R; e += blockDim.x) {
-        a.lk_pool[(pid * PAGE + t) * R + e] = a.lk_rows[(size_t)tok * R + e];
-        a.lv_pool[(pid * R + e) * PAGE + t] = a.lv_rows[(size_t)tok * R + e];
+    for (int e = threadIdx.x; e < a.n_lr * R; e += blockDim.x) {
+        const int ag = e / R, k = e % R;
+        const size_t src = ((size_t)ag * a.n_tok + tok) * R + k;
+        a.lk_pool[ag * a.lr_stride + (pid * PAGE + t) * R + k] = a.lk_rows[src];
+        a.lv_pool[ag * a.lr_stride + (pid * R + k) * PAGE + t] = a.lv_rows[src];
     }
 }
 
@@ -127,6 +131,8 @@ lra_status launch_append_t(const lra::PagedArgs& p, hipStream_t s) {
     k.n_tok = p.n_tok;
     k.n_pages = p.n_pages;
     k.h_kv = p.h_kv;
+    k.n_lr = p.n_lr;
+    k.lr_stride = p.lr_stride;
     hipLaunchKernelGGL((lra_cache_append_kernel<D, R>), dim3(p.n_tok), dim3(256), 0, s, k);
     return lra::check_launch("lra_cache_append_kernel");
 }

@@ -76,10 +76,10 @@ typedef struct lra_dims {
      * LR cache per agent (BaseShared, or PreLRShared with per-agent A; LRAgent
      * §3, PReCache): agent a's L_k / L_v start lr_agent_stride elements after
      * agent a-1's, in l_k / l_v of lra_attn_prefill and lk_pool / lv_pool of
-     * lra_attn_decode (which then packs at most 4 requests per row group and
-     * does not combine it with RoPE) and lk_pool / lv_pool of
-     * lra_attn_prefill_paged.  The staged paged prefill, the cache append and
-     * the naive baseline take 0 only. */
+     * lra_attn_decode (which then packs at most 4 requests per row group,
+     * with or without RoPE), lra_attn_prefill_paged,
+     * lra_cache_append and the naive baselines.  The staged paged prefill
+     * takes 0 only. */
     int64_t lr_agent_stride;
 } lra_dims;
 
@@ -301,19 +301,24 @@ lra_status lra_attn_prefill_paged_staged(const lra_dims* dims,
                                          size_t workspace_bytes, void* stream);
 /*
  * Append new tokens to the paged pools (the decode-time and prefill-time write
- * of the base K/V rows and the shared LR rows; LRAgent §3 BaseLRShared: one LR
- * row per token serves every agent).  Token i goes to slot slot_mapping[i] =
- * page * page_size + offset; a negative slot skips the token.
+ * of the base K/V rows and the LR rows; LRAgent §3 BaseLRShared: one LR row
+ * per token serves every agent; BaseShared: one per agent).  Token i goes to
+ * slot slot_mapping[i] = page * page_size + offset; a negative slot skips the
+ * token.
  *   slot_mapping   [n_tok] int64                    device
  *   k_new, v_new   [n_tok, H_kv, d] (K already rotated if the model uses RoPE)
- *   lk_new, lv_new [n_tok, r]  (e.g. rows written by lra_lr_cache_build)
+ *   lk_new, lv_new [n_lr, n_tok, r]  (e.g. rows written by lra_lr_cache_build)
+ *   n_lr           LR row sets: 1 with one shared LR pool
+ *                  (dims->lr_agent_stride == 0); with per-agent pools
+ *                  (lr_agent_stride >= n_pages * page_size * r) set a goes to
+ *                  agent a's pools, for a < n_lr (the pools must hold n_lr)
  *   k_pool ...     the pools of lra_attn_decode, written in place
  * Slots at or past n_pages * page_size are skipped.  Two tokens with the same
  * slot leave either one.  bf16 only.
  */
 lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* slot_mapping,
                             const void* k_new, const void* v_new,
-                            const void* lk_new, const void* lv_new,
+                            const void* lk_new, const void* lv_new, int32_t n_lr,
                             void* k_pool, void* v_pool, void* lk_pool, void* lv_pool,
                             int32_t n_pages, int32_t page_size, void* stream);
 /*
@@ -376,7 +381,8 @@ lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos,
  * in the layouts of k_pool / v_pool, bf16 rounded to nearest even.  Decode
  * attention over those pages (lra_attn_decode with one context per request,
  * block table i * out_blocks + b and B = 0) is then plain attention over
- * per-request materialised caches.  Arguments as in lra_attn_decode;
+ * per-request materialised caches.  Arguments as in lra_attn_decode (L_k, L_v
+ * from agent a's pools when dims->lr_agent_stride > 0);
  *   k_out, v_out   [n_req * out_blocks, H_kv, ...] device, caller-owned
  *   out_blocks     blocks reserved per request, 1 <= out_blocks <= max_blocks
  * bf16 only.  Blocks past a context's length are not written.

@@ -90,7 +90,8 @@ def call_decode(dm, **over):
     (dims(), {"ws": None}, 1),
     (dims(), {"cos": A}, 1),                 # rope tables go in pairs
     (lra.Dims(32, 8, 128, 16, 1, 0.0, -1), {}, 2),   # negative LR stride
-    (lra.Dims(32, 8, 128, 16, 1, 0.0, 2048 * 16 * 16), {"cos": A, "sin": A}, 3),  # per-agent LR + RoPE
+    # per-agent LR + RoPE is supported: a short table is still rejected before launch
+    (lra.Dims(32, 8, 128, 16, 1, 0.0, 2048 * 16 * 16), {"cos": A, "sin": A, "rows": 100}, 2),
     (dims(), {"cos": A, "sin": ctypes.c_void_p(0x100004)}, 4),
     (dims(), {"cos": A, "sin": A, "rows": 8191}, 2),          # tables shorter than max_ctx_len
     (dims(), {"cos": A, "sin": A, "rows": 0, "max_ctx": 0}, 2),  # at least one row
@@ -220,6 +221,7 @@ def call_expand(dm, **over):
     (dims(), {"n_ctx": 0}, 2),
     (dims(), {"ko": None}, 1),
     (dims(), {"vo": ctypes.c_void_p(0x100002)}, 4),
+    (dims(stride=64 * 16 * 16 - 1), {}, 2),   # per-agent LR pools: stride below one pool
 ])
 def test_naive_expand_validation(dm, over, want):
     st, msg = call_expand(dm, **over)
@@ -270,16 +272,19 @@ def test_paged_prefill_and_append_validation():
     assert ps(dm=dims(stride=64 * 16 * 16)) == 3
 
     def ap(**o):
-        a = dict(n=4, slots=A, k=A, v=A, lk=A, lv=A, kp=A, vp=A, lkp=A, lvp=A, n_pages=8, page=16)
+        a = dict(n=4, slots=A, k=A, v=A, lk=A, lv=A, n_lr=1, kp=A, vp=A, lkp=A, lvp=A, n_pages=8, page=16)
         a.update(o)
         return lib.lra_cache_append(ctypes.byref(o.pop("dm", dm)), a["n"], a["slots"], a["k"], a["v"],
-                                    a["lk"], a["lv"], a["kp"], a["vp"], a["lkp"], a["lvp"],
+                                    a["lk"], a["lv"], a["n_lr"], a["kp"], a["vp"], a["lkp"], a["lvp"],
                                     a["n_pages"], a["page"], None)
     assert ap(slots=None) == 1
     assert ap(n=-1) == 2
     assert ap(page=8) == 3
     assert ap(dm=dims(dt=0)) == 3
     assert ap(kp=ctypes.c_void_p(0x100004)) == 4
+    assert ap(n_lr=0) == 2
+    assert ap(n_lr=2) == 2                                  # several row sets need per-agent pools
+    assert ap(n_lr=2, dm=dims(stride=8 * 16 * 16 - 1)) == 2  # stride below one agent's pool
 
 
 def test_lr_build_workspace_size():

@@ -137,8 +137,10 @@ def test_decode_equals_last_prefill_row():
 
 
 @pytest.mark.slow
-def test_cfg5_layer_prefill_sampled():
-    """One layer of the 4096-over-131072 PreLRShared step: LR build, then 8 agents' prefill."""
+def test_cfg5_layer_prefill_64_rows_all_agents():
+    """One layer of the 4096-over-131072 PreLRShared step: LR build, then 8 agents' prefill;
+    64 rows (first and last included) of every agent against the oracle over the LR rows the
+    kernel read, and a subset against the oracle's own fp64 X A."""
     import torch
     import attention_shared_base_amd as lra
     from gpu_helpers import dev
@@ -159,13 +161,18 @@ def test_cfg5_layer_prefill_sampled():
     got = host(d.run(lk=lk, lv=lv))
     # oracle: the same LR bits the attention read (staged check), and the fp64 X A end to end
     lk_h, lv_h = host(lk), host(lv)
-    rows = [0, 1, 2047, 4094, 4095]
-    ref = oracle_prefill(pre, rows=rows, l_k=lk_h, l_v=lv_h, requests=[0, 3, 7])
-    ma, rel = assert_parity(got[[0, 3, 7]][:, rows], ref, "bf16", "cfg5 layer 0 (GPU-built L)")
-    print(f"[prefill] cfg5 layer 0 sampled: max-abs {ma:.2e} rel-L2 {rel:.2e}")
+    # 64 rows of every agent: the first and last new tokens and 62 spread between
+    rows = np.unique(np.concatenate([[0, 1, 4094, 4095], np.linspace(2, 4093, 60).astype(int)]))
+    assert len(rows) == 64
+    agents = list(range(len(pre.req_agent)))
+    ref = oracle_prefill(pre, rows=rows, l_k=lk_h, l_v=lv_h, requests=agents)
+    ma, rel = assert_parity(got[:, rows], ref, "bf16", "cfg5 layer 0 (GPU-built L)")
+    print(f"[prefill] cfg5 layer 0, 64 rows x {len(agents)} agents: max-abs {ma:.2e} rel-L2 {rel:.2e}")
+    for i in agents:  # each agent on its own at the same bar
+        assert_parity(got[i, rows], ref[i], "bf16", f"cfg5 layer 0 agent {i}")
     import oracle
     xk, xv = oracle.lr_cache_build(w.widen(lr.x), w.widen(lr.a_k).T, w.widen(lr.a_v).T)
     lk_e = np.concatenate([w.widen(pre.l_k), xk])
     lv_e = np.concatenate([w.widen(pre.l_v), xv])
-    ref_e = oracle_prefill(pre, rows=rows, l_k=lk_e, l_v=lv_e, requests=[0, 3, 7])
-    assert_parity(got[[0, 3, 7]][:, rows], ref_e, "bf16", "cfg5 layer 0 (fp64 X A)")
+    ref_e = oracle_prefill(pre, rows=rows[::8], l_k=lk_e, l_v=lv_e, requests=[0, 3, 7])
+    assert_parity(got[[0, 3, 7]][:, rows[::8]], ref_e, "bf16", "cfg5 layer 0 (fp64 X A)")
