@@ -18,14 +18,14 @@ __all__ = [
     "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
     "prefill_paged", "prefill_paged_staged", "prefill_paged_staged_workspace_size",
     "cache_append", "decode_noalloc",
-    "naive_prefill", "naive_prefill_workspace_size",
+    "naive_prefill", "naive_prefill_workspace_size", "ceiling_hbm_read", "ceiling_mfma_bf16",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "liblra_attn.so")
 
 LRA_F32, LRA_BF16 = 0, 1
-ABI_VERSION = 5  # LRA_ABI_VERSION of include/lra_attn.h
+ABI_VERSION = 6  # LRA_ABI_VERSION of include/lra_attn.h
 
 EXPORTED_SYMBOLS = (
     "lra_abi_version", "lra_status_str", "lra_last_error", "lra_attn_decode_workspace_size",
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "lra_naive_expand_pages", "lra_attn_prefill_paged", "lra_attn_prefill_paged_staged_workspace_size",
     "lra_attn_prefill_paged_staged",
     "lra_cache_append", "lra_attn_decode_noalloc", "lra_naive_prefill_workspace_size",
-    "lra_naive_prefill",
+    "lra_naive_prefill", "lra_ceiling_hbm_read", "lra_ceiling_mfma_bf16",
 )
 
 
@@ -118,6 +118,10 @@ def load():
     lib.lra_naive_expand_pages.argtypes = [
         ctypes.POINTER(Dims), I32, P, I32, P, P, P, P, P, I32, I32, P, I32, P, P, P, I32, P, P,
         I32, P]
+    lib.lra_ceiling_hbm_read.restype = I32
+    lib.lra_ceiling_hbm_read.argtypes = [P, ctypes.c_size_t, I32, I32, P, P]
+    lib.lra_ceiling_mfma_bf16.restype = I32
+    lib.lra_ceiling_mfma_bf16.argtypes = [I32, I32, I32, P, P]
     _lib = lib
     return lib
 
@@ -594,3 +598,25 @@ def naive_prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=
         _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), workspace.numel(),
         _stream(q, stream)))
     return out
+
+
+def ceiling_hbm_read(buf, sink, *, n_workgroups=0, nontemporal=True, chunked=False, stream=None):
+    """Device ceiling, not part of the method: ``lra_ceiling_hbm_read`` streams every
+    byte of the contiguous device tensor ``buf`` (its size a multiple of 16 bytes)
+    and keeps nothing; ``sink`` is a small device tensor (>= 4 bytes).  ``chunked``:
+    each workgroup reads one contiguous chunk, else a grid-stride sweep."""
+    lib = load()
+    _contig("buf", buf)
+    flags = (1 if nontemporal else 0) | (2 if chunked else 0)
+    _check(lib.lra_ceiling_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), int(n_workgroups), flags,
+                                    _ptr(sink), _stream(buf, stream)))
+
+
+def ceiling_mfma_bf16(sink, *, n_workgroups, iters, lds_operand=False, stream=None):
+    """Device ceiling, not part of the method: ``lra_ceiling_mfma_bf16`` issues
+    n_workgroups * iters * 524288 flops of bf16 MFMA (B operand from LDS when
+    ``lds_operand``).  Returns that flop count."""
+    lib = load()
+    _check(lib.lra_ceiling_mfma_bf16(int(bool(lds_operand)), int(n_workgroups), int(iters), _ptr(sink),
+                                     _stream(sink, stream)))
+    return int(n_workgroups) * int(iters) * 524288

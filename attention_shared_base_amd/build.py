@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.hip", "decode_bf16.hip", "decode_pa_bf16.hip", "decode_rope_bf16.hip",
            "decode_rope_pa_bf16.hip", "prefill_bf16.hip", "attn_f32.hip", "lr_build.hip",
-           "naive_expand.hip", "paged.hip"]
+           "naive_expand.hip", "paged.hip", "ceiling.hip"]
 # per-source extra flags: the RoPE decodes keep MFMA results in VGPRs (their rotation
 # reads them on the VALU)
 EXTRA_FLAGS = {"decode_rope_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -827,4 +827,34 @@ lra_status lra_rope_table_build(double theta, int32_t head_dim, int32_t n_pos, f
     return lra::launch_rope_table(theta, head_dim, n_pos, cos_out, sin_out, (hipStream_t)stream);
 }
 
+lra_status lra_ceiling_hbm_read(const void* buf, size_t n_bytes, int32_t n_workgroups, int32_t flags,
+                                uint32_t* sink, void* stream) {
+    g_err[0] = 0;
+    REQUIRE_PTR(buf);
+    REQUIRE_PTR(sink);
+    if (n_bytes == 0 || n_bytes % 16 != 0)
+        return fail(LRA_ERR_BAD_SHAPE, "n_bytes %zu must be a positive multiple of 16", n_bytes);
+    if (n_workgroups < 0 || n_workgroups > 65535)
+        return fail(LRA_ERR_BAD_SHAPE, "n_workgroups %d outside [0, 65535]", n_workgroups);
+    if (flags & ~(LRA_READ_NONTEMPORAL | LRA_READ_CHUNKED)) return fail(LRA_ERR_BAD_SHAPE, "unknown flags 0x%x", flags);
+    int n_wg = n_workgroups;
+    if (n_wg == 0) {  // 16 workgroups per CU of the 256, fewer when the buffer is small
+        const uint64_t need = (n_bytes / 16 + 4095) / 4096;
+        n_wg = (int)(need < 4096 ? need : 4096);
+    }
+    return lra::launch_ceiling_read(buf, n_bytes, n_wg, (flags & LRA_READ_NONTEMPORAL) != 0,
+                                    (flags & LRA_READ_CHUNKED) != 0, sink, (hipStream_t)stream);
+}
+
+lra_status lra_ceiling_mfma_bf16(int32_t lds_operand, int32_t n_workgroups, int32_t iters, uint32_t* sink,
+                                 void* stream) {
+    g_err[0] = 0;
+    REQUIRE_PTR(sink);
+    if (lds_operand != 0 && lds_operand != 1) return fail(LRA_ERR_BAD_SHAPE, "lds_operand must be 0 or 1");
+    if (n_workgroups < 1 || n_workgroups > 65535)
+        return fail(LRA_ERR_BAD_SHAPE, "n_workgroups %d outside [1, 65535]", n_workgroups);
+    if (iters < 1 || iters > (1 << 20)) return fail(LRA_ERR_BAD_SHAPE, "iters %d outside [1, 2^20]", iters);
+    return lra::launch_ceiling_mfma(lds_operand != 0, n_workgroups, iters, sink, (hipStream_t)stream);
+}
+
 }  // extern "C"

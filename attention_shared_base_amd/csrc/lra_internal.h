@@ -122,6 +122,11 @@ lra_status launch_lr_build_f32(const LRBuildArgs& a, hipStream_t s);
 lra_status launch_rope_table(double theta, int head_dim, int n_pos, float* c, float* s,
                              hipStream_t st);
 
+// ----------------------------------------------------------------- device ceilings
+lra_status launch_ceiling_read(const void* buf, uint64_t n_bytes, int n_wg, bool nt, bool chunked,
+                               uint32_t* sink, hipStream_t s);
+lra_status launch_ceiling_mfma(bool lds, int n_wg, int iters, uint32_t* sink, hipStream_t s);
+
 // ----------------------------------------------------------------- naive baseline
 // Materialised adapter terms (measurement baseline only; see naive_expand.hip).
 struct ExpandArgs {

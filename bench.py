@@ -203,13 +203,54 @@ def measured_traffic(leg):
         return None, f"no counter summary ({type(e).__name__})"
 
 
-def _roofline(leg, bound, achieved, bytes_or_flops=None):
+_FLOORS = {}
+
+
+def read_floor(nbytes, calls=60):
+    """The fastest plain read of nbytes this device gives (lra_ceiling_hbm_read): best of
+    non-temporal / cached loads, grid-stride / chunked layouts and three grid sizes,
+    rotated over buffers of >= 1 GiB in all so that the 256 MB Infinity Cache cannot
+    serve repeats.  Measured once per size."""
+    nbytes = -(-int(nbytes) // 16) * 16
+    if nbytes in _FLOORS:
+        return _FLOORS[nbytes]
+    import torch
+    import attention_shared_base_amd as lra
+    n_sets = max(2, -(-(1 << 30) // nbytes))
+    bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device="cuda") for i in range(n_sets)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best = None
+    for nt in (True, False):
+        for chunked in (False, True):
+            for n_wg in (2048, 4096, 8192):
+                ms = _time_calls(lambda i: lra.ceiling_hbm_read(bufs[i], sink, n_workgroups=n_wg, nontemporal=nt,
+                                                                chunked=chunked), n_sets, calls, 5)
+                if best is None or ms < best[0]:
+                    best = (ms, nt, chunked, n_wg)
+    ms, nt, chunked, n_wg = best
+    dev_kernel = f"hbm_read{'_chunked' if chunked else ''}_kernel<{'true' if nt else 'false'}>"
+    _FLOORS[nbytes] = {"bytes": nbytes, "us_per_call": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                       "kernel": f"lra_ceiling_hbm_read ({dev_kernel})", "device_kernel": dev_kernel,
+                       "loads": "non-temporal" if nt else "cached",
+                       "layout": "chunked" if chunked else "grid-stride", "workgroups": n_wg,
+                       "buffers_rotated": n_sets, "calls": calls}
+    del bufs
+    return _FLOORS[nbytes]
+
+
+def _roofline(leg, bound, achieved, floor_bytes=None):
+    """The roofline object of a leg; for HBM-bound legs given floor_bytes, also the
+    leg's rate as a fraction of a plain read of that many bytes on this device."""
     peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
     rl = {"bound": bound, "achieved": achieved, "peak": peak,
           "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": achieved / peak}
     traffic, src = measured_traffic(leg)
     rl["traffic"] = traffic
     rl["traffic_source"] = src
+    if floor_bytes:
+        fl = read_floor(floor_bytes)
+        rl["measured_read"] = fl
+        rl["frac_of_measured_read"] = achieved / fl["gbs"]
     return rl
 
 
@@ -365,7 +406,7 @@ def _decode_leg(name, workload, case, ms, stats, nbytes, got, oracle_fn, oracle_
     gbs = nbytes / (ms * 1e-3) / 1e9
     leg = {"workload": workload, "value": case.n_req / (ms * 1e-3), "unit": "tokens/s",
            "ms_per_call": ms, "call_us": stats,
-           "roofline": _roofline(name, "hbm", gbs),
+           "roofline": _roofline(name, "hbm", gbs, nbytes),
            "algorithmic_bytes": nbytes}
     leg.update(UNCHECKED)
     if CHECK:
@@ -545,7 +586,7 @@ def leg_paged_decode(steps, warmup):
                         "16-token pages, 32 requests over 8 agents, Hq32 Hkv8 d128 r32, bf16"
                         % int(lens.sum()),
             "value": 32 / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "call_us": stats,
-            "roofline": _roofline("paged_decode", "hbm", gbs), "algorithmic_bytes": nbytes,
+            "roofline": _roofline("paged_decode", "hbm", gbs, nbytes), "algorithmic_bytes": nbytes,
             "data": "seeded host generator (workload 4 of the tests)"}
     leg.update(UNCHECKED)
     if CHECK:
@@ -870,7 +911,7 @@ def leg_lr_build(steps, warmup, n_sets=8):
     c0 = cases[0]
     leg = {"workload": "LR-cache build L = X [A_k|A_v]: X [4096, 4096] bf16, r 16",
             "value": gbs, "unit": "GB/s", "ms_per_call": ms, "call_us": stats,
-            "roofline": _roofline("lr_build", "hbm", gbs), "algorithmic_bytes": nbytes,
+            "roofline": _roofline("lr_build", "hbm", gbs, nbytes), "algorithmic_bytes": nbytes,
             "input_sets_rotated": n_sets}
     leg.update(UNCHECKED)
     if CHECK:
@@ -984,6 +1025,49 @@ def leg_prelr_step(steps, warmup, n_layers=32):
     return leg
 
 
+def leg_ceilings(steps, warmup):
+    """What this device sustains, as reference points for the rooflines: the plain read
+    stream at 1 GiB, the bf16 MFMA stream with both operands in registers and with the
+    B operand read from LDS for every MFMA, and torch's bf16 GEMM (8192^3)."""
+    import torch
+    import attention_shared_base_amd as lra
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    rd = read_floor(1 << 30)
+    n_wg, iters = 2048, 2048  # 8 workgroups (32 wavefronts) per CU, about a millisecond a call
+    mfma = {}
+    for lds in (False, True):
+        flops = n_wg * iters * 524288
+        ms = _time_calls(lambda i: lra.ceiling_mfma_bf16(sink, n_workgroups=n_wg, iters=iters, lds_operand=lds),
+                         1, max(10, steps // 10), 3)
+        tf = flops / (ms * 1e-3) / 1e12
+        mfma["lds_operand" if lds else "register_operands"] = {
+            "kernel": "lra_ceiling_mfma_bf16", "flops_per_call": flops, "ms_per_call": ms, "tflops": tf,
+            "frac_of_peak": tf / BF16_PEAK_TFLOPS,
+            # v_mfma_f32_32x32x16_bf16 at one issue per 8 passes on every SIMD, at the
+            # published 2.4 GHz, is the published peak; this is the clock that would
+            # give the measured rate if the MFMA pipes never idled
+            "clock_ghz_if_pipes_never_idle": 2.4 * tf / BF16_PEAK_TFLOPS}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty_like(a)
+    gms = _time_calls(lambda i: torch.mm(a, b, out=c), 1, max(10, steps // 10), 3)
+    gtf = 2 * 8192 ** 3 / (gms * 1e-3) / 1e12
+    best = max(v["tflops"] for v in mfma.values())
+    leg = {"workload": "device ceilings: HBM read stream of 1 GiB; bf16 MFMA stream, 2048 workgroups x "
+                       "2048 rounds; torch bf16 GEMM 8192^3",
+           "value": best, "unit": "TFLOP/s", "ms_per_call": mfma["register_operands"]["ms_per_call"],
+           "roofline": _roofline("ceilings", "mfma", best),
+           "hbm_read": dict(rd, frac_of_peak=rd["gbs"] / HBM_PEAK_GBS,
+                            traffic=measured_traffic(f"ceilings_read_{rd['device_kernel']}")[0]),
+           "mfma_bf16": mfma,
+           "torch_gemm_bf16": {"shape": [8192, 8192, 8192], "ms_per_call": gms, "tflops": gtf,
+                               "frac_of_peak": gtf / BF16_PEAK_TFLOPS},
+           "cpu_baseline": None, "parity": None,
+           "note_oracle": "device probes: nothing to compare with the oracle"}
+    return leg
+
+
 # ----------------------------------------------------------------------------- misc
 
 def copy_calibration(nbytes=1 << 30, reps=10):
@@ -1032,12 +1116,13 @@ def _extra_legs(args, base_ms, primary_cpu, extra=None):
             "workload1_fp32": lambda: leg_workload1_fp32(args.steps, 10),
             "agent_scaling": lambda: leg_agent_scaling(max(20, args.steps // 2), 5, pcpu),
             "lr_build": lambda: leg_lr_build(args.steps, 10),
-            "prelr_step": lambda: leg_prelr_step(1, 1)}
+            "prelr_step": lambda: leg_prelr_step(1, 1),
+            "ceilings": lambda: leg_ceilings(args.steps, 3)}
 
 
 ALL_LEGS = ("workload1_fp32,agent_scaling,decode_rope,decode_qkvo_r4,decode_per_agent,naive_decode,"
             "prefill_rope,prefill_paged,naive_prefill,paged_decode,naive_paged_decode,lr_build,"
-            "prelr_step")
+            "prelr_step,ceilings")
 
 
 def main():
@@ -1135,7 +1220,7 @@ def main():
             "algorithmic_bytes_per_call": nbytes,
             "bytes_if_agents_did_not_share": unshared,
         },
-        "roofline": _roofline("primary", "hbm", gbs),
+        "roofline": _roofline("primary", "hbm", gbs, nbytes),
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,
         "parity": par,

@@ -63,7 +63,7 @@ typedef int32_t lra_status;
 #define LRA_F32 0
 #define LRA_BF16 1
 
-#define LRA_ABI_VERSION 5
+#define LRA_ABI_VERSION 6
 
 typedef struct lra_dims {
     int32_t n_q_heads;   /* H_q */
@@ -423,6 +423,44 @@ lra_status lra_naive_prefill(const lra_dims* dims,
                              const void* b_k, const void* b_v, int32_t n_agents,
                              const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                              void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Device ceilings, not part of the method: two measurement kernels that give the
+ * rates this device sustains, so that the attention kernels' rates can be set
+ * against a rate reached on the same chip as well as against the published peaks.
+ *
+ * lra_ceiling_hbm_read streams n_bytes from buf (device, 16-byte aligned, n_bytes a
+ * positive multiple of 16) with 16-byte loads, sixteen in flight per lane, and
+ * keeps nothing.
+ *   n_workgroups  256-lane workgroups in the grid; 0 chooses 16 per CU (4096),
+ *                 fewer when the buffer is smaller
+ *   flags         LRA_READ_NONTEMPORAL: non-temporal loads (else ordinary cached
+ *                 loads); LRA_READ_CHUNKED: workgroup b reads the b-th contiguous
+ *                 chunk of the buffer (else a grid-stride sweep, each wavefront
+ *                 instruction covering 1 KB, the grid moving front to back)
+ *   sink          device, 16-byte aligned, >= 4 bytes; written only when the XOR
+ *                 fold of the 16-byte words one lane read equals 0x6a09e667 (a
+ *                 guard against the loads being removed)
+ * Algorithmic bytes per call: n_bytes.
+ *
+ * lra_ceiling_mfma_bf16 runs n_workgroups workgroups of four wavefronts; each
+ * wavefront issues iters rounds of four independent v_mfma_f32_32x32x16_bf16
+ * (fp32 accumulation).  lds_operand 1 takes every MFMA's B operand from a new
+ * 16-byte LDS read per lane (1 KB per wavefront per MFMA), 0 keeps both operands
+ * in registers.  n_workgroups in [1, 65535], iters in [1, 2^20].  sink as above
+ * (written only for an impossible sum).
+ * Flops per call: n_workgroups * 4 * iters * 4 * (2 * 32 * 32 * 16)
+ *               = n_workgroups * iters * 524288.
+ *
+ * Both are asynchronous on stream and allocate nothing.  Errors: LRA_ERR_NULL_PTR,
+ * LRA_ERR_MISALIGNED, LRA_ERR_BAD_SHAPE, LRA_ERR_HIP.
+ */
+#define LRA_READ_NONTEMPORAL 1
+#define LRA_READ_CHUNKED 2
+lra_status lra_ceiling_hbm_read(const void* buf, size_t n_bytes, int32_t n_workgroups, int32_t flags,
+                                uint32_t* sink, void* stream);
+lra_status lra_ceiling_mfma_bf16(int32_t lds_operand, int32_t n_workgroups, int32_t iters, uint32_t* sink,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

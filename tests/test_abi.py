@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = lra.load()
-    assert lra.abi_version() == 5
+    assert lra.abi_version() == 6
     for s in range(7):
         assert lib.lra_status_str(s).decode().startswith("LRA_")
     assert b"unknown" in lib.lra_status_str(99)
@@ -349,3 +349,24 @@ def test_naive_prefill_validation():
     assert call(wsz=16) == 5
     assert call(cos=A, sin=A, rows=255) == 2
     assert call(n_req=0) == 0
+
+
+def test_ceiling_validation():
+    lib = lra.load()
+    rd = lib.lra_ceiling_hbm_read
+    assert rd(None, 1024, 0, 1, A, None) == 1
+    assert rd(A, 1024, 0, 1, None, None) == 1
+    assert rd(ctypes.c_void_p(0x100008), 1024, 0, 1, A, None) == 4
+    assert rd(A, 0, 0, 1, A, None) == 2
+    assert rd(A, 1000, 0, 1, A, None) == 2
+    assert rd(A, 1024, -1, 1, A, None) == 2
+    assert rd(A, 1024, 65536, 1, A, None) == 2
+    assert rd(A, 1024, 0, 4, A, None) == 2
+    assert rd(A, 1024, 0, -1, A, None) == 2
+    mm = lib.lra_ceiling_mfma_bf16
+    assert mm(0, 256, 16, None, None) == 1
+    assert mm(2, 256, 16, A, None) == 2
+    assert mm(0, 0, 16, A, None) == 2
+    assert mm(1, 65536, 16, A, None) == 2
+    assert mm(0, 256, 0, A, None) == 2
+    assert mm(0, 256, (1 << 20) + 1, A, None) == 2

@@ -56,6 +56,8 @@ def test_launching_entry_points_report_hip_error():
         "append": lambda: lib.lra_cache_append(ctypes.byref(dm), 4, A, A, A, A, A, 1, A, A, A, A, 8, 16, None),
         "naive_expand": lambda: lib.lra_naive_expand_pages(ctypes.byref(dm), 4, A, 1, A, A, A, A, A, 8, 16, A, 4,
                                                            A, A, A, 4, A, A, 4, None),
+        "ceiling_read": lambda: lib.lra_ceiling_hbm_read(A, 1 << 20, 0, 1, A, None),
+        "ceiling_mfma": lambda: lib.lra_ceiling_mfma_bf16(1, 256, 16, A, None),
     }
     for name, call in cases.items():
         st = call()
