@@ -612,11 +612,11 @@ def ceiling_hbm_read(buf, sink, *, n_workgroups=0, nontemporal=True, chunked=Fal
                                     _ptr(sink), _stream(buf, stream)))
 
 
-def ceiling_mfma_bf16(sink, *, n_workgroups, iters, lds_operand=False, stream=None):
+def ceiling_mfma_bf16(sink, *, n_workgroups, iters, lds_operands=0, stream=None):
     """Device ceiling, not part of the method: ``lra_ceiling_mfma_bf16`` issues
-    n_workgroups * iters * 524288 flops of bf16 MFMA (B operand from LDS when
-    ``lds_operand``).  Returns that flop count."""
+    n_workgroups * iters * 524288 flops of bf16 MFMA, ``lds_operands`` (0, 1 or 2)
+    of each MFMA's operands read from LDS.  Returns that flop count."""
     lib = load()
-    _check(lib.lra_ceiling_mfma_bf16(int(bool(lds_operand)), int(n_workgroups), int(iters), _ptr(sink),
+    _check(lib.lra_ceiling_mfma_bf16(int(lds_operands), int(n_workgroups), int(iters), _ptr(sink),
                                      _stream(sink, stream)))
     return int(n_workgroups) * int(iters) * 524288

@@ -846,15 +846,15 @@ lra_status lra_ceiling_hbm_read(const void* buf, size_t n_bytes, int32_t n_workg
                                     (flags & LRA_READ_CHUNKED) != 0, sink, (hipStream_t)stream);
 }
 
-lra_status lra_ceiling_mfma_bf16(int32_t lds_operand, int32_t n_workgroups, int32_t iters, uint32_t* sink,
+lra_status lra_ceiling_mfma_bf16(int32_t lds_operands, int32_t n_workgroups, int32_t iters, uint32_t* sink,
                                  void* stream) {
     g_err[0] = 0;
     REQUIRE_PTR(sink);
-    if (lds_operand != 0 && lds_operand != 1) return fail(LRA_ERR_BAD_SHAPE, "lds_operand must be 0 or 1");
+    if (lds_operands < 0 || lds_operands > 2) return fail(LRA_ERR_BAD_SHAPE, "lds_operands must be 0, 1 or 2");
     if (n_workgroups < 1 || n_workgroups > 65535)
         return fail(LRA_ERR_BAD_SHAPE, "n_workgroups %d outside [1, 65535]", n_workgroups);
     if (iters < 1 || iters > (1 << 20)) return fail(LRA_ERR_BAD_SHAPE, "iters %d outside [1, 2^20]", iters);
-    return lra::launch_ceiling_mfma(lds_operand != 0, n_workgroups, iters, sink, (hipStream_t)stream);
+    return lra::launch_ceiling_mfma(lds_operands, n_workgroups, iters, sink, (hipStream_t)stream);
 }
 
 }  // extern "C"

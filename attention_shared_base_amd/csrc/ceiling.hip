@@ -67,14 +67,15 @@ __global__ __launch_bounds__(256) void hbm_read_chunked_kernel(const u32x4* __re
 }
 
 // Each wavefront runs four independent accumulation chains of
-// v_mfma_f32_32x32x16_bf16 (2 x 32 x 32 x 16 flops each) for `iters` rounds.  With
-// LDS set, every MFMA takes its B operand from a fresh ds_read_b128 (1 KB per
-// wavefront per MFMA, the operand traffic of an attention tile whose keys sit in
-// LDS); the slot index advances by a runtime step so the reads cannot be hoisted.
-template <bool LDS>
+// v_mfma_f32_32x32x16_bf16 (2 x 32 x 32 x 16 flops each) for `iters` rounds.
+// NLDS operands of every MFMA come from a fresh ds_read_b128 (1 KB per wavefront
+// per operand): 0 keeps both in registers, 1 reads B (the operand traffic of an
+// attention tile whose keys sit in LDS), 2 reads A and B.  The slot index
+// advances by a runtime step so the reads cannot be hoisted.
+template <int NLDS>
 __global__ __launch_bounds__(256) void mfma_bf16_kernel(int32_t iters, int32_t step,
                                                         uint32_t* __restrict__ sink) {
-    __shared__ bf16x8 tile[LDS ? 4 * 256 : 1];
+    __shared__ bf16x8 tile[NLDS ? 8 * 256 : 1];
     const int t = threadIdx.x;
     bf16x8 a, b;
 #pragma unroll
@@ -82,9 +83,9 @@ __global__ __launch_bounds__(256) void mfma_bf16_kernel(int32_t iters, int32_t s
         a[e] = (bf16)((float)((t + e) & 7) * 0.125f);
         b[e] = (bf16)((float)((3 * t + e) & 7) * -0.0625f);
     }
-    if constexpr (LDS) {
+    if constexpr (NLDS > 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tile[j * 256 + t] = j & 1 ? a : b;
+        for (int j = 0; j < 8; ++j) tile[j * 256 + t] = j & 1 ? a : b;
         __syncthreads();
     }
     f32x16 c[4];
@@ -96,11 +97,10 @@ __global__ __launch_bounds__(256) void mfma_bf16_kernel(int32_t iters, int32_t s
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bf16x8 bj = b;
-            if constexpr (LDS) {
-                bj = tile[((slot + j) & 3) * 256 + t];
-            }
-            c[j] = mfma32x32x16(a, bj, c[j]);
+            bf16x8 aj = a, bj = b;
+            if constexpr (NLDS >= 1) bj = tile[((slot + j) & 7) * 256 + t];
+            if constexpr (NLDS >= 2) aj = tile[((slot + j + 4) & 7) * 256 + t];
+            c[j] = mfma32x32x16(aj, bj, c[j]);
         }
         slot += step;
     }
@@ -134,11 +134,13 @@ lra_status launch_ceiling_read(const void* buf, uint64_t n_bytes, int n_wg, bool
     return check_launch("hbm_read_kernel");
 }
 
-lra_status launch_ceiling_mfma(bool lds, int n_wg, int iters, uint32_t* sink, hipStream_t s) {
-    if (lds)
-        hipLaunchKernelGGL(mfma_bf16_kernel<true>, dim3(n_wg), dim3(256), 0, s, iters, 1, sink);
+lra_status launch_ceiling_mfma(int n_lds, int n_wg, int iters, uint32_t* sink, hipStream_t s) {
+    if (n_lds == 2)
+        hipLaunchKernelGGL(mfma_bf16_kernel<2>, dim3(n_wg), dim3(256), 0, s, iters, 1, sink);
+    else if (n_lds == 1)
+        hipLaunchKernelGGL(mfma_bf16_kernel<1>, dim3(n_wg), dim3(256), 0, s, iters, 1, sink);
     else
-        hipLaunchKernelGGL(mfma_bf16_kernel<false>, dim3(n_wg), dim3(256), 0, s, iters, 1, sink);
+        hipLaunchKernelGGL(mfma_bf16_kernel<0>, dim3(n_wg), dim3(256), 0, s, iters, 1, sink);
     return check_launch("mfma_bf16_kernel");
 }
 

@@ -125,7 +125,7 @@ lra_status launch_rope_table(double theta, int head_dim, int n_pos, float* c, fl
 // ----------------------------------------------------------------- device ceilings
 lra_status launch_ceiling_read(const void* buf, uint64_t n_bytes, int n_wg, bool nt, bool chunked,
                                uint32_t* sink, hipStream_t s);
-lra_status launch_ceiling_mfma(bool lds, int n_wg, int iters, uint32_t* sink, hipStream_t s);
+lra_status launch_ceiling_mfma(int n_lds, int n_wg, int iters, uint32_t* sink, hipStream_t s);
 
 // ----------------------------------------------------------------- naive baseline
 // Materialised adapter terms (measurement baseline only; see naive_expand.hip).

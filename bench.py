@@ -1035,18 +1035,20 @@ def leg_ceilings(steps, warmup):
     rd = read_floor(1 << 30)
     n_wg, iters = 2048, 2048  # 8 workgroups (32 wavefronts) per CU, about a millisecond a call
     mfma = {}
-    for lds in (False, True):
+    for lds, key in ((0, "register_operands"), (1, "lds_operand_b"), (2, "lds_operands_ab")):
         flops = n_wg * iters * 524288
-        ms = _time_calls(lambda i: lra.ceiling_mfma_bf16(sink, n_workgroups=n_wg, iters=iters, lds_operand=lds),
+        ms = _time_calls(lambda i: lra.ceiling_mfma_bf16(sink, n_workgroups=n_wg, iters=iters, lds_operands=lds),
                          1, max(10, steps // 10), 3)
         tf = flops / (ms * 1e-3) / 1e12
-        mfma["lds_operand" if lds else "register_operands"] = {
-            "kernel": "lra_ceiling_mfma_bf16", "flops_per_call": flops, "ms_per_call": ms, "tflops": tf,
-            "frac_of_peak": tf / BF16_PEAK_TFLOPS,
+        mfma[key] = {
+            "kernel": "lra_ceiling_mfma_bf16", "lds_operands": lds, "flops_per_call": flops, "ms_per_call": ms,
+            "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS,
             # v_mfma_f32_32x32x16_bf16 at one issue per 8 passes on every SIMD, at the
             # published 2.4 GHz, is the published peak; this is the clock that would
             # give the measured rate if the MFMA pipes never idled
-            "clock_ghz_if_pipes_never_idle": 2.4 * tf / BF16_PEAK_TFLOPS}
+            "clock_ghz_if_pipes_never_idle": 2.4 * tf / BF16_PEAK_TFLOPS,
+            # LDS operand bytes read per CU per second (1 KB per wavefront per operand per MFMA)
+            "lds_gb_per_s_per_cu": lds * n_wg * 4 * iters * 4 * 1024 / (ms * 1e-3) / 256 / 1e9}
     g = torch.Generator(device="cuda").manual_seed(7)
     a = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
     b = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)

@@ -445,12 +445,13 @@ lra_status lra_naive_prefill(const lra_dims* dims,
  *
  * lra_ceiling_mfma_bf16 runs n_workgroups workgroups of four wavefronts; each
  * wavefront issues iters rounds of four independent v_mfma_f32_32x32x16_bf16
- * (fp32 accumulation).  lds_operand 1 takes every MFMA's B operand from a new
- * 16-byte LDS read per lane (1 KB per wavefront per MFMA), 0 keeps both operands
- * in registers.  n_workgroups in [1, 65535], iters in [1, 2^20].  sink as above
- * (written only for an impossible sum).
+ * (fp32 accumulation).  lds_operands of every MFMA's two operands come from a
+ * new 16-byte LDS read per lane (1 KB per wavefront per operand): 0 keeps both
+ * in registers, 1 reads B, 2 reads A and B.  n_workgroups in [1, 65535], iters
+ * in [1, 2^20].  sink as above (written only for an impossible sum).
  * Flops per call: n_workgroups * 4 * iters * 4 * (2 * 32 * 32 * 16)
- *               = n_workgroups * iters * 524288.
+ *               = n_workgroups * iters * 524288;
+ * LDS bytes read per call: lds_operands * n_workgroups * 4 * iters * 4 * 1024.
  *
  * Both are asynchronous on stream and allocate nothing.  Errors: LRA_ERR_NULL_PTR,
  * LRA_ERR_MISALIGNED, LRA_ERR_BAD_SHAPE, LRA_ERR_HIP.
@@ -459,7 +460,7 @@ lra_status lra_naive_prefill(const lra_dims* dims,
 #define LRA_READ_CHUNKED 2
 lra_status lra_ceiling_hbm_read(const void* buf, size_t n_bytes, int32_t n_workgroups, int32_t flags,
                                 uint32_t* sink, void* stream);
-lra_status lra_ceiling_mfma_bf16(int32_t lds_operand, int32_t n_workgroups, int32_t iters, uint32_t* sink,
+lra_status lra_ceiling_mfma_bf16(int32_t lds_operands, int32_t n_workgroups, int32_t iters, uint32_t* sink,
                                  void* stream);
 
 #ifdef __cplusplus

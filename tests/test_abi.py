@@ -365,7 +365,8 @@ def test_ceiling_validation():
     assert rd(A, 1024, 0, -1, A, None) == 2
     mm = lib.lra_ceiling_mfma_bf16
     assert mm(0, 256, 16, None, None) == 1
-    assert mm(2, 256, 16, A, None) == 2
+    assert mm(3, 256, 16, A, None) == 2
+    assert mm(-1, 256, 16, A, None) == 2
     assert mm(0, 0, 16, A, None) == 2
     assert mm(1, 65536, 16, A, None) == 2
     assert mm(0, 256, 0, A, None) == 2

@@ -45,12 +45,12 @@ def test_read_stream_quiet_on_zero_buffer():
     assert int(sink.abs().sum().item()) == 0
 
 
-@pytest.mark.parametrize("lds", [False, True])
+@pytest.mark.parametrize("lds", [0, 1, 2])
 def test_mfma_stream_runs(lds):
     import torch
     import attention_shared_base_amd as lra
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    flops = lra.ceiling_mfma_bf16(sink, n_workgroups=512, iters=64, lds_operand=lds)
+    flops = lra.ceiling_mfma_bf16(sink, n_workgroups=512, iters=64, lds_operands=lds)
     torch.cuda.synchronize()
     assert flops == 512 * 64 * 524288
     assert int(sink.abs().sum().item()) == 0
