@@ -118,11 +118,31 @@ def _randn_bf16(shape, sigma, gen):
     return x.to(torch.bfloat16)
 
 
-def _time_calls(fn, n_sets, steps, warmup):
-    """Average time per call (ms) over `steps` calls, HIP events on the launch stream."""
+# Extra legs time a kernel only after at least this much of its own calls: the chip runs
+# the first tens of milliseconds of a new heavy kernel slower (workload-3 prefill: about
+# 800 us per call falling to 650 us over its first 40 calls, with or without other load
+# before it), so a short warm-up would time that transient instead of the steady state.
+MIN_WARM_S = 0.1
+
+
+def _time_calls(fn, n_sets, steps, warmup, min_warm_s=0.0):
+    """Average time per call (ms) over `steps` calls, HIP events on the launch stream, after
+    at least `warmup` calls and min_warm_s seconds of calls (each input set at least once
+    when min_warm_s > 0).  The counts go to call_counts()."""
     import torch
-    for i in range(warmup):
-        fn(i % n_sets)
+    n_w = 0
+    while n_w < warmup:
+        fn(n_w % n_sets)
+        n_w += 1
+    if min_warm_s > 0:
+        # counted from here: a first call's one-time set-up (a library's kernel load) is not warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while n_w < n_sets or time.perf_counter() - t0 < min_warm_s:
+            for _ in range(n_sets):
+                fn(n_w % n_sets)
+                n_w += 1
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -132,7 +152,16 @@ def _time_calls(fn, n_sets, steps, warmup):
         fn(i % n_sets)
     t1.record(stream)
     torch.cuda.synchronize()
+    _COUNTS.update(warmup_calls=n_w, timed_calls=steps)
     return t0.elapsed_time(t1) / steps
+
+
+_COUNTS = {}
+
+
+def call_counts():
+    """Warm-up and timed call counts of the last _time_calls."""
+    return dict(_COUNTS)
 
 
 def _call_stats(fn, n_sets, n_calls):
@@ -152,10 +181,13 @@ def _call_stats(fn, n_sets, n_calls):
             "p90": float(np.percentile(t, 90)), "calls": n_calls}
 
 
-def _timed(fn, n_sets, steps, warmup, stat_calls=None):
-    """(ms per call over the timed region, per-call statistics)."""
-    ms = _time_calls(fn, n_sets, steps, warmup)
+def _timed(fn, n_sets, steps, warmup, stat_calls=None, min_warm_s=MIN_WARM_S):
+    """(ms per call over the timed region, per-call statistics with the call counts: warm-up
+    calls, then timed calls, then the statistics calls, in that order on the stream)."""
+    ms = _time_calls(fn, n_sets, steps, warmup, min_warm_s)
+    counts = call_counts()
     stats = _call_stats(fn, n_sets, stat_calls if stat_calls else max(10, min(steps, 100)))
+    stats.update(counts)
     return ms, stats
 
 
@@ -224,7 +256,7 @@ def read_floor(nbytes, calls=60):
         for chunked in (False, True):
             for n_wg in (2048, 4096, 8192):
                 ms = _time_calls(lambda i: lra.ceiling_hbm_read(bufs[i], sink, n_workgroups=n_wg, nontemporal=nt,
-                                                                chunked=chunked), n_sets, calls, 5)
+                                                                chunked=chunked), n_sets, calls, 5, MIN_WARM_S / 2)
                 if best is None or ms < best[0]:
                     best = (ms, nt, chunked, n_wg)
     ms, nt, chunked, n_wg = best
@@ -364,7 +396,7 @@ def _per_agent_lr(case, layer):
     return (w.draw(102, TAG_LK, shape, 1.0, "bf16", layer), w.draw(102, TAG_LV, shape, 1.0, "bf16", layer))
 
 
-def run_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, rank=16):
+def run_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, rank=16, min_warm_s=MIN_WARM_S):
     """Time lra_attn_decode over n_sets rotated seeded sets of the primary workload's shapes.
     Returns (case of set 0, ms per call, per-call stats, algorithmic bytes, set 0's output,
     set 0's per-agent LR pools or None)."""
@@ -392,7 +424,7 @@ def run_decode(steps, warmup, n_sets, rope_theta=None, per_agent=False, rank=16)
                    max_req_per_ctx=mrpc, max_ctx_len=max_len, rope_cos=cos, rope_sin=sin,
                    out=s.out, workspace=ws)
 
-    ms, stats = _timed(call, n_sets, steps, warmup, max(20, min(steps, 200)))
+    ms, stats = _timed(call, n_sets, steps, warmup, max(20, min(steps, 200)), min_warm_s)
     nbytes = decode_bytes(c0.ctx_len, c0.n_req, len(np.unique(c0.req_agent)), 32, 8, 128, rank)
     if rope_theta is not None:
         nbytes += 2 * max_len * 64 * 4  # the cos / sin rows, read once
@@ -534,8 +566,8 @@ def leg_agent_scaling(steps, warmup, primary_cpu):
             lra.naive_decode(qs[i], crs, agent, st.k, st.v, st.lk, st.lv, st.bt, st.clen, b_k, b_v,
                              max_req_per_ctx=rpc, max_ctx_len=8192, scratch=scratch)
 
-        ms = _time_calls(call, len(sets), steps, warmup)
-        ms_naive = _time_calls(call_naive, len(sets), max(4, steps // 20), 2)
+        ms = _time_calls(call, len(sets), steps, warmup, MIN_WARM_S)
+        ms_naive = _time_calls(call_naive, len(sets), max(4, steps // 20), 2, MIN_WARM_S)
         table[str(rpc)] = {"decode_us": ms * 1e3, "naive_us": ms_naive * 1e3,
                            "decode_tokens_per_s": n_req / (ms * 1e-3)}
         del scratch, ws
@@ -1038,7 +1070,7 @@ def leg_ceilings(steps, warmup):
     for lds, key in ((0, "register_operands"), (1, "lds_operand_b"), (2, "lds_operands_ab")):
         flops = n_wg * iters * 524288
         ms = _time_calls(lambda i: lra.ceiling_mfma_bf16(sink, n_workgroups=n_wg, iters=iters, lds_operands=lds),
-                         1, max(10, steps // 10), 3)
+                         1, max(10, steps // 10), 3, MIN_WARM_S)
         tf = flops / (ms * 1e-3) / 1e12
         mfma[key] = {
             "kernel": "lra_ceiling_mfma_bf16", "lds_operands": lds, "flops_per_call": flops, "ms_per_call": ms,
@@ -1053,7 +1085,7 @@ def leg_ceilings(steps, warmup):
     a = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
     b = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
     c = torch.empty_like(a)
-    gms = _time_calls(lambda i: torch.mm(a, b, out=c), 1, max(10, steps // 10), 3)
+    gms = _time_calls(lambda i: torch.mm(a, b, out=c), 1, max(10, steps // 10), 3, MIN_WARM_S)
     gtf = 2 * 8192 ** 3 / (gms * 1e-3) / 1e12
     best = max(v["tflops"] for v in mfma.values())
     leg = {"workload": "device ceilings: HBM read stream of 1 GiB; bf16 MFMA stream, 2048 workgroups x "
@@ -1172,7 +1204,8 @@ def main():
         return
 
     _log("primary: decode, 4 shared contexts x 8192 tokens, 16 requests")
-    case, ms, call_us, nbytes, got, _ = run_decode(args.steps, args.warmup, args.sets)
+    # exactly --warmup untimed calls before the --steps timed ones
+    case, ms, call_us, nbytes, got, _ = run_decode(args.steps, args.warmup, args.sets, min_warm_s=0.0)
     gbs = nbytes / (ms * 1e-3) / 1e9
     value = case.n_req / (ms * 1e-3)
     _log(f"primary: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, {value:.0f} tokens/s")
