@@ -58,13 +58,20 @@ I32 = ctypes.c_int32
 
 
 def load():
-    """Load liblra_attn.so once; raises if it has not been built."""
+    """Load liblra_attn.so once; raises if it has not been built.
+
+    torch is imported first: its HIP runtime (``libamdhip64.so``, soname
+    ``libamdhip64.so.7``) then satisfies the library's dependency, so the process
+    holds one HIP runtime.  Loaded the other way round, the library would bring in
+    the system runtime and torch a second one, and launches on torch's memory
+    would find no device."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(lib_path):
         raise ImportError(f"{lib_path} not found: build it with "
                           "`python -m attention_shared_base_amd.build` (hipcc, gfx950)")
+    import torch  # noqa: F401  (one HIP runtime per process: torch's)
     lib = ctypes.CDLL(lib_path)
     lib.lra_abi_version.restype = I32
     lib.lra_abi_version.argtypes = []
