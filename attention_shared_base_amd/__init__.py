@@ -17,7 +17,7 @@ __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
     "prefill_paged", "prefill_paged_staged", "prefill_paged_staged_workspace_size",
-    "cache_append", "decode_noalloc",
+    "cache_append", "decode_noalloc", "prepare_decode", "PreparedCall",
     "naive_prefill", "naive_prefill_workspace_size", "ceiling_hbm_read", "ceiling_mfma_bf16",
 ]
 
@@ -191,7 +191,7 @@ def decode_workspace_size(*, n_q_heads, n_kv_heads, head_dim, rank, dtype, n_req
 
 def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table, ctx_len,
            b_k, b_v, *, max_req_per_ctx, max_ctx_len, rope_cos=None, rope_sin=None, out=None,
-           workspace=None, softmax_scale=0.0, stream=None):
+           workspace=None, softmax_scale=0.0, stream=None, _prepare=False):
     """Paged decode (``lra_attn_decode``).  Layouts as in include/lra_attn.h:
 
     q [n_req, H_q, d]; k_pool [n_pages, H_kv, d/8, 16, 8]; v_pool [n_pages, H_kv, d, 16];
@@ -245,13 +245,40 @@ def decode(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_
     if workspace is None and ws_bytes > 0:
         workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.lra_attn_decode(
-        ctypes.byref(dims), _ptr(q), n_req, _ptr(ctx_req_start), n_ctx, max_req_per_ctx,
-        _ptr(req_agent), _ptr(k_pool), _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, page,
-        _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
-        _ptr(rope_cos), _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), wsz,
-        _stream(q, stream)))
+    args = (ctypes.byref(dims), _ptr(q), n_req, _ptr(ctx_req_start), n_ctx, max_req_per_ctx,
+            _ptr(req_agent), _ptr(k_pool), _ptr(v_pool), _ptr(lk_pool), _ptr(lv_pool), n_pages, page,
+            _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx_len, _ptr(b_k), _ptr(b_v), n_agents,
+            _ptr(rope_cos), _ptr(rope_sin), _rows(rope_cos), _ptr(out), _ptr(workspace), wsz,
+            _stream(q, stream))
+    if _prepare:
+        keep = (dims, q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table, ctx_len,
+                b_k, b_v, rope_cos, rope_sin, out, workspace)
+        return PreparedCall(lib.lra_attn_decode, args, keep, out)
+    _check(lib.lra_attn_decode(*args))
     return out
+
+
+class PreparedCall:
+    """One C-ABI call with its arguments checked and marshalled once (``prepare_decode``).
+    Calling it issues the same launch again on the same buffers and stream; it holds
+    references to every tensor it points into.  ``out`` is the output tensor."""
+
+    def __init__(self, fn, args, keep, out):
+        self._fn, self._args, self._keep, self.out = fn, args, keep, out
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            _check(st)
+        return self.out
+
+
+def prepare_decode(*args, **kwargs):
+    """``decode`` with its validation and argument marshalling done once: returns a
+    PreparedCall whose every call launches the decode on the same tensors (whose contents
+    may change between calls) and stream.  For loops that call the decode on fixed
+    buffers, such as one serving step after another."""
+    return decode(*args, _prepare=True, **kwargs)
 
 
 def decode_noalloc(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool, block_table,

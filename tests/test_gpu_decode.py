@@ -243,3 +243,27 @@ def test_decode_context_longer_than_max_ctx_len(persistent):
         os.environ.pop("LRA_DECODE_CHUNK", None)
         os.environ.pop("LRA_DECODE_PERSISTENT", None)
     assert_parity(full, oracle_decode(case), "bf16", "following valid call")
+
+
+def test_prepared_decode_equals_decode():
+    """lra.prepare_decode: the same launch as decode(), bit for bit, on every call; new
+    contents of the same input tensors between calls are seen; RoPE tables pass through."""
+    import torch
+    import attention_shared_base_amd as lra
+    case = w.make_decode(71, dtype="bf16", ctx_lens=[2500, 900], reqs=[(0, 0), (0, 1), (1, 1)], n_agents=2,
+                         h_q=32, h_kv=8, d=128, r=16, shuffle=True, name="prepared")
+    d = DecodeDev(case)
+    for theta in (None, 500000.0):
+        ref = host(d.run(rope_theta=theta))
+        cos, sin = d.rope(theta) if theta is not None else (None, None)
+        out = torch.empty_like(d.q)
+        call = lra.prepare_decode(d.q, d.crs, d.agent, d.k, d.v, d.lk, d.lv, d.bt, d.clen, d.b_k, d.b_v,
+                                  max_req_per_ctx=d.max_req_per_ctx, max_ctx_len=d.max_ctx_len,
+                                  rope_cos=cos, rope_sin=sin, out=out)
+        for _ in range(3):
+            assert np.array_equal(host(call()), ref)
+        q_saved = d.q.clone()
+        d.q.mul_(-1.0)
+        flipped = host(d.run(rope_theta=theta))
+        assert np.array_equal(host(call()), flipped) and not np.array_equal(flipped, ref)
+        d.q.copy_(q_saved)
