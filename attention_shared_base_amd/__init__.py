@@ -17,7 +17,7 @@ __all__ = [
     "LraError", "lib_path", "load", "decode", "decode_workspace_size", "prefill",
     "lr_cache_build", "lr_cache_build_workspace_size", "rope_table", "abi_version", "EXPORTED_SYMBOLS", "naive_decode",
     "prefill_paged", "prefill_paged_staged", "prefill_paged_staged_workspace_size",
-    "cache_append", "decode_noalloc", "prepare_decode", "PreparedCall",
+    "cache_append", "decode_noalloc", "prepare_decode", "prepare_prefill", "PreparedCall",
     "naive_prefill", "naive_prefill_workspace_size", "ceiling_hbm_read", "ceiling_mfma_bf16",
 ]
 
@@ -321,7 +321,7 @@ def decode_noalloc(q, ctx_req_start, req_agent, k_pool, v_pool, lk_pool, lv_pool
 
 
 def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, rope_sin=None,
-            out=None, softmax_scale=0.0, stream=None):
+            out=None, softmax_scale=0.0, stream=None, _prepare=False):
     """Chunked prefill (``lra_attn_prefill``): q [n_req, q_len, H_q, d] over
     k_base/v_base [H_kv, kv_len, d], l_k/l_v [kv_len, r] (shared) or [n_agents, kv_len, r]
     (one LR cache per agent); optional RoPE tables [kv_len, d/2] fp32 rotate the adapter
@@ -354,11 +354,20 @@ def prefill(q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, *, rope_cos=None, 
         out = torch.empty_like(q)
     _contig("out", out)
     dims = _dims(h_q, h_kv, d, r, dt, softmax_scale, kv_len * r if per_agent else 0)
-    _check(lib.lra_attn_prefill(
-        ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_base), _ptr(v_base),
-        kv_len, _ptr(l_k), _ptr(l_v), _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
-        _ptr(rope_sin), _rows(rope_cos), _ptr(out), _stream(q, stream)))
+    args = (ctypes.byref(dims), _ptr(q), n_req, q_len, _ptr(req_agent), _ptr(k_base), _ptr(v_base),
+            kv_len, _ptr(l_k), _ptr(l_v), _ptr(b_k), _ptr(b_v), n_agents, _ptr(rope_cos),
+            _ptr(rope_sin), _rows(rope_cos), _ptr(out), _stream(q, stream))
+    if _prepare:
+        keep = (dims, q, req_agent, k_base, v_base, l_k, l_v, b_k, b_v, rope_cos, rope_sin, out)
+        return PreparedCall(lib.lra_attn_prefill, args, keep, out)
+    _check(lib.lra_attn_prefill(*args))
     return out
+
+
+def prepare_prefill(*args, **kwargs):
+    """``prefill`` with its validation and argument marshalling done once (a PreparedCall,
+    as ``prepare_decode``)."""
+    return prefill(*args, _prepare=True, **kwargs)
 
 
 def lr_cache_build_workspace_size(*, dtype, n_tok, d_model, rank, n_lr=1):

@@ -176,3 +176,19 @@ def test_cfg5_layer_prefill_64_rows_all_agents():
     lv_e = np.concatenate([w.widen(pre.l_v), xv])
     ref_e = oracle_prefill(pre, rows=rows[::8], l_k=lk_e, l_v=lv_e, requests=[0, 3, 7])
     assert_parity(got[[0, 3, 7]][:, rows[::8]], ref_e, "bf16", "cfg5 layer 0 (fp64 X A)")
+
+
+def test_prepared_prefill_equals_prefill():
+    """lra.prepare_prefill: the same launch as prefill(), bit for bit, with and without RoPE."""
+    import torch
+    import attention_shared_base_amd as lra
+    for theta in (None, 500000.0):
+        case = w.make_prefill(72, dtype="bf16", kv_len=400, q_len=50, req_agents=[1, 0], n_agents=2, h_q=32,
+                              h_kv=8, d=128, r=16, rope_theta=theta, name="prepared")
+        d = PrefillDev(case)
+        ref = host(d.run())
+        out = torch.empty_like(d.q)
+        call = lra.prepare_prefill(d.q, d.agent, d.k, d.v, d.lk, d.lv, d.b_k, d.b_v, rope_cos=d.cos,
+                                   rope_sin=d.sin, out=out)
+        for _ in range(3):
+            assert np.array_equal(host(call()), ref)
