@@ -25,6 +25,9 @@
 // to the workspace and the last workgroup of the 64 tokens (a counter per
 // token block) adds the KS partials in range order and rounds once to bf16.
 //
+// LDS-staged kernel (the default when d_model is a multiple of its stage): see
+// its definition below.
+//
 // Single-pass kernel (no workspace): a workgroup owns 16 tokens; its 8 wavefronts take
 // interleaved 32-wide slices of d_model (so together they stream each X row
 // contiguously) and each accumulates the full 16 x 2r tile with
@@ -32,6 +35,9 @@
 // rounded once to bf16.  Every wavefront issues the X and A loads of up to 16
 // of its slices (8 for r = 32) before the first MFMA, so the whole product waits for about
 // one memory round trip instead of one per slice.
+#include <stdlib.h>
+#include <string.h>
+
 #include "lra_common.h"
 #include "lra_internal.h"
 
@@ -121,6 +127,145 @@ __global__ __launch_bounds__(512) void lra_lr_build_bf16_kernel(const bf16* __re
         const size_t row = (size_t)(row_offset + tok0 + t);
         if (c < R) l_k[row * R + c] = (bf16)s;
         else l_v[row * R + (c - R)] = (bf16)s;
+    }
+}
+
+// LDS-staged kernel: a workgroup owns 16 tokens and the whole of d_model, so no
+// partial crosses workgroups.  X rows and the agent's A rows stream through a
+// ring of S LDS stages of KC values of k each, moved by buffer_load ... lds in
+// 1 KB transfers that each cover whole 128-byte lines (halves or wholes of
+// 512- / 1024-byte row pieces).  A CU fetches such transfers about three times
+// as fast as the loads of MFMA fragments straight from memory, each of which
+// touches 16 rows x 64 bytes.  In LDS the 16-byte chunks of a row sit
+// XOR-swizzled by the row index mod 16: the fragment reads of 16 rows
+// (ds_read_b128) meet 16 distinct bank groups, and every aligned group of 8
+// DMA lanes still fetches one whole line.  The 8 wavefronts split each stage's
+// k-steps; their partial 16 x 2R tiles are summed in LDS and rounded once.
+template <int R>
+struct LdsCfg {
+    static constexpr int KC = R <= 8 ? 512 : 256;  // k values per stage (a multiple of d_model)
+    static constexpr int CPR = KC / 8;             // 16-byte chunks of a row piece
+    static constexpr int ROWS = TOK + 2 * R;       // X rows, then A_k rows, then A_v rows
+    static constexpr int STAGE = ROWS * KC * 2;    // bytes of one stage
+    static constexpr int S = (160 * 1024 / STAGE) < 6 ? (160 * 1024 / STAGE) : 6;  // ring depth: the LDS, at most 6
+    static constexpr int NBLK = STAGE / 1024;      // 1 KB transfers per stage
+    static constexpr int PER_WAVE = NBLK / WAVES;
+    static constexpr int KPW = KC / 32 / WAVES;    // MFMA k-steps per wavefront per stage
+    static_assert(NBLK % WAVES == 0 && (KC / 32) % WAVES == 0, "even split over the wavefronts");
+    static_assert(1024 % (CPR * 16) == 0 || (CPR * 16) % 1024 == 0, "transfers hold whole row pieces");
+    static_assert(PER_WAVE * (S - 2) < 16, "vmcnt immediate");
+};
+
+template <int N>
+LRA_DEV void wait_vmcnt() { __builtin_amdgcn_s_waitcnt(0x0f70 | N); }
+
+template <int R>
+__global__ __launch_bounds__(512) void lra_lr_build_lds_kernel(const bf16* __restrict__ x,
+                                                               const bf16* __restrict__ a_k,
+                                                               const bf16* __restrict__ a_v,
+                                                               bf16* __restrict__ l_k,
+                                                               bf16* __restrict__ l_v,
+                                                               int n_tok, int d_model,
+                                                               long long row_offset, int n_lr,
+                                                               long long lr_stride) {
+    using C = LdsCfg<R>;
+    constexpr int NT = (2 * R + 15) / 16;  // 16-column output tiles (R = 4 fills half of one)
+    constexpr int NC = NT * 16;
+    __shared__ __attribute__((aligned(1024))) char ring[C::S * C::STAGE];
+    static_assert(WAVES * TOK * (NC + 1) * 4 <= C::S * C::STAGE, "reduction buffer fits the ring");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int ag = blockIdx.x % n_lr;  // whose A / LR cache
+    const int tok0 = (blockIdx.x / n_lr) * TOK;
+    const int rows = min(TOK, n_tok - tok0);
+    const uint32_t rowb = (uint32_t)d_model * 2;
+    // this block's X rows (rows past n_tok read as zero) and the agent's A_k, A_v
+    const u32x4 rx = make_rsrc(x + (size_t)tok0 * d_model, (uint32_t)rows * rowb);
+    const u32x4 rk = make_rsrc(a_k + (size_t)ag * R * d_model, (uint32_t)R * rowb);
+    const u32x4 rv = make_rsrc(a_v + (size_t)ag * R * d_model, (uint32_t)R * rowb);
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
+
+    // stage st into its ring slot: transfer b of the stage lands at slot + 1 KB * b;
+    // its lane i fills 16-byte chunk p = 64 b + i, i.e. row p / CPR at swizzled
+    // position p % CPR, and so reads that row's chunk (p % CPR) ^ (row % 16).
+    // Every workgroup walks d_model in the same order: they all read the same A,
+    // and requests of one line that arrive together are served by one fetch
+    // (starting each block at another stage measured 20% slower).
+    auto issue = [&](int st) {
+        const uint32_t slot = ring_lds + (uint32_t)(st % C::S) * C::STAGE;
+        const uint32_t k0b = (uint32_t)st * C::KC * 2;
+#pragma unroll
+        for (int u = 0; u < C::PER_WAVE; ++u) {
+            const int b = wave + WAVES * u;
+            const int p = 64 * b + lane;
+            const int row = p / C::CPR;
+            const int chunk = (p % C::CPR) ^ (row & 15);
+            const int row0 = (64 * b) / C::CPR;  // first row of the transfer: picks the matrix
+            const uint32_t inrow = k0b + 16u * chunk;
+            if (row0 < TOK)
+                dma_1k(rx, slot + 1024u * b, (uint32_t)row * rowb + inrow);
+            else if (row0 < TOK + R)
+                dma_1k(rk, slot + 1024u * b, (uint32_t)(row - TOK) * rowb + inrow);
+            else
+                dma_1k(rv, slot + 1024u * b, (uint32_t)(row - TOK - R) * rowb + inrow);
+        }
+    };
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = zf4();
+    auto compute = [&](int st) {
+        const char* slot = ring + (st % C::S) * C::STAGE;
+#pragma unroll
+        for (int u = 0; u < C::KPW; ++u) {
+            const int j = 4 * (wave + WAVES * u) + kq;  // chunk of this lane's 8 k values
+            const bf16x8 xa = *(const bf16x8*)(slot + 16 * (l16 * C::CPR + (j ^ l16)));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int c = nt * 16 + l16;  // output column = A row
+                bf16x8 wb = zero8();
+                if (c < 2 * R) wb = *(const bf16x8*)(slot + 16 * ((TOK + c) * C::CPR + (j ^ l16)));
+                acc[nt] = mfma16x16x32(xa, wb, acc[nt]);
+            }
+        }
+    };
+
+    const int n_st = d_model / C::KC;
+#pragma unroll
+    for (int st = 0; st < C::S - 1; ++st)
+        if (st < n_st) issue(st);
+    for (int st = 0; st < n_st; ++st) {
+        // this wavefront's transfers of stage st have landed; those of the (at
+        // most S - 2) stages it issued after st may still be in flight
+        if (st + C::S - 2 < n_st) wait_vmcnt<C::PER_WAVE * (C::S - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wavefront's part of stage st is in LDS, and stage st - 1 is consumed
+        if (st + C::S - 1 < n_st) issue(st + C::S - 1);  // into stage st - 1's slot
+        compute(st);
+    }
+
+    __syncthreads();  // the ring becomes the reduction buffer
+    float(*sm)[TOK][NC + 1] = reinterpret_cast<float(*)[TOK][NC + 1]>(ring);
+    // C lane layout: tokens 4*kq + v, column l16 of each tile
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm[wave][4 * kq + v][nt * 16 + l16] = acc[nt][v];
+    __syncthreads();
+    l_k += (size_t)ag * lr_stride;
+    l_v += (size_t)ag * lr_stride;
+    for (int e = tid; e < TOK * 2 * R; e += blockDim.x) {
+        const int t = e / (2 * R), c = e % (2 * R);
+        if (t >= rows) continue;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) sum += sm[w][t][c];
+        const size_t row = (size_t)(row_offset + tok0 + t);
+        if (c < R) l_k[row * R + c] = (bf16)sum;
+        else l_v[row * R + (c - R)] = (bf16)sum;
     }
 }
 
@@ -350,8 +495,31 @@ lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
     bf16* lk = (bf16*)a.l_k;
     bf16* lv = (bf16*)a.l_v;
     const long long ro = (long long)a.row_offset, ls = (long long)a.lr_stride;
+    // The LDS-staged kernel whenever d_model is a multiple of its stage (256, or
+    // 512 for ranks <= 8); it needs no workspace.  LRA_LR_BUILD_PATH = split or
+    // single selects one of the other two kernels instead (comparisons, tests).
+    const char* path = getenv("LRA_LR_BUILD_PATH");
+    const bool want_split = path && strcmp(path, "split") == 0;
+    const bool want_single = path && strcmp(path, "single") == 0;
+    const int kc = a.rank <= 8 ? 512 : 256;
+    if (!want_split && !want_single && a.d_model % kc == 0) {
+        const long long nb = (long long)(a.n_tok + TOK - 1) / TOK * a.n_lr;
+        if (nb > 0x7fffffffLL) {
+            set_error("lr build: grid of %lld workgroups too large", nb);
+            return LRA_ERR_BAD_SHAPE;
+        }
+        const dim3 grid((unsigned)nb), block(64 * WAVES);
+        switch (a.rank) {
+            case 4: hipLaunchKernelGGL(lra_lr_build_lds_kernel<4>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
+            case 8: hipLaunchKernelGGL(lra_lr_build_lds_kernel<8>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
+            case 16: hipLaunchKernelGGL(lra_lr_build_lds_kernel<16>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
+            case 32: hipLaunchKernelGGL(lra_lr_build_lds_kernel<32>, grid, block, 0, s, x, ak, av, lk, lv, a.n_tok, a.d_model, ro, a.n_lr, ls); break;
+            default: set_error("lr build: unsupported rank %d", a.rank); return LRA_ERR_UNSUPPORTED;
+        }
+        return check_launch("lra_lr_build_lds_kernel");
+    }
     const LRPlan pl = lr_build_plan(a.n_tok, a.d_model, a.rank, a.n_lr);
-    if (pl.ks == 1 || a.workspace != nullptr) {
+    if (!want_single && (pl.ks == 1 || a.workspace != nullptr)) {
         const long long nb = pl.units * pl.ks;
         if (nb > 0x7fffffffLL) {
             set_error("lr build: grid of %lld workgroups too large", nb);

@@ -89,6 +89,24 @@ LRA_DEV u32x4 make_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
+// One 1 KB HBM -> LDS block (buffer_load_dwordx4 ... lds): lane i reads 16
+// bytes at byte offset voff of the resource and they land at LDS address
+// lds + 16*i.  Issued from asm so that the compiler does not serialise the
+// transfer against unrelated LDS reads; the caller awaits completion with
+// s_waitcnt vmcnt before the barrier that publishes the data.  M0 is restored.
+LRA_DEV void dma_1k(u32x4 r, uint32_t lds, uint32_t voff) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r)
+        : "memory");
+}
+
 // Streaming (read-once) load: bypasses reuse in the caches it can.
 template <typename T>
 LRA_DEV T ldg_stream(const T* p) { return __builtin_nontemporal_load(p); }

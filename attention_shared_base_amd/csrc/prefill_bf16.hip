@@ -116,24 +116,6 @@ LRA_DEV bf16x4 lds_read_tr(const char* p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
-// One 1 KB HBM -> LDS block (buffer_load_dwordx4 ... lds): lane i reads 16
-// bytes at byte offset voff of the resource and they land at LDS address
-// lds + 16*i.  Issued from asm so that the compiler does not serialise the
-// transfer against unrelated LDS reads; completion is awaited explicitly
-// (wait_dma) before the barrier that publishes the tile.  M0 is restored.
-LRA_DEV void dma_1k(u32x4 r, uint32_t lds, uint32_t voff) {
-    uint32_t keep;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(keep)
-        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r)
-        : "memory");
-}
-
 // The same with 4 bytes per lane (lane i -> lds + 4 i): the rank-4 L rows, 8
 // bytes each, spread over 16-byte LDS slots.
 LRA_DEV void dma_256(u32x4 r, uint32_t lds, uint32_t voff) {

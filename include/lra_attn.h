@@ -340,11 +340,13 @@ lra_status lra_cache_append(const lra_dims* dims, int32_t n_tok, const int64_t* 
  *   workspace  optional (may be NULL), device, caller-owned, 16-byte aligned,
  *              >= lra_lr_cache_build_workspace_size(...) bytes, zero-filled
  *              before its first use (each call leaves it ready for the next:
- *              its counters return to zero).  With it,
- *              bf16 builds split d_model over several workgroups per token
- *              block and add their fp32 partials in a fixed order (faster when
- *              n_tok * n_lr is small); without it one workgroup covers each
- *              token's whole d_model.  Either way the result is deterministic.
+ *              its counters return to zero).  bf16 builds whose d_model is a
+ *              multiple of 256 (512 for rank <= 8) stage X and A through LDS,
+ *              one workgroup per 16 tokens over the whole of d_model, and use
+ *              no workspace.  Otherwise, with a workspace, they split d_model
+ *              over several workgroups per token block and add the fp32
+ *              partials in a fixed order; without one a workgroup covers each
+ *              token's whole d_model.  Every path is deterministic.
  *              Concurrent calls must not share a workspace.
  *   Requires d_model % 32 == 0.  bf16 results are rounded to nearest even
  *   once, after fp32 accumulation.
