@@ -43,3 +43,23 @@ def test_prefill_flops_closed_forms():
 
 def test_lr_build_bytes():
     assert bench.lr_build_bytes(4096, 4096, 16) == (4096 * 4096 + 2 * 16 * 4096 + 2 * 4096 * 16) * 2
+
+
+def test_committed_counter_summary_is_of_the_current_kernel_sources():
+    """profiles/hbm_traffic__all_legs.txt was taken on the kernel sources in the tree, and
+    every HBM- or MFMA-bound leg bench.py reports (and the read ceilings) has its record, so
+    the bench's `roofline.traffic` is measured, not null.  A kernel change without a new
+    profiling session fails here."""
+    import bench
+    legs = ("primary", "decode_rope", "decode_qkvo_r4", "decode_per_agent", "naive_decode", "paged_decode",
+            "naive_paged_decode", "prefill_rope", "prefill_paged", "naive_prefill", "lr_build", "prelr_step",
+            "ceilings", "ceilings_read_hbm_read_chunked_kernel<true>", "ceilings_read_hbm_read_kernel<true>")
+    for leg in legs:
+        traffic, src = bench.measured_traffic(leg)
+        assert traffic is not None, f"{leg}: {src}"
+        assert traffic > 0 and "rocprofv3" in src
+    # the read ceiling moves what it reads: 1 GiB per launch within the counters' granularity
+    assert abs(bench.measured_traffic("ceilings_read_hbm_read_chunked_kernel<true>")[0] - (1 << 30)) < (1 << 20)
+    # the decode's measured traffic is within 10% of its algorithmic bytes (no wasted re-reads)
+    alg = bench.decode_bytes([8192] * 4, 16, 4, 32, 8, 128, 16)
+    assert 1.0 <= bench.measured_traffic("primary")[0] / alg < 1.1
