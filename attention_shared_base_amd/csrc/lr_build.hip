@@ -502,7 +502,10 @@ lra_status launch_lr_build_bf16(const LRBuildArgs& a, hipStream_t s) {
     const bool want_split = path && strcmp(path, "split") == 0;
     const bool want_single = path && strcmp(path, "single") == 0;
     const int kc = a.rank <= 8 ? 512 : 256;
-    if (!want_split && !want_single && a.d_model % kc == 0) {
+    // its buffer ranges and offsets are 32-bit byte counts: X rows of a block and
+    // the 2 * rank A rows must stay below 2^31 bytes
+    const bool fits = (long long)(TOK > 2 * a.rank ? TOK : 2 * a.rank) * a.d_model * 2 < (1LL << 31);
+    if (!want_split && !want_single && a.d_model % kc == 0 && fits) {
         const long long nb = (long long)(a.n_tok + TOK - 1) / TOK * a.n_lr;
         if (nb > 0x7fffffffLL) {
             set_error("lr build: grid of %lld workgroups too large", nb);
