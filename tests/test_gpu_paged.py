@@ -124,15 +124,17 @@ def test_prefill_paged_equals_contiguous(rope, h_q, h_kv, d, r, kv_len, q_len):
     print(f"max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
 
 
-def test_prefill_paged_per_agent_lr():
+@pytest.mark.parametrize("rope,r", [(False, 16), (True, 16), (True, 4), (False, 32)])
+def test_prefill_paged_per_agent_lr(rope, r):
     """One LR pool per agent ([n_agents, n_pages, 16, r] / [.., r, 16]) through the same block
-    table: equals the contiguous per-agent prefill bit for bit, and the oracle."""
+    table, with and without RoPE on the adapter key: equals the contiguous per-agent prefill
+    bit for bit, and the oracle."""
     import torch
     import attention_shared_base_amd as lra
     n_ag, kv_len = 3, 700
     case = w.make_prefill(91, dtype="bf16", kv_len=kv_len, q_len=90, req_agents=[2, 0, 1, 2],
-                          n_agents=n_ag, h_q=32, h_kv=8, d=128, r=16, b_sigma=0.2,
-                          name="per-agent paged prefill")
+                          n_agents=n_ag, h_q=32, h_kv=8, d=128, r=r, b_sigma=0.2,
+                          rope_theta=500000.0 if rope else None, name="per-agent paged prefill")
     rng = np.random.default_rng(92)
     lk = np.stack([w.f32_to_bf16_bits(rng.standard_normal(case.l_k.shape).astype(np.float32))
                    for _ in range(n_ag)])
@@ -152,11 +154,11 @@ def test_prefill_paged_per_agent_lr():
     d_ = PrefillDev(case)
     table = torch.from_numpy(ids.astype(np.int32)).to("cuda")
     got = lra.prefill_paged(d_.q, d_.agent, dev(k), dev(v), dev(np.stack(lkps)), dev(np.stack(lvps)),
-                            table, kv_len, d_.b_k, d_.b_v)
+                            table, kv_len, d_.b_k, d_.b_v, rope_cos=d_.cos, rope_sin=d_.sin)
     assert torch.equal(got, d_.run(lk=dev(lk), lv=dev(lv)))
     ma, rel = assert_parity(host(got), oracle_prefill(case, l_k=w.widen(lk), l_v=w.widen(lv)), "bf16",
                             "per-agent paged prefill")
-    print(f"[per-agent paged prefill] max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
+    print(f"[per-agent paged prefill rope={rope} r{r}] max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
 
 
 def test_serving_loop_append_prefill_decode():
