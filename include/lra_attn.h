@@ -36,6 +36,14 @@
  *   - Element counts and layouts below are in elements of the storage type
  *     (dims->dtype): LRA_BF16 = bfloat16 bits, LRA_F32 = IEEE float.
  *     Accumulation is always fp32.  bf16 outputs are rounded to nearest even.
+ *   - Environment switches (measurement and tests; results stay within the
+ *     documented precision whatever they select): LRA_DECODE_CHUNK (256, 512,
+ *     1024, 2048 or 4096 tokens per decode workgroup; default: planned from the
+ *     longest context), LRA_DECODE_TARGET_WG (workgroups the chunk plan aims at,
+ *     default 256), LRA_DECODE_PERSISTENT (0 or 1: one-shot or chunk-queue
+ *     decode workgroups; default: chosen by grid size), LRA_LR_BUILD_PATH (split
+ *     or single: the LR build's d_model-split or single-pass kernel instead of
+ *     the LDS-staged one).
  *   - Supported: head_dim in {64, 128}, rank in {4, 8, 16, 32} (4: the rank of
  *     the query/key/value/output LoRA setting, LRAgent App. D.1),
  *     n_q_heads % n_kv_heads == 0, page_size == 16.  Query heads map to KV
