@@ -95,6 +95,24 @@ def test_decode_fp32_ragged(r):
     _check(case)
 
 
+FP32_EDGES = [(64, 4, False), (64, 16, True), (64, 32, False), (128, 8, True), (128, 16, False)]
+
+
+@pytest.mark.parametrize("d,r,rope", FP32_EDGES, ids=[f"d{d} r{r}{' rope' if p else ''}" for d, r, p in FP32_EDGES])
+def test_decode_fp32_chunk_edges(d, r, rope):
+    """fp32 rows split over four wavefronts in 64-key chunks: contexts of 1, 63, 64, 65, 256
+    (every wavefront one full chunk), 257 (the first wavefront a second one-key chunk) and
+    1000 keys, at head-dim / rank pairs the other fp32 cases do not use."""
+    ctx = [1, 63, 64, 65, 256, 257, 1000]
+    reqs = [(c, c % 2) for c in range(len(ctx))]
+    case = w.make_decode(29, dtype="f32", ctx_lens=ctx, reqs=reqs, n_agents=2, h_q=8, h_kv=2, d=d, r=r,
+                         shuffle=True, b_sigma=0.2, name=f"fp32 chunk edges d{d} r{r} rope {rope}")
+    theta = 10000.0 if rope else None
+    got = host(DecodeDev(case).run(rope_theta=theta))
+    ma, rel = assert_parity(got, oracle_decode(case, rope_theta=theta), "f32", case.name)
+    print(f"[decode] {case.name}: max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
+
+
 def test_decode_split_count_invariance():
     reqs = [(c, c % 3) for c in range(3) for _ in range(2)]
     case = w.make_decode(23, dtype="bf16", ctx_lens=[3000, 1111, 4096], reqs=reqs, n_agents=3,

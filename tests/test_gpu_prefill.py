@@ -64,6 +64,18 @@ def test_prefill_fp32_rope():
     _check(case)
 
 
+@pytest.mark.parametrize("d,r,rope", [(64, 32, False), (128, 8, True), (128, 4, False), (64, 4, True)],
+                         ids=["d64 r32", "d128 r8 rope", "d128 r4", "d64 r4 rope"])
+def test_prefill_fp32_chunk_edges(d, r, rope):
+    """fp32 prefill rows split over four wavefronts in 64-key chunks: the rows see 193 to 320
+    keys, so their last chunk holds every count from 1 to 64 keys, and rows past 256 keys
+    give the first wavefront a second chunk."""
+    case = w.make_prefill(48, dtype="f32", kv_len=320, q_len=128, req_agents=[1, 0], n_agents=2,
+                          h_q=8, h_kv=2, d=d, r=r, rope_theta=10000.0 if rope else None, b_sigma=0.2,
+                          name=f"fp32 chunk edges d{d} r{r} rope {rope}")
+    _check(case)
+
+
 def test_prefill_adapter_delta_and_rope_zero_bk():
     import torch
     case = w.make_prefill(45, dtype="bf16", kv_len=500, q_len=128, req_agents=[0, 1], n_agents=2,
