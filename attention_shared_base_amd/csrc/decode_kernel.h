@@ -154,6 +154,10 @@ template <int D, int R, int SPW, int DEPTH, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) {
     constexpr bool ROPE = MODE == MODE_ROPE || MODE == MODE_ROPE_PER_AGENT;
     constexpr bool PA = MODE == MODE_PER_AGENT || MODE == MODE_ROPE_PER_AGENT;
+    // RoPE: later steps' cos / sin by angle addition from step 0's rows, except
+    // in the per-agent instances of ranks 8 and 32, whose registers are full (the
+    // angle update spills there): those load every step's rows
+    constexpr bool RADV = MODE == MODE_ROPE || (MODE == MODE_ROPE_PER_AGENT && R != 8 && R != 32);
     constexpr int NQ = PA ? PA_REQ : 1;
     // request -> agent table fetched at kernel start (see below); the RoPE and
     // per-agent rank-32 instances keep scalar loads, as their registers are full
@@ -181,6 +185,9 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
     float(*const sm_o)[ROWS][SP] = reinterpret_cast<float(*)[ROWS][SP]>(sm_raw);
     char* const sm_bk = sm_raw;
     __shared__ int sm_pid[ROPE ? CHUNK / PAGE : 1];
+    // RoPE: cos / sin of the angle of WAVES * 32 positions (table row WAVES * 32),
+    // [dim tile ht][cos, sin][k-group q4]: dims 16*ht + 4*q4 .. + 3
+    __shared__ f32x4 sm_radv[RADV ? D / 32 : 1][2][4];
     __shared__ float sm_m[WAVES][ROWS];
     __shared__ float sm_l[WAVES][ROWS];
     __shared__ float sm_L[ROWS];
@@ -368,10 +375,14 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         }
     };
     // RoPE tables of step i's keys: the key's position in its context is its
-    // token index; tokens past the chunk end read the last valid row (unused).
-    // One buffer: step i+1's rows are requested when step i is done with its own.
-    // Rows are read through a buffer range starting at the page's first key, so
-    // the per-step address stays scalar; rows past the table read as zero.
+    // token index.  With RADV only step 0's rows are loaded: every later step's
+    // keys sit WAVES * 32 positions after the previous step's, so their cos /
+    // sin follow by angle addition with the table row of that distance
+    // (sm_radv), and the stream issues no table loads.  Otherwise step i+1's
+    // rows are requested when step i is done with its own (one buffer).  Rows
+    // are read through a buffer range starting at the page's first key, so the
+    // address stays scalar; rows past the table read as zero (keys there are
+    // past the context and masked).
     const uint32_t rope_voff = (uint32_t)(n16 * (D / 2) + 4 * q4) * 4;
     auto load_rope = [&](StepRope<D>& C, int i) {
 #pragma unroll
@@ -468,6 +479,19 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
         // one rank) for four requests at a time, then scatters them.
         constexpr int PIECES = R * D / 8;  // per request
         constexpr int PPT = (PIECES + 64 * WAVES - 1) / (64 * WAVES);
+        // the angle-advance row: thread e < 8 * D / 32 fetches entry (ht, cos / sin,
+        // q4) = (e / 8, (e / 4) % 2, e % 4)
+        constexpr int ADV = WAVES * KEYS_PER_STEP;
+        f32x4 radv = zf4();
+        if constexpr (RADV) {
+            const int e = min(tid, 8 * (D / 32) - 1);
+            const float* tab = ((e >> 2) & 1) ? a.rope_sin : a.rope_cos;
+            const uint32_t bytes = (uint32_t)max(a.rope_rows - ADV, 0) * (D / 2) * 4;
+            const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(tab + (size_t)ADV * (D / 2)), (short)0, bytes, 0x00020000);
+            radv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rt, (16 * (e >> 3) + 4 * (e & 3)) * 4, 0, 0));
+        }
         for (int s0 = 0; s0 < nreq; s0 += 4) {
             int agent[4];
 #pragma unroll
@@ -513,6 +537,7 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
                 }
             }
         }
+        if (RADV && tid < 8 * (D / 32)) sm_radv[tid >> 3][(tid >> 2) & 1][tid & 3] = radv;
         __syncthreads();
     } else {
     auto bk_mfma = [&](const int s0, const bf16x8 (&bk)[4][NRT][NJ]) __attribute__((always_inline)) {
@@ -709,7 +734,21 @@ __global__ __launch_bounds__(64 * WAVES) void lra_decode_bf16_kernel(DecodeK a) 
             load(nxt, pn);
             __builtin_amdgcn_sched_barrier(0);
             compute(cur, kbeg + (wave + WAVES * i) * KEYS_PER_STEP);
-            load_rope(rope_buf, in);
+            // cos / sin of the next step's keys: angle + WAVES * 32 positions
+            if constexpr (!RADV) {
+                load_rope(rope_buf, in);
+            } else {
+#pragma unroll
+                for (int ht = 0; ht < D / 32; ++ht) {
+                    const f32x4 ca = sm_radv[ht][0][q4], sa = sm_radv[ht][1][q4];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 c = rope_buf.cs[t][ht][0], sn = rope_buf.cs[t][ht][1];
+                        rope_buf.cs[t][ht][0] = c * ca - sn * sa;
+                        rope_buf.cs[t][ht][1] = sn * ca + c * sa;
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         };
 #pragma unroll 1
