@@ -142,7 +142,12 @@ const char* lra_last_error(void);
  *   rope_sin       NULL (no rotation of the adapter key term) or both
  *                  [rope_rows, d/2] fp32 device tables of
  *                  cos/sin(pos * theta^(-2i/d)) (lra_rope_table_build); the
- *                  key at token index j of a context has position j.
+ *                  key at token index j of a context has position j.  The
+ *                  bf16 kernel reads only some rows and derives the others
+ *                  by angle addition (row p + 128 from row p and row 128), so
+ *                  the tables must hold a plain rotation: row p =
+ *                  cos/sin(p * w_i) for fixed frequencies w_i (no scaling
+ *                  of cos and sin by a factor).
  *   rope_rows      rows of each table; with tables it must be at least
  *                  max(max_ctx_len, 1) (else LRA_ERR_BAD_SHAPE); ignored
  *                  without them.  K_base
@@ -236,8 +241,11 @@ lra_status lra_attn_decode_noalloc(const lra_dims* dims,
  *   rope_sin   NULL (no rotation of the adapter key term) or both
  *              [rope_rows, d/2] fp32 device tables of cos/sin(pos * theta^(-2i/d))
  *              (see lra_rope_table_build), rope_rows >= kv_len (else
- *              LRA_ERR_BAD_SHAPE; ignored without tables).  K_base is expected
- *              already rotated;
+ *              LRA_ERR_BAD_SHAPE; ignored without tables).  The bf16 kernel
+ *              reads rows 0..63 and the first row of each 64-key tile and
+ *              derives the others by angle addition, so the tables must hold
+ *              a plain rotation: row p = cos/sin(p * w_i) for fixed
+ *              frequencies w_i.  K_base is expected already rotated;
  *              the kernel rotates only L_k B_k (rotate-half pairing i, i+d/2)
  *              before adding it to K_base.
  *   out        [n_req, q_len, H_q, d]          device
