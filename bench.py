@@ -1022,8 +1022,8 @@ def leg_prelr_step(steps, warmup, n_layers=32):
         return leg
     del leg["note_oracle"]
     # ---- oracle on the last layer (whose rows `out` holds): LR build vs X A in float64, and
-    # attention of 16 sampled rows (first and last included) of all 8 agents given the LR rows
-    # the GPU built.  One (agent, layer) pair is timed at two row counts; the fit
+    # attention of 16 sampled rows (first and last included) of all 8 agents, end to end (the
+    # oracle's own X A rows as the new LR rows).  One (agent, layer) pair is timed at two row counts; the fit
     # t(n) = a + b n (a: materialising K and V, b: per row) gives the pair's full-call time,
     # extrapolated x 256 pairs plus 32 LR builds.
     L = layers[-1]
@@ -1033,6 +1033,7 @@ def leg_prelr_step(steps, warmup, n_layers=32):
     lk, lv = _host(L["lk"]), _host(L["lv"])
     lr_par = _parity(np.concatenate([lk[n_old:], lv[n_old:]], 1), np.concatenate([rk, rv], 1),
                      "bf16", "last layer's 4096 new LR rows (both caches) vs X A in float64")
+    lk_o, lv_o = np.concatenate([lk[:n_old], rk]), np.concatenate([lv[:n_old], rv])
     kb, vb = _host(L["k"]), _host(L["v"])
     bk, bv = _host(L["bk"]), _host(L["bv"])
     rows16 = np.unique(np.linspace(0, n_new - 1, 16).astype(np.int64))
@@ -1042,12 +1043,12 @@ def leg_prelr_step(steps, warmup, n_layers=32):
     for a in range(n_ag):
         qa = _host(L["q"][a:a + 1])
         t0 = time.perf_counter()
-        ref = oracle.prefill(qa, np.array([a]), kb, vb, lk, lv, bk, bv, rows=rows16)
+        ref = oracle.prefill(qa, np.array([a]), kb, vb, lk_o, lv_o, bk, bv, rows=rows16)
         t = time.perf_counter() - t0
         if a == 0:
             t16 = t
             t0 = time.perf_counter()
-            oracle.prefill(qa, np.array([a]), kb, vb, lk, lv, bk, bv, rows=rows48)
+            oracle.prefill(qa, np.array([a]), kb, vb, lk_o, lv_o, bk, bv, rows=rows48)
             t48 = time.perf_counter() - t0
         p = _parity(got[a:a + 1, rows16], ref, "bf16", "")
         ok_max, ok_rel, ok = max(ok_max, p["max_abs"]), max(ok_rel, p["rel_l2"]), ok and p["pass"]
@@ -1061,7 +1062,8 @@ def leg_prelr_step(steps, warmup, n_layers=32):
                                  f"per row -> {t_pair:.0f} s per pair), x 256 pairs + 32 LR builds "
                                  f"({el_lr / reps_lr:.2f} s each) = {t_total / 3600:.1f} h per step"),
             "parity": {"attention": {"checked": "last layer, 16 rows (first and last included) of "
-                                                "each of the 8 agents, given the GPU-built LR rows",
+                                                "each of the 8 agents, end to end (new LR rows: the "
+                                                "oracle's X A in float64)",
                                      "max_abs": ok_max, "rel_l2": ok_rel,
                                      "bar": "max-abs 2e-2 and rel-L2 1e-2", "pass": ok},
                        "lr_build": lr_par}})

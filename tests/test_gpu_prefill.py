@@ -151,10 +151,11 @@ def test_decode_equals_last_prefill_row():
 @pytest.mark.slow
 def test_cfg5_layer_prefill_64_rows_all_agents():
     """One layer of the 4096-over-131072 PreLRShared step: LR build, then 8 agents' prefill;
-    64 rows (first and last included) of every agent against the oracle over the LR rows the
-    kernel read, and a subset against the oracle's own fp64 X A."""
+    64 rows (first and last included) of every agent against the oracle end to end (the
+    oracle builds the new LR rows from X and A itself in float64)."""
     import torch
     import attention_shared_base_amd as lra
+    import oracle
     from gpu_helpers import dev
     layer = w.config5_layer(0)
     pre = layer.prefill
@@ -171,24 +172,67 @@ def test_cfg5_layer_prefill_64_rows_all_agents():
                                  l_k=np.zeros((1, 16), np.uint16), l_v=np.zeros((1, 16), np.uint16),
                                  b_k=pre.b_k, b_v=pre.b_v))
     got = host(d.run(lk=lk, lv=lv))
-    # oracle: the same LR bits the attention read (staged check), and the fp64 X A end to end
-    lk_h, lv_h = host(lk), host(lv)
+    xk, xv = oracle.lr_cache_build(w.widen(lr.x), w.widen(lr.a_k).T, w.widen(lr.a_v).T)
+    lk_e = np.concatenate([w.widen(pre.l_k), xk])
+    lv_e = np.concatenate([w.widen(pre.l_v), xv])
     # 64 rows of every agent: the first and last new tokens and 62 spread between
     rows = np.unique(np.concatenate([[0, 1, 4094, 4095], np.linspace(2, 4093, 60).astype(int)]))
     assert len(rows) == 64
     agents = list(range(len(pre.req_agent)))
-    ref = oracle_prefill(pre, rows=rows, l_k=lk_h, l_v=lv_h, requests=agents)
-    ma, rel = assert_parity(got[:, rows], ref, "bf16", "cfg5 layer 0 (GPU-built L)")
+    ref = oracle_prefill(pre, rows=rows, l_k=lk_e, l_v=lv_e, requests=agents)
+    ma, rel = assert_parity(got[:, rows], ref, "bf16", "cfg5 layer 0")
     print(f"[prefill] cfg5 layer 0, 64 rows x {len(agents)} agents: max-abs {ma:.2e} rel-L2 {rel:.2e}")
     for i in agents:  # each agent on its own at the same bar
         assert_parity(got[i, rows], ref[i], "bf16", f"cfg5 layer 0 agent {i}")
-    import oracle
-    xk, xv = oracle.lr_cache_build(w.widen(lr.x), w.widen(lr.a_k).T, w.widen(lr.a_v).T)
-    lk_e = np.concatenate([w.widen(pre.l_k), xk])
-    lv_e = np.concatenate([w.widen(pre.l_v), xv])
-    ref_e = oracle_prefill(pre, rows=rows[::8], l_k=lk_e, l_v=lv_e, requests=[0, 3, 7])
-    assert_parity(got[[0, 3, 7]][:, rows[::8]], ref_e, "bf16", "cfg5 layer 0 (fp64 X A)")
 
+
+def _gpu_bf16(shape, sigma, gen):
+    """Seeded N(0, sigma^2) draw on the GPU, rounded once to bf16 (round to nearest even)."""
+    import torch
+    x = torch.randn(shape, dtype=torch.float32, device="cuda", generator=gen)
+    return (x * sigma if sigma != 1.0 else x).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("first", [0, 8, 16, 24], ids=lambda f: f"layers {f}-{f + 7}")
+def test_cfg5_step_every_layer_sampled(first):
+    """Every (agent, layer) pair of the 32-layer PreLRShared step (4096 new tokens over 131072,
+    8 agents, each layer with its own seeded draws, made on the GPU at this size): the layer's
+    LR build of its new rows, then the 8 agents' prefill; four rows (first and last included) of
+    the four query heads of one KV head per layer (head = layer mod 8) against the oracle, end
+    to end: the oracle builds the new LR rows from X and A itself in float64."""
+    import torch
+    import attention_shared_base_amd as lra
+    import oracle
+    n_new, n_old, d_model, h_q, h_kv, d, r, n_ag = 4096, 131072, 4096, 32, 8, 128, 16, 8
+    kv_len = n_old + n_new
+    g = h_q // h_kv
+    rows = np.array([0, 1, 2048 + 7 * first, n_new - 1])
+    agent = torch.arange(n_ag, dtype=torch.int32, device="cuda")
+    for layer in range(first, first + 8):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(5000 + layer)
+        x = _gpu_bf16((n_new, d_model), 1.0, gen)
+        ak, av = _gpu_bf16((r, d_model), 1.0 / 64, gen), _gpu_bf16((r, d_model), 1.0 / 64, gen)
+        k, v = _gpu_bf16((h_kv, kv_len, d), 1.0, gen), _gpu_bf16((h_kv, kv_len, d), 1.0, gen)
+        lk, lv = _gpu_bf16((kv_len, r), 1.0, gen), _gpu_bf16((kv_len, r), 1.0, gen)
+        q = _gpu_bf16((n_ag, n_new, h_q, d), 1.0, gen)
+        bk, bv = _gpu_bf16((n_ag, r, h_kv * d), 0.05, gen), _gpu_bf16((n_ag, r, h_kv * d), 0.05, gen)
+        lk_old, lv_old = host(lk[:n_old]), host(lv[:n_old])  # before the build writes the new rows
+        lra.lr_cache_build(x, ak, av, lk, lv, row_offset=n_old)
+        out = lra.prefill(q, agent, k, v, lk, lv, bk, bv)
+        h = layer % h_kv
+        hs = slice(h * g, (h + 1) * g)
+        got = host(out[:, rows, hs])
+        # oracle on KV head h alone (its g query heads, B columns h*d .. h*d + d - 1)
+        rk, rv = oracle.lr_cache_build(host(x), host(ak).T, host(av).T)
+        lk_o, lv_o = np.concatenate([lk_old, rk]), np.concatenate([lv_old, rv])
+        cols = slice(h * d, (h + 1) * d)
+        ref = oracle.prefill(host(q[:, :, hs]), np.arange(n_ag), host(k[h:h + 1]), host(v[h:h + 1]),
+                             lk_o, lv_o, host(bk[:, :, cols]), host(bv[:, :, cols]), rows=rows)
+        ma, rel = assert_parity(got, ref, "bf16", f"cfg5 layer {layer} head {h}")
+        print(f"[prefill] cfg5 layer {layer}, KV head {h}, rows {rows.tolist()} x {n_ag} agents: "
+              f"max-abs {ma:.2e} rel-L2 {rel:.2e}", flush=True)
+        del x, ak, av, k, v, lk, lv, q, bk, bv, out
 
 def test_prepared_prefill_equals_prefill():
     """lra.prepare_prefill: the same launch as prefill(), bit for bit, with and without RoPE."""
