@@ -69,6 +69,26 @@ def test_decode_rope_small_shuffled(label, h_q, h_kv, d, r, lens, rpc, bs):
     _check(case, theta=10000.0)
 
 
+
+def test_decode_rope_long_chunks_high_frequencies():
+    """4096-token chunks (32 steps per wavefront: the keys' cos / sin advanced by angle addition
+    31 times) at theta 1e4, whose fastest pair turns 128 rad per step, with a large adapter term
+    (B ~ N(0, 0.3^2)): the whole result and the adapter's own contribution against the oracle,
+    whose tables are computed per position."""
+    import torch
+    reqs = [(c, c % 3) for c in range(3) for _ in range(2)]
+    case = w.make_decode(57, dtype="bf16", ctx_lens=[8191, 4096, 6000], reqs=reqs, n_agents=3, h_q=32,
+                         h_kv=8, d=128, r=16, shuffle=True, b_sigma=0.3, name="rope long chunks")
+    try:
+        os.environ["LRA_DECODE_CHUNK"] = "4096"
+        d, got, ref = _check(case, theta=10000.0, label="rope 4096-token chunks theta 1e4")
+        got0 = host(d.run(b_k=torch.zeros_like(d.b_k), b_v=torch.zeros_like(d.b_v), rope_theta=10000.0))
+    finally:
+        os.environ.pop("LRA_DECODE_CHUNK", None)
+    ref0 = oracle_decode(case, zero_b=True, rope_theta=10000.0)
+    _, rel = metrics(got - got0, ref - ref0)
+    assert rel <= DELTA_REL_L2, f"adapter delta rel-L2 {rel:.3e}"
+
 def test_decode_rope_fp32():
     reqs = [(0, 0), (0, 1), (1, 1), (2, 0)]
     case = w.make_decode(43, dtype="f32", ctx_lens=[1, 45, 300], reqs=reqs, n_agents=2, h_q=8,
